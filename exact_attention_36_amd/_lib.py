@@ -1,0 +1,201 @@
+"""ctypes binding of libattn36.so (include/attn.h).
+
+Argument marshalling only: shapes and dtypes are read off the tensors, outputs
+and the workspace are allocated with torch on the inputs' device, and the
+call is enqueued on torch's current stream.  Every computation happens in the
+library's HIP kernels; if the library is missing this module raises instead
+of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn36.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EHIP = 0, 1, 2, 3
+ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
+
+EXPORTED = (
+    "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
+    "attn_fwd_varlen", "attn_fwd_varlen_workspace_size", "attn_bwd_varlen",
+    "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version",
+)
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from the library; .status holds the code."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__("attn status %d: %s" % (status, msg))
+        self.status = status
+
+
+class attn_params(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+        ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+        ("sinks", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libattn36.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libattn36.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(attn_params)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [P, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_fwd_workspace_size.argtypes = [P, i64, i64, i64]
+    lib.attn_bwd.argtypes = [P, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.attn_bwd_workspace_size.argtypes = [P, i64, i64, i64, i32]
+    lib.attn_fwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.attn_fwd_varlen_workspace_size.argtypes = [P, i32, i64, i64, i32, i32]
+    lib.attn_bwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, i32, vp, sz, vp]
+    lib.attn_bwd_varlen_workspace_size.argtypes = [P, i32, i64, i64, i32, i32, i32]
+    for name in EXPORTED:
+        if name.endswith("workspace_size"):
+            getattr(lib, name).restype = ctypes.c_size_t
+        elif name == "attn_last_error":
+            lib.attn_last_error.restype = ctypes.c_char_p
+        else:
+            getattr(lib, name).restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def version() -> int:
+    return int(load_library().attn_version())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return ATTN_BF16
+    if t == torch.float16:
+        return ATTN_FP16
+    if t == torch.float32:
+        return ATTN_FP32
+    raise ValueError("unsupported dtype %s" % t)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=None) -> attn_params:
+    p = attn_params()
+    p.dtype = _dtype_code(q.dtype)
+    p.head_dim = q.shape[-1]
+    p.heads_q = q.shape[-2]
+    p.heads_kv = k.shape[-2]
+    p.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    p.causal = 1 if causal else 0
+    p.window_left, p.window_right = int(window[0]), int(window[1])
+    p.sinks = _ptr(sinks)
+    return p
+
+
+def _check(st):
+    if st != ATTN_OK:
+        raise AttnError(st, last_error())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(nbytes, dev):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, out=None, lse=None):
+    """Batched forward: q [B,Sq,Hq,D], k, v [B,Sk,Hkv,D] -> (o, lse [B,Hq,Sq] fp32)."""
+    lib = load_library()
+    B, sq, hq, d = q.shape
+    sk = k.shape[1]
+    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, hq, sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    n = lib.attn_fwd_workspace_size(ctypes.byref(p), B, sq, sk)
+    ws = _workspace(n, q.device)
+    _check(lib.attn_fwd(ctypes.byref(p), B, sq, sk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                        _ptr(ws), n, _stream(q.device)))
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, softmax_scale=None,
+             grad_dtype=None):
+    """Batched backward -> (dq, dk, dv, dsinks or None)."""
+    lib = load_library()
+    B, sq, hq, d = q.shape
+    sk = k.shape[1]
+    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device)
+    dk = torch.empty(k.shape, dtype=gd, device=q.device)
+    dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    dsinks = torch.empty(hq, dtype=torch.float32, device=q.device) if sinks is not None else None
+    n = lib.attn_bwd_workspace_size(ctypes.byref(p), B, sq, sk, _dtype_code(gd))
+    ws = _workspace(n, q.device)
+    _check(lib.attn_bwd(ctypes.byref(p), B, sq, sk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                        _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _dtype_code(gd),
+                        _ptr(ws), n, _stream(q.device)))
+    return dq, dk, dv, dsinks
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
+                    window=(-1, -1), sinks=None, softmax_scale=None, out=None, lse=None):
+    """Packed forward: q [Tq,Hq,D], k, v [Tk,Hkv,D], int32 cu_seqlens [N+1] -> (o, lse [Hq,Tq])."""
+    lib = load_library()
+    tq, hq, d = q.shape
+    tk = k.shape[0]
+    n = cu_seqlens_q.shape[0] - 1
+    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    nb = lib.attn_fwd_varlen_workspace_size(ctypes.byref(p), n, tq, tk, max_seqlen_q, max_seqlen_k)
+    ws = _workspace(nb, q.device)
+    _check(lib.attn_fwd_varlen(ctypes.byref(p), n, tq, tk, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                               int(max_seqlen_q), int(max_seqlen_k), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(o), _ptr(lse), _ptr(ws), nb, _stream(q.device)))
+    return o, lse
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    causal=False, window=(-1, -1), sinks=None, softmax_scale=None, grad_dtype=None):
+    """Packed backward -> (dq, dk, dv, dsinks or None)."""
+    lib = load_library()
+    tq, hq, d = q.shape
+    tk = k.shape[0]
+    n = cu_seqlens_q.shape[0] - 1
+    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device)
+    dk = torch.empty(k.shape, dtype=gd, device=q.device)
+    dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    dsinks = torch.empty(hq, dtype=torch.float32, device=q.device) if sinks is not None else None
+    nb = lib.attn_bwd_varlen_workspace_size(ctypes.byref(p), n, tq, tk, max_seqlen_q, max_seqlen_k,
+                                            _dtype_code(gd))
+    ws = _workspace(nb, q.device)
+    _check(lib.attn_bwd_varlen(ctypes.byref(p), n, tq, tk, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                               int(max_seqlen_q), int(max_seqlen_k), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(dsinks), _dtype_code(gd), _ptr(ws), nb, _stream(q.device)))
+    return dq, dk, dv, dsinks

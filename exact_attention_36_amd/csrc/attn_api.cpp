@@ -1,0 +1,349 @@
+// attn_api.cpp -- the C ABI: host-side argument checks, work decomposition
+// and kernel launches.  Nothing here reads device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "attn_kernels.h"
+
+using namespace attn;
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+constexpr int64_t OFF_LIMIT = (int64_t)1 << 31;  // byte offsets inside one sequence are 32-bit
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+float resolve_scale(const attn_params* p) {
+  const float s = p->softmax_scale;
+  if (!(s > 0.f) || std::isnan(s)) return 1.0f / std::sqrt((float)p->head_dim);
+  return s;
+}
+
+attn_status check_params(const attn_params* p) {
+  if (!p) return fail(ATTN_EINVAL, "params is NULL");
+  if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16)
+    return fail(ATTN_EINVAL, "dtype must be ATTN_BF16 or ATTN_FP16 (got %d)", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128) {
+    if (p->head_dim > 0 && p->head_dim <= 256 && p->head_dim % 8 == 0)
+      return fail(ATTN_ENOTSUP, "head_dim %d is valid but not built (built: 64, 128)", p->head_dim);
+    return fail(ATTN_EINVAL, "head_dim must be a multiple of 8 in [8, 256] (got %d)", p->head_dim);
+  }
+  if (p->heads_q < 1 || p->heads_kv < 1)
+    return fail(ATTN_EINVAL, "heads_q and heads_kv must be >= 1 (got %d, %d)", p->heads_q, p->heads_kv);
+  if (p->heads_q % p->heads_kv)
+    return fail(ATTN_EINVAL, "heads_kv (%d) must divide heads_q (%d)", p->heads_kv, p->heads_q);
+  if (p->heads_q > FWD_BM && p->heads_q / p->heads_kv > FWD_BM)
+    return fail(ATTN_ENOTSUP, "more than %d q heads per kv head", FWD_BM);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_EINVAL, "window bounds must be >= -1 (got %d, %d)", p->window_left, p->window_right);
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1");
+  return ATTN_OK;
+}
+
+attn_status check_extent(int64_t max_q, int64_t max_k, const attn_params* p) {
+  const int64_t D = p->head_dim;
+  if ((max_q + FWD_BM) * p->heads_q * D * 4 >= OFF_LIMIT)
+    return fail(ATTN_ENOTSUP, "a sequence of %lld queries exceeds the 32-bit offset range", (long long)max_q);
+  if ((max_k + BWD_BN) * p->heads_kv * D * 4 >= OFF_LIMIT)
+    return fail(ATTN_ENOTSUP, "a sequence of %lld keys exceeds the 32-bit offset range", (long long)max_k);
+  return ATTN_OK;
+}
+
+SeqArgs seq_args(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int64_t sq,
+                 int64_t sk, int64_t total_q) {
+  SeqArgs s{};
+  s.cu_q = cu_q;
+  s.cu_k = cu_k;
+  s.nseq = nseq;
+  s.sq = (int32_t)sq;
+  s.sk = (int32_t)sk;
+  s.total_q = (int32_t)total_q;
+  s.hq = p->heads_q;
+  s.hkv = p->heads_kv;
+  s.group = p->heads_q / p->heads_kv;
+  s.causal = p->causal;
+  s.wl = p->window_left;
+  s.wr = p->window_right;
+  return s;
+}
+
+// Split-KV when the grid would not fill the chip and each split keeps >= 8 tiles.
+int choose_split(int64_t base_ctas, int64_t sk) {
+  const int64_t tiles = cdiv(sk, FWD_BN);
+  if (base_ctas >= 512 || tiles < 16) return 1;
+  int64_t n = cdiv(1024, base_ctas);
+  n = std::min<int64_t>(n, tiles / 8);
+  n = std::min<int64_t>(n, 64);
+  return (int)std::max<int64_t>(n, 1);
+}
+
+size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_split_out) {
+  const int G = p->heads_q / p->heads_kv;
+  const int64_t nmb = cdiv(sq * G, FWD_BM);
+  const int ns = choose_split(nmb * p->heads_kv * B, sk);
+  if (n_split_out) *n_split_out = ns;
+  if (ns <= 1) return 0;
+  const int64_t rows = (int64_t)ns * B * p->heads_kv * nmb * FWD_BM;
+  return align_up(rows * p->head_dim * 4) + align_up(rows * 4);
+}
+
+struct BwdWs {
+  size_t dq_acc, delta, lse2, total;
+};
+BwdWs bwd_ws(const attn_params* p, int64_t tq, int32_t grad_dtype) {
+  BwdWs w{};
+  const int64_t rows = tq * p->heads_q;
+  w.dq_acc = grad_dtype == ATTN_FP32 ? 0 : align_up(rows * p->head_dim * 4);
+  w.delta = align_up(rows * 4);
+  w.lse2 = align_up(rows * 4);
+  w.total = w.dq_acc + w.delta + w.lse2;
+  return w;
+}
+
+attn_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(ATTN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+attn_status check_ws(const void* ws, size_t have, size_t need) {
+  if (have < need) return fail(ATTN_EINVAL, "workspace too small: %zu bytes given, %zu needed", have, need);
+  if (need && !ws) return fail(ATTN_EINVAL, "workspace is NULL but %zu bytes are needed", need);
+  if (need && ((uintptr_t)ws % 16)) return fail(ATTN_EINVAL, "workspace must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int64_t sq,
+                    int64_t sk, int64_t total_q, int64_t max_q, const void* q, const void* k, const void* v, void* o,
+                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const bool packed = cu_q != nullptr;
+  FwdArgs a{};
+  a.s = seq_args(p, cu_q, cu_k, nseq, sq, sk, total_q);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.sinks = p->sinks;
+  a.scale_log2 = resolve_scale(p) * 1.4426950408889634f;
+  const int G = a.s.group;
+  a.n_split = 1;
+  if (packed) {
+    a.nblk = (int32_t)((total_q * G) / FWD_BM + nseq);
+    const int64_t ctas = (int64_t)a.nblk * p->heads_kv;
+    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    a.total_ctas = (int32_t)ctas;
+    (void)max_q;
+  } else {
+    a.nmb = (int32_t)cdiv(sq * G, FWD_BM);
+    int ns = 1;
+    const size_t need = fwd_ws(p, nseq, sq, sk, &ns);
+    attn_status st = check_ws(ws, ws_bytes, need);
+    if (st != ATTN_OK) return st;
+    a.n_split = ns;
+    if (ns > 1) {
+      const int64_t rows = (int64_t)ns * nseq * p->heads_kv * a.nmb * FWD_BM;
+      a.o_part = (float*)ws;
+      a.lse_part = (float*)((char*)ws + align_up(rows * p->head_dim * 4));
+    }
+    const int64_t ctas = (int64_t)a.nmb * ns * p->heads_kv * nseq;
+    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    a.total_ctas = (int32_t)ctas;
+  }
+  if (a.total_ctas == 0) return ATTN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  attn_status st = launched(launch_fwd(a, p->head_dim, p->dtype == ATTN_FP16, s));
+  if (st != ATTN_OK || a.n_split <= 1) return st;
+  return launched(launch_fwd_combine(a, p->head_dim, p->dtype == ATTN_FP16, s));
+}
+
+attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int64_t sq,
+                    int64_t sk, int64_t total_q, int64_t total_k, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                    int32_t grad_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const bool packed = cu_q != nullptr;
+  const int64_t tq = packed ? total_q : nseq * sq;
+  const BwdWs w = bwd_ws(p, tq, grad_dtype);
+  attn_status st = check_ws(ws, ws_bytes, w.total);
+  if (st != ATTN_OK) return st;
+  BwdArgs a{};
+  a.s = seq_args(p, cu_q, cu_k, nseq, sq, sk, total_q);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.sinks = p->sinks;
+  a.dsinks = dsinks;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.grad_f32 = grad_dtype == ATTN_FP32;
+  char* wp = (char*)ws;
+  a.dq_acc = a.grad_f32 ? (float*)dq : (float*)wp;
+  wp += w.dq_acc;
+  a.delta = (float*)wp;
+  wp += w.delta;
+  a.lse2 = (float*)wp;
+  const float scale = resolve_scale(p);
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (packed) {
+    a.nblk = (int32_t)(total_k / BWD_BN + nseq);
+    const int64_t ctas = (int64_t)a.nblk * p->heads_kv;
+    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    a.total_ctas = (int32_t)ctas;
+  } else {
+    a.nkb = (int32_t)cdiv(sk, BWD_BN);
+    const int64_t ctas = (int64_t)a.nkb * p->heads_kv * nseq;
+    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    a.total_ctas = (int32_t)ctas;
+  }
+  return launched(launch_bwd(a, p->head_dim, p->dtype == ATTN_FP16, (hipStream_t)stream));
+}
+
+attn_status check_grad_dtype(const attn_params* p, int32_t grad_dtype) {
+  if (grad_dtype != p->dtype && grad_dtype != ATTN_FP32)
+    return fail(ATTN_EINVAL, "grad_dtype must be the input dtype or ATTN_FP32 (got %d)", grad_dtype);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err; }
+
+int32_t attn_version(void) { return 100; }
+
+size_t attn_fwd_workspace_size(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k) {
+  if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1 || seqlen_k < 1) return 0;
+  return fwd_ws(p, batch, seqlen_q, seqlen_k, nullptr);
+}
+
+size_t attn_bwd_workspace_size(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
+                               int32_t grad_dtype) {
+  (void)seqlen_k;
+  if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1) return 0;
+  return bwd_ws(p, batch * seqlen_q, grad_dtype).total;
+}
+
+size_t attn_fwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                                      int32_t max_seqlen_q, int32_t max_seqlen_k) {
+  (void)p;
+  (void)num_seqs;
+  (void)total_q;
+  (void)total_k;
+  (void)max_seqlen_q;
+  (void)max_seqlen_k;
+  return 0;
+}
+
+size_t attn_bwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t grad_dtype) {
+  (void)num_seqs;
+  (void)total_k;
+  (void)max_seqlen_q;
+  (void)max_seqlen_k;
+  if (check_params(p) != ATTN_OK || total_q < 0) return 0;
+  return bwd_ws(p, total_q, grad_dtype).total;
+}
+
+attn_status attn_fwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
+                     const void* k, const void* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if (batch < 1 || seqlen_q < 1 || seqlen_k < 1)
+    return fail(ATTN_EINVAL, "batch, seqlen_q, seqlen_k must be >= 1 (got %lld, %lld, %lld)", (long long)batch,
+                (long long)seqlen_q, (long long)seqlen_k);
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_EINVAL, "q, k, v, o and lse must be non-NULL");
+  if ((st = check_extent(seqlen_q, seqlen_k, p)) != ATTN_OK) return st;
+  if (batch * seqlen_q * (p->heads_q / p->heads_kv) >= INT32_MAX || batch >= INT32_MAX)
+    return fail(ATTN_ENOTSUP, "problem too large");
+  return run_fwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, seqlen_q, q, k, v, o,
+                 lse, ws, ws_bytes, stream);
+}
+
+attn_status attn_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
+                     const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                     void* dk, void* dv, float* dsinks, int32_t grad_dtype, void* ws, size_t ws_bytes,
+                     void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if ((st = check_grad_dtype(p, grad_dtype)) != ATTN_OK) return st;
+  if (batch < 1 || seqlen_q < 1 || seqlen_k < 1)
+    return fail(ATTN_EINVAL, "batch, seqlen_q, seqlen_k must be >= 1 (got %lld, %lld, %lld)", (long long)batch,
+                (long long)seqlen_q, (long long)seqlen_k);
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(ATTN_EINVAL, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
+  if (p->sinks && !dsinks) return fail(ATTN_EINVAL, "dsinks must be non-NULL when sinks are given");
+  if ((st = check_extent(seqlen_q, seqlen_k, p)) != ATTN_OK) return st;
+  if (batch * seqlen_q * (p->heads_q / p->heads_kv) >= INT32_MAX || batch >= INT32_MAX)
+    return fail(ATTN_ENOTSUP, "problem too large");
+  return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k, q, k,
+                 v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ws_bytes, stream);
+}
+
+static attn_status check_varlen(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                                const int32_t* cu_q, const int32_t* cu_k, int32_t max_q, int32_t max_k) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if (num_seqs < 1) return fail(ATTN_EINVAL, "num_seqs must be >= 1 (got %d)", num_seqs);
+  if (total_q < 0 || total_k < 0) return fail(ATTN_EINVAL, "total_q and total_k must be >= 0");
+  if (!cu_q || !cu_k) return fail(ATTN_EINVAL, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (max_q < 0 || max_k < 0) return fail(ATTN_EINVAL, "max_seqlen_q and max_seqlen_k must be >= 0");
+  if ((st = check_extent(max_q, max_k, p)) != ATTN_OK) return st;
+  const int64_t G = p->heads_q / p->heads_kv;
+  if ((total_q * G) / FWD_BM + num_seqs >= INT32_MAX / p->heads_kv || total_q >= INT32_MAX ||
+      total_k >= INT32_MAX)
+    return fail(ATTN_ENOTSUP, "problem too large");
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_varlen(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                            const int32_t* cu_q, const int32_t* cu_k, int32_t max_q, int32_t max_k, const void* q,
+                            const void* k, const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+  attn_status st = check_varlen(p, num_seqs, total_q, total_k, cu_q, cu_k, max_q, max_k);
+  if (st != ATTN_OK) return st;
+  if ((total_q > 0 && (!q || !o || !lse)) || (total_k > 0 && (!k || !v)))
+    return fail(ATTN_EINVAL, "q, k, v, o and lse must be non-NULL");
+  (void)ws;
+  (void)ws_bytes;
+  if (total_q == 0) return ATTN_OK;
+  return run_fwd(p, cu_q, cu_k, num_seqs, 0, 0, total_q, max_q, q, k, v, o, lse, nullptr, 0, stream);
+}
+
+attn_status attn_bwd_varlen(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
+                            const int32_t* cu_q, const int32_t* cu_k, int32_t max_q, int32_t max_k, const void* q,
+                            const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv, float* dsinks, int32_t grad_dtype, void* ws,
+                            size_t ws_bytes, void* stream) {
+  attn_status st = check_varlen(p, num_seqs, total_q, total_k, cu_q, cu_k, max_q, max_k);
+  if (st != ATTN_OK) return st;
+  if ((st = check_grad_dtype(p, grad_dtype)) != ATTN_OK) return st;
+  if ((total_q > 0 && (!q || !o || !lse || !dout || !dq)) || (total_k > 0 && (!k || !v || !dk || !dv)))
+    return fail(ATTN_EINVAL, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
+  if (p->sinks && !dsinks) return fail(ATTN_EINVAL, "dsinks must be non-NULL when sinks are given");
+  return run_bwd(p, cu_q, cu_k, num_seqs, 0, 0, total_q, total_k, q, k, v, o, lse, dout, dq, dk, dv, dsinks,
+                 grad_dtype, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

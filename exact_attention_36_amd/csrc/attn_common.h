@@ -1,0 +1,87 @@
+// attn_common.h -- sequence geometry and the causal / sliding-window band,
+// shared by the forward and backward kernels.
+#pragma once
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+struct SeqInfo {
+  int q0, lq, k0, lk;  // first token and length of the sequence in q and in k/v
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const SeqArgs& s, int seq) {
+  SeqInfo r;
+  if (s.cu_q) {
+    r.q0 = s.cu_q[seq];
+    r.lq = s.cu_q[seq + 1] - r.q0;
+    r.k0 = s.cu_k[seq];
+    r.lk = s.cu_k[seq + 1] - r.k0;
+  } else {
+    r.q0 = seq * s.sq;
+    r.lq = s.sq;
+    r.k0 = seq * s.sk;
+    r.lk = s.sk;
+  }
+  return r;
+}
+
+// Keys visible to query i: [kmin(i), kmax(i)] (empty when kmax < kmin).
+// Causal and window bounds are aligned bottom-right: query i lines up with
+// key i + lk - lq (fa4-jax page, bottom-right alignment paragraph; window
+// interval of the flash_attn_func docstring, vllm-project/flash-attention
+// README on the GitHub search page).  Both bounds are nondecreasing in i.
+struct Band {
+  int wl, wr, causal, delta, lk;
+  __device__ __forceinline__ Band(const SeqArgs& s, const SeqInfo& si)
+      : wl(s.wl), wr(s.wr), causal(s.causal), delta(si.lk - si.lq), lk(si.lk) {}
+  __device__ __forceinline__ int kmin(int i) const { return wl >= 0 ? max(0, i + delta - wl) : 0; }
+  __device__ __forceinline__ int kmax(int i) const {
+    int hi = lk - 1;
+    if (causal) hi = min(hi, i + delta + (wr >= 0 ? min(0, wr) : 0));
+    else if (wr >= 0) hi = min(hi, i + delta + wr);
+    return hi;
+  }
+};
+
+// Queries that see key j: [qmin(j), qmax(j)], the inverse of the band.
+// Used by the key-major backward to visit only the query blocks that see a
+// key block.
+struct QBand {
+  int wl, wr, causal, delta, lq;
+  __device__ __forceinline__ QBand(const SeqArgs& s, const SeqInfo& si)
+      : wl(s.wl), wr(s.wr), causal(s.causal), delta(si.lk - si.lq), lq(si.lq) {}
+  // j <= i + delta + r  <=>  i >= j - delta - r   (r = effective right offset)
+  __device__ __forceinline__ int qmin(int j) const {
+    int r = causal ? (wr >= 0 ? min(0, wr) : 0) : wr;
+    if (!causal && wr < 0) return 0;
+    return max(0, j - delta - r);
+  }
+  // j >= i + delta - wl  <=>  i <= j - delta + wl
+  __device__ __forceinline__ int qmax(int j) const { return wl >= 0 ? min(lq - 1, j - delta + wl) : lq - 1; }
+};
+
+// Packed-batch block start of sequence i: floor(cu[i] * G / BM) + i, so a
+// sequence's blocks start right after the previous sequence's and a batch of
+// empty or short sequences costs what its tokens do (dew-flash-attn page, the
+// packed-backward paragraph).
+__device__ __forceinline__ int packed_block_start(const int32_t* cu, int i, int G, int BM) {
+  return (int)(((int64_t)cu[i] * G) / BM) + i;
+}
+
+// Largest i in [0, n) with packed_block_start(i) <= t (block starts are
+// strictly increasing, and start(0) = 0).
+__device__ __forceinline__ int find_sequence(const int32_t* cu, int n, int t, int G, int BM) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (packed_block_start(cu, mid, G, BM) <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace attn

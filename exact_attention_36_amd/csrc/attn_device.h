@@ -1,0 +1,145 @@
+// attn_device.h -- gfx950 device helpers shared by the attention kernels:
+// MFMA operand types, buffer resources (hardware bounds checks: loads past
+// the end return 0, stores past the end are dropped), LDS swizzle, the
+// transposing LDS read, cross-half wave reductions and 16-bit conversions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_{bf16,f16}: A is 32(M) x 16(K), B is 16(K) x 32(N).
+// Lane l holds A[m = l%32][k = 8*(l/32) .. +7] and B[k = 8*(l/32) .. +7][n = l%32];
+// accumulator register i of lane l is C[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32].
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+// Two floats -> two 16-bit values packed in one dword, round to nearest even.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (F16) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  } else {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+}
+
+template <bool F16>
+__device__ __forceinline__ float to_f32(uint16_t h) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, h);
+  else return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// ---------------------------------------------------------------- buffer resources
+// Raw buffer with `bytes` valid bytes from `base`; dword 3 is the gfx9-family
+// default (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+// 16 bytes straight from global memory into LDS: lane l's bytes land at
+// lds_base + 16*l (lds_base must be wave-uniform).
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_base), 16, off, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A [rows][D] 16-bit tile is stored with 16-byte chunk c of row r at chunk
+// position c ^ swz(r).  The two access patterns of the kernels -- 16 lanes
+// reading one chunk of 16 consecutive rows, and the transposing read of 4
+// consecutive rows x 4 consecutive chunks by 32 lanes -- then touch every
+// one of the 64 banks exactly once.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ constexpr int tile_off(int r, int chunk) {  // byte offset of a chunk
+  return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes every lane supplies the address of 4 consecutive 16-bit values; lane
+// i receives, as its element e (e = 0..3), value i%4 of the 4 values
+// addressed by lane 4e + i/4.  With lane 4e+j pointing at row kbase+e,
+// columns cbase+4j .. +3 of a row-major tile, lane i therefore receives
+// column cbase+i of rows kbase .. kbase+3.
+__device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const void* p) { return *LDS_PTR(const u32x4, p); }
+
+// ---------------------------------------------------------------- wave reductions
+// Lanes l and l^32 exchange a value; returns op(own, partner) on every lane.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------- scheduling
+// Workgroups are dealt to the 8 XCDs round robin.  Renumber them so that
+// each XCD receives a contiguous range of logical ids (neighbouring tiles that
+// share K/V then share an L2).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = id % 8, slot = id / 8;
+  // XCDs < rem own per+1 logical ids, the others own per.
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
+}
+
+}  // namespace attn

@@ -1,0 +1,322 @@
+// attn_fwd.hip -- fused exact-attention forward for gfx950.
+//
+// One pass over the visible K/V tiles with an online softmax: the running
+// row max m and row sum l are rescaled by exp(m_old - m_new) as each tile is
+// merged, so the output and the per-row log-sum-exp are written once
+// (GitHub search page, gitctrlx/flash-attention-tutorial README, sections 3
+// "Online Softmax", 4 and 5 "Flash Attention (With Tiling)").  Keys outside
+// the causal / sliding-window band are skipped a whole tile at a time
+// (fa4-jax page, the two-sided sliding window item).  Attention sinks add
+// one value-less logit per q head to each row's denominator, which scales
+// the output by sigmoid(lse - sink) (dew-flash-attn page, sinks paragraph).
+//
+// Work tile: 128 packed query rows (the G q heads of one kv head, query
+// major) x one kv head x one sequence, 4 waves of 32 rows each.  Each wave
+// computes S^T = K Q^T with v_mfma_f32_32x32x16 so that a lane owns one
+// query row: the row max needs one cross-half exchange and the row sum
+// none until the end, and the output O^T = V^T P^T keeps the same lane
+// ownership, so the rescale by alpha is lane-local.  P never leaves
+// registers.  K/V tiles of 64 keys are streamed global -> LDS directly
+// (buffer_load ... lds), double buffered, in an XOR-swizzled layout that the
+// 16-byte K reads and the transposing V reads (ds_read_b64_tr_b16) both hit
+// without bank conflicts.
+//
+// Split-KV (decode shapes): the visible tiles of a work tile are divided
+// among n_split workgroups, each writing a normalised fp32 partial output
+// and its log-sum-exp; a combine kernel merges them with weights
+// exp(lse_s - lse) (vllm-project/flash-attention README on the GitHub search
+// page, "2.2: Optimize for inference").
+#include "attn_common.h"
+
+namespace attn {
+
+template <int D, bool F16>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(const FwdArgs a) {
+  constexpr int KS = D / 16;               // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;               // 32-wide blocks of the head dim
+  constexpr int ROWB = D * 2;              // bytes per K/V row
+  constexpr int TILE = FWD_BN * ROWB;      // bytes per K (or V) tile
+  constexpr int SLABS = TILE / 1024 / 4;   // 1 KB wave-loads per tile per wave
+  constexpr int KB = FWD_BN / 32;          // 32-key blocks per tile
+  constexpr int PT = FWD_BN / 16;          // 16-key MFMA steps per tile
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 V0 K1 V1
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int G = a.s.group;
+  const int id = xcd_remap(blockIdx.x, a.total_ctas);
+
+  // ---- which work tile
+  int seq, g, mb, sp = 0;
+  if (a.s.cu_q) {
+    g = id / a.nblk;
+    const int t = id - g * a.nblk;
+    seq = find_sequence(a.s.cu_q, a.s.nseq, t, G, FWD_BM);
+    mb = t - packed_block_start(a.s.cu_q, seq, G, FWD_BM);
+  } else {
+    const int mbi = id % a.nmb;
+    int r = id / a.nmb;
+    sp = r % a.n_split;
+    r /= a.n_split;
+    g = r % a.s.hkv;
+    seq = r / a.s.hkv;
+    mb = a.nmb - 1 - mbi;  // causal: the longest tiles start first
+  }
+  const SeqInfo si = seq_info(a.s, seq);
+  const int prows = si.lq * G;
+  const int p0 = mb * FWD_BM;
+  if (p0 >= prows) return;  // idle slot of the packed grid (whole workgroup)
+
+  const Band band(a.s, si);
+  const int i_lo = p0 / G, i_hi = (min(p0 + FWD_BM, prows) - 1) / G;
+  const int kv_lo = band.kmin(i_lo), kv_hi = band.kmax(i_hi);
+  int t_begin = 0, t_end = 0;
+  if (kv_hi >= kv_lo) {
+    t_begin = kv_lo / FWD_BN;
+    t_end = kv_hi / FWD_BN + 1;
+  }
+  if (a.n_split > 1) {
+    const int per = (t_end - t_begin + a.n_split - 1) / a.n_split;
+    const int b0 = t_begin + sp * per;
+    t_end = min(t_end, b0 + per);
+    t_begin = min(b0, t_end);
+  }
+  // Tiles inside [full_lo, full_hi] are visible to every row of the work tile.
+  const int full_lo = band.kmin(i_hi), full_hi = band.kmax(i_lo);
+
+  // ---- this lane's query row
+  const int my_p = p0 + wave * 32 + l32;
+  const int my_i = my_p / G;
+  const int my_hl = my_p - my_i * G;
+  const int my_h = g * G + my_hl;
+  const int my_kmin = band.kmin(my_i), my_kmax = band.kmax(my_i);
+
+  const int64_t qrow = (int64_t)a.s.hq * D;   // elements per q/o token
+  const int64_t krow = (int64_t)a.s.hkv * D;  // elements per k/v token
+  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * D;
+  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 2) : 0u;
+  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * D) * 2);
+  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
+  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2) : 0u;
+  const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
+  const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
+  const auto rv = make_rsrc((const uint16_t*)a.v + kbase_e, kbytes);
+
+  // Q^T as the B operand: lane holds 8 consecutive dims of its query row per k-step.
+  u32x4 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; s++) qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+
+  auto load_tile = [&](int t, int buf) {
+    char* kd = smem + buf * 2 * TILE;
+    char* vd = kd + TILE;
+#pragma unroll
+    for (int n = 0; n < SLABS; n++) {
+      const int slab = wave * SLABS + n;
+      const int byte = slab * 1024 + lane * 16;
+      const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
+      const int c = pos ^ swz<D>(r);
+      const uint32_t goff = (uint32_t)((((int64_t)(t * FWD_BN + r)) * krow + c * 8) * 2);
+      buf_load_lds16(rk, kd + slab * 1024, goff);
+      buf_load_lds16(rv, vd + slab * 1024, goff);
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; d++) acc[d] = f32x16{};
+  float m_run = -INFINITY, l_part = 0.f;
+  const float c = a.scale_log2;
+
+  // transposing-read geometry of this lane (V^T as the A operand)
+  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
+
+  if (t_begin < t_end) load_tile(t_begin, 0);
+  for (int t = t_begin; t < t_end; t++) {
+    const int buf = (t - t_begin) & 1;
+    wait_vmcnt<0>();                 // this lane's part of tile t is in LDS
+    __builtin_amdgcn_s_barrier();    // everyone's part, and everyone is done with tile t-1
+    if (t + 1 < t_end) load_tile(t + 1, buf ^ 1);
+    const char* kt = smem + buf * 2 * TILE;
+    const char* vt = kt + TILE;
+
+    // S^T = K Q^T (raw scores; the scale is folded into the exponent)
+    f32x16 st[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++) {
+      st[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; s++)
+        st[kb] = mfma32<F16>(lds_read16(kt + tile_off<D>(kb * 32 + l32, 2 * s + hh)), qf[s], st[kb]);
+    }
+
+    const int j0 = t * FWD_BN;
+    if (!(j0 >= full_lo && j0 + FWD_BN - 1 <= full_hi)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (j < my_kmin || j > my_kmax) st[kb][i] = -INFINITY;
+        }
+    }
+
+    // online softmax update
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, st[kb][i]);
+    mx = half_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2_fast((m_run - m_use) * c);
+    m_run = m_new;
+    const float mc = m_use * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float p = exp2_fast(fmaf(st[kb][i], c, -mc));
+        st[kb][i] = p;
+        rs += p;
+      }
+    l_part = fmaf(l_part, alpha, rs);
+#pragma unroll
+    for (int d = 0; d < DB; d++) acc[d] *= alpha;
+
+    // P^T as the B operand: k-step u of block kb covers keys
+    // kb*32 + 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}, which are exactly the
+    // accumulator registers 8u..8u+7 of this lane.
+    u32x4 pf[PT];
+#pragma unroll
+    for (int t2 = 0; t2 < PT; t2++) {
+      const int kb = t2 >> 1, u = t2 & 1;
+      pf[t2] = u32x4{pack2<F16>(st[kb][8 * u + 0], st[kb][8 * u + 1]),
+                     pack2<F16>(st[kb][8 * u + 2], st[kb][8 * u + 3]),
+                     pack2<F16>(st[kb][8 * u + 4], st[kb][8 * u + 5]),
+                     pack2<F16>(st[kb][8 * u + 6], st[kb][8 * u + 7])};
+    }
+    // O^T += V^T P^T, V^T read with the same key order as P.
+#pragma unroll
+    for (int d = 0; d < DB; d++) {
+      const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+#pragma unroll
+      for (int t2 = 0; t2 < PT; t2++) {
+        const int kbase = t2 * 16 + 4 * hh + esrc;
+        const u32x2 a1 = lds_read_tr(vt + tile_off<D>(kbase, col >> 3) + (jsrc & 1) * 8);
+        const u32x2 a2 = lds_read_tr(vt + tile_off<D>(kbase + 8, col >> 3) + (jsrc & 1) * 8);
+        acc[d] = mfma32<F16>(u32x4{a1[0], a1[1], a2[0], a2[1]}, pf[t2], acc[d]);
+      }
+    }
+  }
+
+  // ---- epilogue
+  const float l_tot = half_sum(l_part);
+  const float lse_v = l_tot > 0.f ? (m_run * c + log2_fast(l_tot)) * LN2 : -INFINITY;
+  const bool row_ok = my_p < prows;
+
+  if (a.n_split > 1) {
+    const int64_t pidx = ((int64_t)(sp * a.s.nseq + seq) * a.s.hkv + g) * ((int64_t)a.nmb * FWD_BM) + my_p;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* op = a.o_part + pidx * D;
+#pragma unroll
+    for (int d = 0; d < DB; d++)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const int dd = d * 32 + 8 * j4 + 4 * hh;
+        *(f32x4*)(op + dd) = f32x4{acc[d][4 * j4] * inv, acc[d][4 * j4 + 1] * inv, acc[d][4 * j4 + 2] * inv,
+                                   acc[d][4 * j4 + 3] * inv};
+      }
+    if (hh == 0) a.lse_part[pidx] = lse_v;
+    return;
+  }
+
+  float denom = l_tot;
+  if (a.sinks && l_tot > 0.f) denom += exp2_fast(fmaf(a.sinks[my_h], LOG2E, -m_run * c));
+  const float inv = l_tot > 0.f ? 1.f / denom : 0.f;
+  const auto ro = make_rsrc((uint16_t*)a.o + qbase_e, qbytes);
+#pragma unroll
+  for (int d = 0; d < DB; d++)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; j4++) {
+      const int dd = d * 32 + 8 * j4 + 4 * hh;
+      const u32x2 w{pack2<F16>(acc[d][4 * j4] * inv, acc[d][4 * j4 + 1] * inv),
+                    pack2<F16>(acc[d][4 * j4 + 2] * inv, acc[d][4 * j4 + 3] * inv)};
+      buf_store8(w, ro, qoff + (uint32_t)(dd * 2));
+    }
+  if (hh == 0 && row_ok) {
+    const int64_t li_ = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
+                                 : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
+    a.lse[li_] = lse_v;
+  }
+}
+
+// Merge split-KV partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s,
+// then the sink gate sigmoid(lse - sink).  One wave per packed row.
+template <int D, bool F16>
+__global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rows_bg = a.nmb * FWD_BM;
+  const int64_t total = (int64_t)a.s.nseq * a.s.hkv * rows_bg;
+  if (row >= total) return;
+  const int p = (int)(row % rows_bg);
+  const int r = (int)(row / rows_bg);
+  const int g = r % a.s.hkv, seq = r / a.s.hkv;
+  const int G = a.s.group;
+  const SeqInfo si = seq_info(a.s, seq);
+  if (p >= si.lq * G) return;
+  const int i = p / G, hl = p - i * G, h = g * G + hl;
+  const int64_t split_stride = (int64_t)a.s.nseq * a.s.hkv * rows_bg;
+
+  float mx = -INFINITY;
+  for (int s = 0; s < a.n_split; s++) mx = fmaxf(mx, a.lse_part[row + s * split_stride]);
+  float sum = 0.f;
+  if (mx != -INFINITY)
+    for (int s = 0; s < a.n_split; s++) sum += exp2_fast((a.lse_part[row + s * split_stride] - mx) * LOG2E);
+  const float lse = mx == -INFINITY ? -INFINITY : mx + log2_fast(sum) * LN2;
+  float o[PER] = {};
+  if (mx != -INFINITY) {
+    for (int s = 0; s < a.n_split; s++) {
+      const float w = exp2_fast((a.lse_part[row + s * split_stride] - lse) * LOG2E);
+      const float* op = a.o_part + (row + s * split_stride) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; e++) o[e] = fmaf(w, op[e], o[e]);
+    }
+  }
+  float gate = mx == -INFINITY ? 0.f : 1.f;
+  if (a.sinks && mx != -INFINITY) gate = 1.f / (1.f + exp2_fast((a.sinks[h] - lse) * LOG2E));
+  uint16_t* ob = (uint16_t*)a.o + ((int64_t)(si.q0 + i) * a.s.hq + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; e += 2) *(uint32_t*)(ob + e) = pack2<F16>(o[e] * gate, o[e + 1] * gate);
+  if (lane == 0) a.lse[((int64_t)seq * a.s.hq + h) * a.s.sq + i] = lse;
+}
+
+template <int D, bool F16>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((fwd_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f16, hipStream_t st) {
+  if (head_dim == 128) return f16 ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);
+  return f16 ? launch_fwd_t<64, true>(a, st) : launch_fwd_t<64, false>(a, st);
+}
+
+template <int D, bool F16>
+static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t st) {
+  const int64_t rows = (int64_t)a.s.nseq * a.s.hkv * a.nmb * FWD_BM;
+  hipLaunchKernelGGL((fwd_combine_kernel<D, F16>), dim3((unsigned)((rows + 3) / 4)), dim3(THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine(const FwdArgs& a, int head_dim, bool f16, hipStream_t st) {
+  if (head_dim == 128) return f16 ? launch_combine_t<128, true>(a, st) : launch_combine_t<128, false>(a, st);
+  return f16 ? launch_combine_t<64, true>(a, st) : launch_combine_t<64, false>(a, st);
+}
+
+}  // namespace attn

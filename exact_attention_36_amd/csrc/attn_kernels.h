@@ -1,0 +1,67 @@
+// attn_kernels.h -- kernel argument blocks and launchers (host <-> device
+// contract inside the library; not part of the public C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Rows of one work tile.  Query rows of the kv group g are packed
+// query-major: packed row p is query p / G of q head g*G + p % G, so a tile
+// of FWD_BM packed rows reads each K/V byte once for all G heads.
+constexpr int FWD_BM = 128;     // packed query rows per forward workgroup
+constexpr int FWD_BN = 64;      // keys per K/V tile
+constexpr int BWD_BN = 128;     // keys per backward workgroup
+constexpr int BWD_BM = 32;      // packed query rows per backward step
+constexpr int THREADS = 256;    // 4 wave64s
+
+// Sequence geometry shared by all kernels.  Batched problems have
+// cu_q == nullptr: sequence b starts at token b*sq (queries) and b*sk (keys).
+struct SeqArgs {
+  const int32_t* cu_q;   // [nseq+1] or nullptr
+  const int32_t* cu_k;   // [nseq+1] or nullptr
+  int32_t nseq;
+  int32_t sq, sk;        // per-sequence lengths in batched mode
+  int32_t total_q;       // tokens of q (lse row stride in packed mode)
+  int32_t hq, hkv, group;
+  int32_t causal, wl, wr;  // window bounds, -1 = unbounded
+};
+
+struct FwdArgs {
+  SeqArgs s;
+  const void* q; const void* k; const void* v;
+  void* o; float* lse;
+  const float* sinks;     // [hq] or nullptr
+  float* o_part;          // split-KV partial outputs (fp32) or nullptr
+  float* lse_part;        // split-KV partial log-sum-exps
+  float scale_log2;       // softmax scale * log2(e)
+  int32_t nmb;            // m-blocks per (sequence, kv head) in batched mode
+  int32_t nblk;           // linear blocks per kv head in packed mode
+  int32_t n_split;
+  int32_t total_ctas;
+};
+
+struct BwdArgs {
+  SeqArgs s;
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  const float* lse;       // sink-free log-sum-exp from the forward
+  const float* sinks;     // [hq] or nullptr
+  float* dsinks;          // [hq] or nullptr
+  float* dq_acc;          // fp32 [tokens_q][hq][D] accumulator
+  float* delta;           // fp32, laid out like lse: D_i = <dO_i, O_i>
+  float* lse2;            // fp32, laid out like lse: log-sum-exp with the sink, in log2 units
+  void* dq; void* dk; void* dv;
+  int32_t grad_f32;       // gradients written as fp32 (else the input dtype)
+  float scale;            // softmax scale
+  float scale_log2;       // scale * log2(e)
+  int32_t nkb;            // kv-blocks per (sequence, kv head) in batched mode
+  int32_t nblk;           // linear kv blocks per kv head in packed mode
+  int32_t total_ctas;
+};
+
+// Launchers (defined in the .hip files).  Return hipGetLastError().
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f16, hipStream_t st);
+hipError_t launch_fwd_combine(const FwdArgs& a, int head_dim, bool f16, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool f16, hipStream_t st);
+
+}  // namespace attn

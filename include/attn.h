@@ -1,0 +1,162 @@
+/*
+ * attn.h -- C ABI of the gfx950 fused exact-attention library (libattn36.so).
+ *
+ * The library computes exact scaled-dot-product attention,
+ *     O = softmax(scale * Q K^T + mask) V,
+ * in one tiled pass with an online softmax, and its backward pass by
+ * recomputing the probabilities from the saved per-row log-sum-exp
+ * (GitHub search page, gitctrlx/flash-attention-tutorial README: sections
+ * 1 "Standard Self-Attention", 3 "Online Softmax", 5 "Flash Attention (With
+ * Tiling)" and 6 "Flash Attention Backward Pass").
+ *
+ * Semantics (all four entry points):
+ *  - Inputs are bf16 or fp16, head dim 64 or 128 (fa4-jax page, restrictions
+ *    paragraph, allows multiples of 8 up to 256; this build covers 64 and 128).
+ *  - Grouped-query attention: heads_q % heads_kv == 0 and q head h reads kv
+ *    head h / (heads_q / heads_kv) (flash_attn_func docstring, 6/2-head
+ *    example, vllm-project/flash-attention README on the GitHub search page;
+ *    dew-flash-attn page, grouped-query sentence).
+ *  - Causal masking and the two-sided sliding window (left, right) are
+ *    aligned bottom-right: query i of a sequence with Lq queries and Lk keys
+ *    sees key j iff  (!causal || j <= i + Lk - Lq)
+ *                 && (left  == -1 || j >= i + Lk - Lq - left)
+ *                 && (right == -1 || j <= i + Lk - Lq + right)
+ *    (fa4-jax page, bottom-right alignment paragraph; window interval of the
+ *    flash_attn_func docstring; dew-flash-attn page, window_size paragraph).
+ *    A row that sees no key gets output 0 and log-sum-exp -inf (same
+ *    docstring: an all-zero mask row gives zero output).
+ *  - Attention sinks: one fp32 logit per q head joins each row's softmax
+ *    denominator with no value, which multiplies the row's output by
+ *    sigmoid(lse - sink); the returned lse is the sink-free one, and the
+ *    backward returns d(loss)/d(sink) (dew-flash-attn page, sinks paragraph).
+ *  - Packed variable-length batches: [T, H, D] tensors with int32 offsets
+ *    cu_seqlens [N+1] from 0 to T; attention never crosses sequences; the
+ *    mask applies per sequence with that sequence's own Lq, Lk; zero-length
+ *    sequences are allowed; the lse of a packed call is laid out [Hq, T_q]
+ *    (fa4-jax page, varlen semantics paragraph).  cu_seqlens contents are NOT
+ *    checked: they must be nondecreasing, start at 0 and end at the token
+ *    count.  The grid covers only the batch's real blocks: sequence i's blocks
+ *    start at floor(cu_seqlens[i] * G / 128) + i and a workgroup finds its
+ *    sequence by binary search (dew-flash-attn page, packed-backward
+ *    paragraph).
+ *
+ * Layouts (all contiguous, last dim stride 1):
+ *   batched:  q, o, dout, dq   [B, Sq, Hq, D];  k, v, dk, dv  [B, Sk, Hkv, D]
+ *             lse              fp32 [B, Hq, Sq]
+ *   packed:   q, o, dout, dq   [Tq, Hq, D];     k, v, dk, dv  [Tk, Hkv, D]
+ *             lse              fp32 [Hq, Tq]
+ *   sinks, dsinks              fp32 [Hq]
+ *
+ * Ownership: every pointer except `params` is device memory owned by the
+ * caller; the library allocates nothing and keeps no device state.  Scratch
+ * memory is the caller's `workspace` of at least the size the matching
+ * *_workspace_size function returns (0 is allowed when that size is 0).
+ * Work is enqueued on `stream` (a hipStream_t, NULL = the default stream);
+ * calls return without synchronising.  Concurrent calls are safe if they
+ * use distinct workspaces and outputs.
+ *
+ * Errors: a status code is returned and a message is kept per thread
+ * (attn_last_error).  Argument checks run on the host before anything is
+ * launched and never read device memory.  Nothing aborts or prints.
+ */
+#ifndef ATTN36_H
+#define ATTN36_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,   /* bad argument: null pointer, bad shape, Hq % Hkv != 0,
+                          window < -1, workspace too small, bad dtype */
+    ATTN_ENOTSUP = 2,  /* valid request outside this build: head dim not 64/128,
+                          sizes whose byte offsets exceed 2^31 */
+    ATTN_EHIP = 3      /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 } attn_dtype;
+
+typedef struct {
+    int32_t dtype;          /* ATTN_BF16 or ATTN_FP16: q, k, v, o, dout */
+    int32_t head_dim;       /* D: 64 or 128 */
+    int32_t heads_q;        /* Hq */
+    int32_t heads_kv;       /* Hkv, divides Hq */
+    float softmax_scale;    /* <= 0 or NaN selects 1/sqrt(D) */
+    int32_t causal;         /* 0 or 1 */
+    int32_t window_left;    /* >= -1; -1 = unbounded */
+    int32_t window_right;   /* >= -1; -1 = unbounded */
+    const float *sinks;     /* device fp32 [Hq] or NULL */
+} attn_params;
+
+/*
+ * Forward, batched [B,S,H,D].  Writes o (input dtype) and lse (fp32).
+ * seqlen_q, seqlen_k >= 1, batch >= 1.  Decode-shaped calls (few query rows
+ * per kv head, long seqlen_k) split the keys among workgroups and need
+ * workspace; see attn_fwd_workspace_size.
+ */
+attn_status attn_fwd(const attn_params *params, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
+                     const void *q, const void *k, const void *v, void *o, float *lse,
+                     void *workspace, size_t workspace_bytes, void *stream);
+size_t attn_fwd_workspace_size(const attn_params *params, int64_t batch, int64_t seqlen_q,
+                               int64_t seqlen_k);
+
+/*
+ * Backward, batched.  Inputs are the forward's q, k, v, o and lse plus the
+ * output gradient dout.  Writes dq [B,Sq,Hq,D], dk, dv [B,Sk,Hkv,D] as
+ * grad_dtype (the input dtype, or ATTN_FP32 for fp32 gradients) and, when
+ * params->sinks is set, dsinks (fp32 [Hq], must then be non-NULL).
+ * dK/dV of a kv head sum over the q heads that share it (fa4-jax page,
+ * restrictions paragraph: fp32 accumulation across the q heads).
+ */
+attn_status attn_bwd(const attn_params *params, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
+                     const void *q, const void *k, const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, float *dsinks,
+                     int32_t grad_dtype, void *workspace, size_t workspace_bytes, void *stream);
+size_t attn_bwd_workspace_size(const attn_params *params, int64_t batch, int64_t seqlen_q,
+                               int64_t seqlen_k, int32_t grad_dtype);
+
+/*
+ * Forward, packed [T,H,D] with device int32 cu_seqlens_q/k [num_seqs+1].
+ * total_q / total_k are the token counts (cu_seqlens_*[num_seqs]);
+ * max_seqlen_q / max_seqlen_k bound every sequence's length.  lse is fp32
+ * [Hq, total_q].
+ */
+attn_status attn_fwd_varlen(const attn_params *params, int32_t num_seqs, int64_t total_q,
+                            int64_t total_k, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, const void *q, const void *k, const void *v,
+                            void *o, float *lse, void *workspace, size_t workspace_bytes,
+                            void *stream);
+size_t attn_fwd_varlen_workspace_size(const attn_params *params, int32_t num_seqs, int64_t total_q,
+                                      int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k);
+
+/*
+ * Backward, packed.  Same arguments as attn_fwd_varlen plus o, lse (fp32
+ * [Hq, total_q]), dout, and the outputs dq, dk, dv, dsinks as in attn_bwd.
+ */
+attn_status attn_bwd_varlen(const attn_params *params, int32_t num_seqs, int64_t total_q,
+                            int64_t total_k, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, const void *q, const void *k, const void *v,
+                            const void *o, const float *lse, const void *dout, void *dq,
+                            void *dk, void *dv, float *dsinks, int32_t grad_dtype,
+                            void *workspace, size_t workspace_bytes, void *stream);
+size_t attn_bwd_varlen_workspace_size(const attn_params *params, int32_t num_seqs,
+                                      int64_t total_q, int64_t total_k, int32_t max_seqlen_q,
+                                      int32_t max_seqlen_k, int32_t grad_dtype);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char *attn_last_error(void);
+
+/* Library version, 100 * major + minor. */
+int32_t attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN36_H */

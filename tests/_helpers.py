@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: move seeded host inputs to the GPU,
+run the library through its binding, and compare with the fp64 oracle.
+
+Tolerances (bf16/fp16 in, fp32 accumulate): per tensor, over the compared
+elements, max-abs error <= 2e-2 and mean-abs error <= 2e-3; the log-sum-exp
+within 1e-3 (and -inf exactly where the oracle has -inf).  A 16-bit output
+cannot be closer to the exact value than its own rounding, so for outputs
+stored in 16 bits the per-element bound is widened by half a unit in the last
+place of the exact value (zero for |x| < 4 in bf16, where half an ulp is
+below 8e-3); fp32 outputs get no widening.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_36_amd import synth
+
+MAX_ABS, MEAN_ABS, LSE_ABS = 2e-2, 2e-3, 1e-3
+
+
+def dev_tensor(bits: np.ndarray, dtype: str = "bf16"):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    return t.cuda()
+
+
+def host(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of a 16-bit format at |ref| (0 below 4 for bf16)."""
+    mant = 7 if dtype == "bf16" else 10
+    a = np.maximum(np.abs(ref), 1e-30)
+    e = np.floor(np.log2(a))
+    if dtype == "fp16":
+        e = np.maximum(e, -14)
+    hu = 0.5 * np.exp2(e - mant)
+    if dtype == "bf16":
+        hu = np.where(np.abs(ref) < 4.0, 0.0, hu)
+    return hu
+
+
+def assert_close(name, got, ref, out_dtype="f32"):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite values" % name
+    err = np.abs(got - ref)
+    bound = MAX_ABS + (half_ulp(ref, out_dtype) if out_dtype in ("bf16", "fp16") else 0.0)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape) if err.size else None
+    assert err.size == 0 or np.all(err <= bound), \
+        "%s: max abs err %.4g at %s (got %.6g ref %.6g)" % (name, err.max(), worst, got[worst], ref[worst])
+    extra = np.mean(half_ulp(ref, out_dtype)) if out_dtype in ("bf16", "fp16") else 0.0
+    assert err.size == 0 or err.mean() <= MEAN_ABS + extra, "%s: mean abs err %.4g" % (name, err.mean())
+    return float(err.max()) if err.size else 0.0
+
+
+def assert_lse(name, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    ninf = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), ninf), "%s: -inf pattern differs" % name
+    fin = ~ninf
+    if fin.any():
+        err = np.abs(got[fin] - ref[fin])
+        assert err.max() <= LSE_ABS, "%s: lse max err %.4g" % (name, err.max())
+
+
+def scale_of(d, scale=None):
+    return synth.default_scale(d) if scale is None else float(np.float32(scale))
+
+
+def oracle_batched(inp, causal, window, scale, dtype="bf16"):
+    return oracle.batched(inp["q"], inp["k"], inp["v"], scale, causal=causal, window=window,
+                          dout=inp["dout"], sinks=inp["sinks"], dtype=dtype)

@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/attn.h declares, and rejects bad arguments on the host (status code
+and message) before launching anything.  No call here reaches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_36_amd as ea
+from exact_attention_36_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ea.load_library()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert ea.version() == 100
+
+
+def _params(**kw):
+    p = _lib.attn_params()
+    p.dtype, p.head_dim, p.heads_q, p.heads_kv = _lib.ATTN_BF16, 128, 4, 2
+    p.softmax_scale, p.causal, p.window_left, p.window_right, p.sinks = 0.0, 1, -1, -1, None
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _fwd(p, B=1, sq=16, sk=16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=None, nws=0):
+    return ea.load_library().attn_fwd(ctypes.byref(p) if p is not None else None, B, sq, sk, q, k, v, o,
+                                      lse, ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=7), _lib.ATTN_EINVAL, "dtype"),
+    (dict(head_dim=96), _lib.ATTN_ENOTSUP, "not built"),
+    (dict(head_dim=100), _lib.ATTN_EINVAL, "multiple of 8"),
+    (dict(head_dim=512), _lib.ATTN_EINVAL, "multiple of 8"),
+    (dict(heads_q=6, heads_kv=4), _lib.ATTN_EINVAL, "divide"),
+    (dict(heads_kv=0), _lib.ATTN_EINVAL, ">= 1"),
+    (dict(window_left=-2), _lib.ATTN_EINVAL, "window"),
+    (dict(window_right=-5), _lib.ATTN_EINVAL, "window"),
+    (dict(causal=2), _lib.ATTN_EINVAL, "causal"),
+])
+def test_fwd_rejects_bad_params(kw, status, needle):
+    assert _fwd(_params(**kw)) == status
+    assert needle in ea.last_error()
+
+
+def test_fwd_rejects_bad_shapes_and_pointers():
+    assert _fwd(None) == _lib.ATTN_EINVAL
+    assert "NULL" in ea.last_error()
+    assert _fwd(_params(), B=0) == _lib.ATTN_EINVAL
+    assert _fwd(_params(), sq=0) == _lib.ATTN_EINVAL
+    assert _fwd(_params(), sk=-3) == _lib.ATTN_EINVAL
+    assert _fwd(_params(), q=None) == _lib.ATTN_EINVAL
+    assert _fwd(_params(), lse=None) == _lib.ATTN_EINVAL
+    assert _fwd(_params(), sq=1 << 24) == _lib.ATTN_ENOTSUP
+    assert "offset" in ea.last_error()
+
+
+def test_fwd_split_workspace_is_checked():
+    p = _params(heads_q=64, heads_kv=8)
+    lib = ea.load_library()
+    need = lib.attn_fwd_workspace_size(ctypes.byref(p), 2, 16, 32768)
+    assert need > 0  # decode shape: keys are split among workgroups
+    assert _fwd(p, B=2, sq=16, sk=32768, ws=None, nws=0) == _lib.ATTN_EINVAL
+    assert "workspace" in ea.last_error()
+    assert _fwd(p, B=2, sq=16, sk=32768, ws=FAKE, nws=need - 1) == _lib.ATTN_EINVAL
+    # a long prefill does not split
+    assert lib.attn_fwd_workspace_size(ctypes.byref(p), 4, 2048, 2048) == 0
+
+
+def test_bwd_rejects_bad_arguments():
+    lib = ea.load_library()
+    p = _params()
+    args = lambda **o: [o.get(n, FAKE) for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv")]
+    call = lambda p, gd=_lib.ATTN_BF16, ds=None, ws=None, nws=0, **o: lib.attn_bwd(
+        ctypes.byref(p), 1, 16, 16, *args(**o), ds, gd, ws, nws, None)
+    assert call(p, gd=_lib.ATTN_FP16) == _lib.ATTN_EINVAL
+    assert "grad_dtype" in ea.last_error()
+    assert call(p, dout=None) == _lib.ATTN_EINVAL
+    ps = _params(sinks=0x2000)
+    assert call(ps, ds=None) == _lib.ATTN_EINVAL
+    assert "dsinks" in ea.last_error()
+    need = lib.attn_bwd_workspace_size(ctypes.byref(p), 1, 16, 16, _lib.ATTN_BF16)
+    assert need >= 16 * 4 * 128 * 4  # the fp32 dQ accumulator
+    assert call(p, ws=FAKE, nws=need - 1) == _lib.ATTN_EINVAL
+    assert "workspace" in ea.last_error()
+    # fp32 gradients accumulate dQ in place: smaller workspace
+    assert lib.attn_bwd_workspace_size(ctypes.byref(p), 1, 16, 16, _lib.ATTN_FP32) < need
+
+
+def test_varlen_rejects_bad_arguments():
+    lib = ea.load_library()
+    p = _params()
+    call = lambda n=2, tq=10, tk=10, cq=FAKE, ck=FAKE, mq=8, mk=8: lib.attn_fwd_varlen(
+        ctypes.byref(p), n, tq, tk, cq, ck, mq, mk, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert call(n=0) == _lib.ATTN_EINVAL
+    assert call(cq=None) == _lib.ATTN_EINVAL
+    assert call(tq=-1) == _lib.ATTN_EINVAL
+    assert call(mq=-1) == _lib.ATTN_EINVAL
+    assert call(mk=1 << 26) == _lib.ATTN_ENOTSUP
+    assert lib.attn_bwd_varlen(ctypes.byref(_params(dtype=5)), 2, 10, 10, FAKE, FAKE, 8, 8, *([FAKE] * 9),
+                               None, 0, None, 0, None) == _lib.ATTN_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load_library()

@@ -1,0 +1,133 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+seeded inputs, element by element, on shapes that span several tiles and end
+in ragged tails, with the edge cases of the method: grouped-query heads,
+causal and two-sided windows aligned bottom-right with s_q < s_k and
+s_q > s_k (empty rows), attention sinks, fp16, split-KV decode, and packed
+batches with zero-length sequences."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_36_amd import synth
+import exact_attention_36_amd as ea
+from _helpers import (assert_close, assert_lse, dev_tensor, host, oracle_batched, scale_of)
+
+pytestmark = pytest.mark.gpu
+
+BATCHED = [
+    # id, B, sq, sk, hq, hkv, d, causal, window, sinks, dtype, bwd
+    ("cfg1_fwd", 1, 128, 128, 2, 2, 64, False, (-1, -1), False, "bf16", False),
+    ("causal_ragged", 2, 200, 200, 4, 2, 128, True, (-1, -1), False, "bf16", True),
+    ("window_sinks_gqa4", 1, 300, 300, 8, 2, 128, True, (37, 0), True, "bf16", True),
+    ("sq_lt_sk", 2, 150, 333, 4, 4, 64, True, (-1, -1), True, "bf16", True),
+    ("sq_gt_sk_empty_rows", 1, 333, 150, 4, 1, 128, True, (-1, -1), False, "bf16", True),
+    ("two_sided_fp16", 1, 257, 190, 2, 2, 64, False, (20, 13), False, "fp16", True),
+    ("sinks_fp16_full", 1, 100, 100, 2, 1, 128, False, (-1, -1), True, "fp16", True),
+    ("split_kv_decode", 2, 3, 5000, 8, 2, 128, True, (-1, -1), True, "bf16", True),
+]
+
+
+def _torch_dtype(dt):
+    return torch.bfloat16 if dt == "bf16" else torch.float16
+
+
+@pytest.mark.parametrize("case", BATCHED, ids=[c[0] for c in BATCHED])
+def test_batched_matches_oracle(case):
+    name, B, sq, sk, hq, hkv, d, causal, window, sinks, dt, bwd = case
+    print("case", name, flush=True)
+    seed = zlib.crc32(name.encode()) % 1000
+    inp = synth.batched_inputs(seed, B, sq, sk, hq, hkv, d, grads=True, sinks=sinks, dtype=dt)
+    scale = scale_of(d)
+    ref = oracle.full(oracle_batched(inp, causal, window, scale, dt), grads=bwd)
+    q, k, v = (dev_tensor(inp[n], dt) for n in ("q", "k", "v"))
+    s_dev = torch.from_numpy(inp["sinks"]).cuda() if sinks else None
+    o, lse = ea.attn_fwd(q, k, v, causal=causal, window=window, sinks=s_dev)
+    o2, lse2 = ea.attn_fwd(q, k, v, causal=causal, window=window, sinks=s_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "forward is not bitwise repeatable"
+    assert_close(name + ".o", host(o).reshape(B * sq, hq, d), ref["o"], dt)
+    assert_lse(name + ".lse", host(lse).transpose(1, 0, 2).reshape(hq, B * sq), ref["lse"])
+    if not bwd:
+        return
+    do = dev_tensor(inp["dout"], dt)
+    for gd in (torch.float32, _torch_dtype(dt)):
+        dq, dk, dv, ds = ea.attn_bwd(q, k, v, o, lse, do, causal=causal, window=window, sinks=s_dev,
+                                     grad_dtype=gd)
+        torch.cuda.synchronize()
+        od = "f32" if gd == torch.float32 else dt
+        assert_close(name + ".dq", host(dq).reshape(B * sq, hq, d), ref["dq"], od)
+        assert_close(name + ".dk", host(dk).reshape(B * sk, hkv, d), ref["dk"], od)
+        assert_close(name + ".dv", host(dv).reshape(B * sk, hkv, d), ref["dv"], od)
+        if sinks:
+            r = oracle.rows(oracle_batched(inp, causal, window, scale, dt),
+                            *_all_rows(B, sq, hq), grads=True)
+            mag = np.zeros(hq)
+            np.add.at(mag, _all_rows(B, sq, hq)[1], np.abs((1 - r["gate"]) * r["delta"]))
+            err = np.abs(host(ds) - ref["dsinks"])
+            assert np.all(err <= 2e-2 + 1e-3 * mag), (err, mag)
+
+
+def _all_rows(B, sq, hq):
+    s, h, i = np.meshgrid(np.arange(B), np.arange(hq), np.arange(sq), indexing="ij")
+    return s.ravel(), h.ravel(), i.ravel()
+
+
+VARLEN = [
+    # id, lens_q, lens_k, hq, hkv, d, causal, window, sinks, dtype
+    ("varlen_gqa_sinks", [0, 17, 283, 128, 1, 0, 77], None, 4, 2, 128, True, (-1, -1), True, "bf16"),
+    ("varlen_mixed_pack", [5, 0, 130, 64, 9], [200, 3, 130, 0, 9], 2, 2, 64, True, (50, 0), False, "bf16"),
+    ("varlen_noncausal_fp16", [33, 190, 1], [64, 190, 300], 6, 2, 128, False, (-1, -1), False, "fp16"),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_varlen_matches_oracle(case):
+    name, lq, lk, hq, hkv, d, causal, window, sinks, dt = case
+    print("case", name, flush=True)
+    lk = lq if lk is None else lk
+    inp = synth.varlen_inputs(zlib.crc32(name.encode()) % 1000, lq, lk, hq, hkv, d, grads=True, sinks=sinks,
+                              dtype=dt)
+    scale = scale_of(d)
+    p = oracle.varlen(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], scale, causal=causal,
+                      window=window, dout=inp["dout"], sinks=inp["sinks"], dtype=dt)
+    ref = oracle.full(p)
+    q, k, v, do = (dev_tensor(inp[n], dt) for n in ("q", "k", "v", "dout"))
+    cq = torch.from_numpy(inp["cu_q"]).cuda()
+    ck = torch.from_numpy(inp["cu_k"]).cuda()
+    s_dev = torch.from_numpy(inp["sinks"]).cuda() if sinks else None
+    o, lse = ea.attn_fwd_varlen(q, k, v, cq, ck, max(lq), max(lk), causal=causal, window=window,
+                                sinks=s_dev)
+    torch.cuda.synchronize()
+    assert_close(name + ".o", host(o), ref["o"], dt)
+    assert_lse(name + ".lse", host(lse), ref["lse"])
+    for gd in (torch.float32, _torch_dtype(dt)):
+        dq, dk, dv, ds = ea.attn_bwd_varlen(q, k, v, o, lse, do, cq, ck, max(lq), max(lk),
+                                            causal=causal, window=window, sinks=s_dev, grad_dtype=gd)
+        torch.cuda.synchronize()
+        od = "f32" if gd == torch.float32 else dt
+        assert_close(name + ".dq", host(dq), ref["dq"], od)
+        assert_close(name + ".dk", host(dk), ref["dk"], od)
+        assert_close(name + ".dv", host(dv), ref["dv"], od)
+        if sinks:
+            assert np.abs(host(ds) - ref["dsinks"]).max() <= 2e-2 + 1e-3 * np.abs(ref["dsinks"]).max()
+
+
+def test_varlen_equals_batched_calls():
+    """Each sequence of a packed call equals the batched call on that sequence alone (bitwise)."""
+    lens = [0, 96, 200, 1, 64]
+    inp = synth.varlen_inputs(3, lens, lens, 4, 1, 128, grads=True)
+    q, k, v, do = (dev_tensor(inp[n]) for n in ("q", "k", "v", "dout"))
+    cq = torch.from_numpy(inp["cu_q"]).cuda()
+    o, lse = ea.attn_fwd_varlen(q, k, v, cq, cq, max(lens), max(lens), causal=True)
+    for s, L in enumerate(lens):
+        if L == 0:
+            continue
+        a, b = int(inp["cu_q"][s]), int(inp["cu_q"][s + 1])
+        ob, lb = ea.attn_fwd(q[a:b][None].contiguous(), k[a:b][None].contiguous(), v[a:b][None].contiguous(),
+                             causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], ob[0]), s
+        assert torch.equal(lse[:, a:b], lb[0]), s
