@@ -1,0 +1,191 @@
+"""Benchmark: one step = the fused attention forward plus backward on the
+causal prefill workload B=4, Hq=Hkv=16, S=2048, D=128, bf16 (seeded synthetic
+N(0,1) inputs resident in HBM), through the C ABI.
+
+Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s
+(14 * D * visible (query, key) pairs per step: 4*D forward, 10*D backward).
+`roofline` reports the kernel with the most time in the timed region, timed
+with HIP events on its own stream; `cpu_baseline` times the fp64 CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+
+WORKLOAD = dict(name="causal prefill fwd+bwd B4 H16 S2048 D128 bf16", B=4, S=2048, HQ=16, HKV=16,
+                D=128, causal=True, window=(-1, -1))
+
+
+def visible_pairs(B, sq, sk, hq, causal, window):
+    """Number of (query, key) pairs the mask keeps, summed over batch and q heads."""
+    import numpy as np
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    diag = i + sk - sq
+    keep = np.ones((sq, sk), bool)
+    if causal:
+        keep &= j <= diag
+    if window[0] >= 0:
+        keep &= j >= diag - window[0]
+    if window[1] >= 0:
+        keep &= j <= diag + window[1]
+    return int(keep.sum()) * B * hq
+
+
+def traffic_from_profile(kernel: str, source_files):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+
+    The summary records a hash of the kernel sources it was measured with; if
+    they changed since, the counters no longer describe this kernel.
+    """
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % kernel)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for p in source_files:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, seconds_target=15.0):
+    """Time the fp64 oracle on whole (batch, head) slices of the workload."""
+    import numpy as np
+    import oracle
+    from exact_attention_36_amd import synth
+    D, S = w["D"], w["S"]
+    scale = synth.default_scale(D)
+    done_pairs, t_used, slices = 0, 0.0, 0
+    for b in range(w["B"]):
+        for h in range(w["HQ"]):
+            sl = lambda a, hh=h: np.ascontiguousarray(a[b:b + 1, :, hh:hh + 1, :])
+            p = oracle.batched(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), scale, causal=w["causal"],
+                               window=w["window"], dout=sl(inp["dout"]))
+            t0 = time.perf_counter()
+            oracle.full(p, grads=True)
+            t_used += time.perf_counter() - t0
+            done_pairs += visible_pairs(1, S, S, 1, w["causal"], w["window"])
+            slices += 1
+            if t_used >= seconds_target:
+                break
+        if t_used >= seconds_target:
+            break
+    flops = 14.0 * D * done_pairs
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d full (batch, head) slices of %dx%d causal, fwd+bwd (O, LSE, dQ, dK, dV), "
+                      "%.1f s" % (slices, S, S, t_used)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the attention kernels run on a single device and this "
+              "build has no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+
+    w = WORKLOAD
+    B, S, HQ, HKV, D = w["B"], w["S"], w["HQ"], w["HKV"], w["D"]
+    inp = synth.batched_inputs(2, B, S, S, HQ, HKV, D, grads=True)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
+    torch.cuda.synchronize()
+
+    def step():
+        o, lse = ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"])
+        ea.attn_bwd(q, k, v, o, lse, do, causal=w["causal"], window=w["window"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ea.attn_timing_enable(True)
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / args.steps
+    kern = {}
+    for name in ea._lib.KERNELS:
+        n, tot = ea.attn_timing_read(name)
+        if n:
+            kern[name] = (n, tot)
+    ea.attn_timing_enable(False)
+
+    pairs = visible_pairs(B, S, S, HQ, w["causal"], w["window"])
+    fwd_flop, bwd_flop = 4.0 * D * pairs, 10.0 * D * pairs
+    tflops = (fwd_flop + bwd_flop) / (ms * 1e-3) / 1e12
+
+    # dominant kernel: most total time; algorithmic flops of its pass per launch
+    dom = max(kern, key=lambda n: kern[n][1])
+    n_l, tot = kern[dom]
+    avg_ms = tot / n_l
+    flop_of = {"fwd": fwd_flop, "bwd_dkdv": bwd_flop}
+    roof = None
+    if dom in flop_of:
+        ach = flop_of[dom] / (avg_ms * 1e-3) / 1e12
+        srcs = {"fwd": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
+                "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"]}[dom]
+        srcs = srcs + ["exact_attention_36_amd/csrc/attn_device.h", "exact_attention_36_amd/csrc/attn_common.h",
+                       "exact_attention_36_amd/csrc/attn_kernels.h"]
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profile(dom, srcs), "avg_launch_ms": round(avg_ms, 5)}
+
+    out = {
+        "metric": "attention fwd+bwd TFLOPS (and % of MFMA bf16 peak), 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dout rounded to bf16",
+        "config": {"workload": w["name"], "batch": B, "seq_len": S, "heads_q": HQ, "heads_kv": HKV,
+                   "head_dim": D, "causal": w["causal"], "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "kernels_ms_per_step": {n: round(t / args.steps, 5) for n, (c, t) in kern.items()},
+        "fwd_tflops": round(fwd_flop / (kern["fwd"][1] / kern["fwd"][0] * 1e-3) / 1e12, 2) if "fwd" in kern else None,
+        "roofline": roof,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

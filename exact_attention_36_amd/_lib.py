@@ -22,8 +22,10 @@ ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 EXPORTED = (
     "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
     "attn_fwd_varlen", "attn_fwd_varlen_workspace_size", "attn_bwd_varlen",
-    "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version",
+    "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable",
+    "attn_timing_read",
 )
+KERNELS = ("fwd", "fwd_combine", "bwd_zero", "bwd_pre", "bwd_dkdv", "bwd_dq")
 
 
 class AttnError(RuntimeError):
@@ -66,6 +68,8 @@ def load_library():
     lib.attn_bwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, vp, i32, vp, sz, vp]
     lib.attn_bwd_varlen_workspace_size.argtypes = [P, i32, i64, i64, i32, i32, i32]
+    lib.attn_timing_enable.argtypes = [i32]
+    lib.attn_timing_read.argtypes = [i32, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
     for name in EXPORTED:
         if name.endswith("workspace_size"):
             getattr(lib, name).restype = ctypes.c_size_t
@@ -83,6 +87,18 @@ def last_error() -> str:
 
 def version() -> int:
     return int(load_library().attn_version())
+
+
+def attn_timing_enable(on: bool = True) -> None:
+    """Start (or stop) bracketing every library kernel launch with HIP events."""
+    _check(load_library().attn_timing_enable(1 if on else 0))
+
+
+def attn_timing_read(kernel: str):
+    """(launches, total milliseconds) of one kernel since attn_timing_enable."""
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(load_library().attn_timing_read(KERNELS.index(kernel), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 def _dtype_code(t: torch.dtype) -> int:

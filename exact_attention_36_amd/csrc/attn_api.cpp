@@ -78,6 +78,7 @@ SeqArgs seq_args(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
   s.hq = p->heads_q;
   s.hkv = p->heads_kv;
   s.group = p->heads_q / p->heads_kv;
+  s.group_magic = s.group >= 2 ? (uint32_t)((((uint64_t)1 << 32) + s.group - 1) / s.group) : 0u;
   s.causal = p->causal;
   s.wl = p->window_left;
   s.wr = p->window_right;

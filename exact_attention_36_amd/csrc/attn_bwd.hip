@@ -103,10 +103,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int QTILE = BM * ROWB;          // one Q (or dO) tile
   constexpr int QSLABS = QTILE / 1024;      // 1 KB slabs per Q tile
   constexpr int DST_ROWB = BM * 2;          // dS^T row: BM queries
-  __shared__ __attribute__((aligned(1024))) char smem[KTILE + 2 * 2 * QTILE + BN * DST_ROWB + 2 * 256];
-  char* const k_lds = smem;
-  char* const q_lds = smem + KTILE;                      // [buf][Q, dO]
-  char* const ds_lds = q_lds + 4 * QTILE;                // dS^T [BN keys][BM queries]
+  __shared__ __attribute__((aligned(1024))) char smem[KTILE + 5 * QTILE + BN * DST_ROWB + 2 * 256];
+  char* const k_lds = smem;                              // K block (fp16 for the dQ product)
+  char* const q_lds = smem + KTILE;                      // [buf][Q, dO], input dtype
+  char* const qh_lds = q_lds + 4 * QTILE;                // Q tile as fp16 (bf16 inputs)
+  char* const ds_lds = qh_lds + QTILE;                   // dS^T [BN keys][BM queries], fp16
   float* const st_lds = (float*)(ds_lds + BN * DST_ROWB);  // [buf][lse2 32 | delta 32]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -155,6 +156,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int64_t st_hs = a.s.cu_q ? a.s.total_q : a.s.sq;
   const int64_t st_total = a.s.cu_q ? (int64_t)a.s.hq * a.s.total_q : (int64_t)a.s.nseq * a.s.hq * a.s.sq;
   const auto rl = make_rsrc(a.lse2, (uint32_t)(st_total * 4));
+  // dQ accumulator rows of this (sequence, kv group), fp32
+  const auto rdq = make_rsrc(a.dq_acc + qbase_e, si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 4) : 0u);
   const auto rd = make_rsrc(a.delta, (uint32_t)(st_total * 4));
 
   // K block -> LDS (swizzled), for the transposing reads of dQ = dS K
@@ -192,14 +195,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
       const int c = pos ^ swz<D>(r);
       const int p = pb * BM + r;
-      const int i = p / G, hl = p - i * G;
+      const int i = div_group(p, a.s), hl = p - i * G;
       const uint32_t off = (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + c * 8) * 2);
       buf_load_lds16(rq, qd + slab * 1024, off);
       buf_load_lds16(rdo, dd + slab * 1024, off);
     }
     if (wave == 0) {
       const int p = pb * BM + l32;
-      const int i = p / G, hl = p - i * G;
+      const int i = div_group(p, a.s), hl = p - i * G;
       const int64_t idx = st_base + (int64_t)(g * G + hl) * st_hs + i;
       // rows past the sequence read index 0 (valid memory); they are masked
       const uint32_t off = p < prows ? (uint32_t)(idx * 4) : 0u;
@@ -226,12 +229,31 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   if (pb_begin < pb_end) load_q(pb_begin, 0);
   for (int pb = pb_begin; pb < pb_end; pb++) {
     const int buf = (pb - pb_begin) & 1;
-    wait_vmcnt<0>();
+    // tile pb was issued before the previous step's 16 dQ atomics
+    if (pb == pb_begin) wait_vmcnt<0>();
+    else wait_vmcnt<16>();
     __builtin_amdgcn_s_barrier();
     if (pb + 1 < pb_end) load_q(pb + 1, buf ^ 1);
     const char* qt = q_lds + buf * 2 * QTILE;
     const char* dot = qt + QTILE;
     const float* stt = st_lds + buf * 64;
+    // dS is kept in fp16 (10 fraction bits instead of bf16's 7), so the dK and
+    // dQ products take fp16 copies of the Q tile and of the K block.
+    if constexpr (!F16) {
+      if (pb == pb_begin) {
+#pragma unroll
+        for (int n = 0; n < KTILE / 16 / THREADS; n++) {
+          char* p16 = k_lds + (threadIdx.x + n * THREADS) * 16;
+          *LDS_PTR(u32x4, p16) = bf16x8_to_f16x8(lds_read16(p16));
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < QTILE / 16 / THREADS; n++) {
+        const int off = (threadIdx.x + n * THREADS) * 16;
+        *LDS_PTR(u32x4, qh_lds + off) = bf16x8_to_f16x8(lds_read16(qt + off));
+      }
+    }
+    const char* qh = F16 ? qt : qh_lds;
 
     // S and dP, [32 queries x 32 keys]: lane = key column, registers = query rows
     f32x16 s_acc = f32x16{}, dp = f32x16{};
@@ -248,7 +270,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       dl[a4] = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
     }
     const int p0 = pb * BM;
-    const int qi_lo = p0 / G, qi_hi = (min(p0 + BM, prows) - 1) / G;
+    const int qi_lo = div_group(p0, a.s), qi_hi = div_group(min(p0 + BM, prows) - 1, a.s);
     const bool interior = (p0 + BM <= prows) && j0 + wave * 32 >= band.kmin(qi_hi) &&
                           j0 + wave * 32 + 31 <= band.kmax(qi_lo);
     f32x16 pm, dsm;
@@ -259,21 +281,21 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       float p = exp2_fast(fmaf(s_acc[i], c, -lse2));
       if (!interior) {
         const int pr = p0 + r;
-        const int qi = pr / G;
+        const int qi = div_group(pr, a.s);
         const bool vis = pr < prows && my_kj < si.lk && my_kj >= band.kmin(qi) && my_kj <= band.kmax(qi);
         if (!vis) p = 0.f;
       }
       pm[i] = p;
       dsm[i] = p * (dp[i] - dl[i >> 2][i & 3]);
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS   (M = dims, N = this wave's keys, K = queries)
+    // dV^T += dO^T P  (M = dims, N = this wave's keys, K = queries)
     u32x4 pf[2], sf[2];
 #pragma unroll
     for (int u = 0; u < 2; u++) {
       pf[u] = u32x4{pack2<F16>(pm[8 * u + 0], pm[8 * u + 1]), pack2<F16>(pm[8 * u + 2], pm[8 * u + 3]),
                     pack2<F16>(pm[8 * u + 4], pm[8 * u + 5]), pack2<F16>(pm[8 * u + 6], pm[8 * u + 7])};
-      sf[u] = u32x4{pack2<F16>(dsm[8 * u + 0], dsm[8 * u + 1]), pack2<F16>(dsm[8 * u + 2], dsm[8 * u + 3]),
-                    pack2<F16>(dsm[8 * u + 4], dsm[8 * u + 5]), pack2<F16>(dsm[8 * u + 6], dsm[8 * u + 7])};
+      sf[u] = u32x4{pack2<true>(dsm[8 * u + 0], dsm[8 * u + 1]), pack2<true>(dsm[8 * u + 2], dsm[8 * u + 3]),
+                    pack2<true>(dsm[8 * u + 4], dsm[8 * u + 5]), pack2<true>(dsm[8 * u + 6], dsm[8 * u + 7])};
     }
 #pragma unroll
     for (int d = 0; d < DB; d++) {
@@ -285,8 +307,6 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         const int off2 = tile_off<D>(rb + 8, col >> 3) + (jsrc & 1) * 8;
         const u32x2 o1 = lds_read_tr(dot + off1), o2 = lds_read_tr(dot + off2);
         dv[d] = mfma32<F16>(u32x4{o1[0], o1[1], o2[0], o2[1]}, pf[u], dv[d]);
-        const u32x2 q1 = lds_read_tr(qt + off1), q2 = lds_read_tr(qt + off2);
-        dk[d] = mfma32<F16>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
       }
     }
     // dS^T -> LDS: row = key, 4 consecutive queries per 8-byte write
@@ -298,8 +318,20 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         *(u32x2*)(drow + q4 * 2) = u32x2{sf[a4 >> 1][2 * (a4 & 1)], sf[a4 >> 1][2 * (a4 & 1) + 1]};
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's dS writes done
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_s_barrier();
+    // dK^T += Q^T dS  (fp16)
+#pragma unroll
+    for (int d = 0; d < DB; d++) {
+      const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int rb = u * 16 + 4 * hh + esrc;
+        const u32x2 q1 = lds_read_tr(qh + tile_off<D>(rb, col >> 3) + (jsrc & 1) * 8);
+        const u32x2 q2 = lds_read_tr(qh + tile_off<D>(rb + 8, col >> 3) + (jsrc & 1) * 8);
+        dk[d] = mfma32<true>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
+      }
+    }
     // dQ[32 q x 32 dims] += dS K over this wave's key range:
     // A = dS (lane: query, 8 keys) via transposing reads of dS^T;
     // B = K  (lane: dim, 8 keys) via transposing reads of the K block.
@@ -314,18 +346,19 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         const int dcol = dq_dblk * 32 + 16 * (gq & 1) + 4 * jsrc;
         const u32x2 k1 = lds_read_tr(k_lds + tile_off<D>(kb, dcol >> 3) + (jsrc & 1) * 8);
         const u32x2 k2 = lds_read_tr(k_lds + tile_off<D>(kb + 4, dcol >> 3) + (jsrc & 1) * 8);
-        dqa = mfma32<F16>(u32x4{s1[0], s1[1], s2[0], s2[1]}, u32x4{k1[0], k1[1], k2[0], k2[1]}, dqa);
+        dqa = mfma32<true>(u32x4{s1[0], s1[1], s2[0], s2[1]}, u32x4{k1[0], k1[1], k2[0], k2[1]}, dqa);
       }
-      // C: lane = dim column, registers = query rows
+      // C: lane = dim column, registers = query rows.  Exactly 16 atomics per
+      // lane per step (rows past the sequence fall outside the buffer and are
+      // dropped by the hardware), so the next step can wait for its tile
+      // loads with vmcnt(16) without waiting for these atomics.
       const int dcol = dq_dblk * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (pr < prows) {
-          const int qi = pr / G, hl = pr - qi * G;
-          float* dst = a.dq_acc + ((int64_t)(si.q0 + qi) * a.s.hq + g * G + hl) * D + dcol;
-          __builtin_amdgcn_global_atomic_fadd_f32(dst, dqa[i] * a.scale);
-        }
+        const int qi = div_group(pr, a.s), hl = pr - qi * G;
+        const uint32_t off = (uint32_t)((((int64_t)qi * a.s.hq + hl) * D + dcol) * 4);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dqa[i] * a.scale, rdq, off, 0, 0);
       }
     }
   }
@@ -364,18 +397,30 @@ __global__ __launch_bounds__(THREADS) void bwd_dq_kernel(const float* __restrict
 
 template <int D, bool F16>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  if (a.sinks && a.dsinks) hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.s.hq + 255) / 256), dim3(256), 0, st, a.dsinks, a.s.hq);
+  if (a.sinks && a.dsinks) {
+    timing_begin(K_BWD_ZERO, st);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.s.hq + 255) / 256), dim3(256), 0, st, a.dsinks, a.s.hq);
+    timing_end(K_BWD_ZERO, st);
+  }
   const int64_t tq = a.s.cu_q ? a.s.total_q : (int64_t)a.s.nseq * a.s.sq;
   const int64_t rows = tq * a.s.hq;
   constexpr int RPB = THREADS / (D / 8);
-  if (rows > 0)
+  if (rows > 0) {
+    timing_begin(K_BWD_PRE, st);
     hipLaunchKernelGGL((bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(THREADS), 0, st, a);
-  if (a.total_ctas > 0)
+    timing_end(K_BWD_PRE, st);
+  }
+  if (a.total_ctas > 0) {
+    timing_begin(K_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    timing_end(K_BWD_DKDV, st);
+  }
   if (!a.grad_f32 && rows > 0) {
     const int64_t n4 = rows * D / 4;
+    timing_begin(K_BWD_DQ, st);
     hipLaunchKernelGGL((bwd_dq_kernel<F16>), dim3((unsigned)((n4 + THREADS - 1) / THREADS)), dim3(THREADS), 0, st,
                        (const float*)a.dq_acc, (uint16_t*)a.dq, n4);
+    timing_end(K_BWD_DQ, st);
   }
   return hipGetLastError();
 }

@@ -9,6 +9,13 @@ namespace attn {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// n / group for 0 <= n < 2^23 (packed rows of one sequence; the host bounds
+// sequence extents so that this holds): with M = ceil(2^32 / G) the error of
+// n*M/2^32 is below n/2^32 < 1/512 < 1/G, so the high word is the quotient.
+__device__ __forceinline__ int div_group(int n, const SeqArgs& s) {
+  return s.group == 1 ? n : (int)__umulhi((uint32_t)n, s.group_magic);
+}
+
 struct SeqInfo {
   int q0, lq, k0, lk;  // first token and length of the sequence in q and in k/v
 };

@@ -46,6 +46,18 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// 8 bf16 values -> the same 8 values as fp16 (exact inside fp16's normal
+// range; rounded to nearest even below it, +-inf above 65504).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 x) {
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const float lo = __builtin_bit_cast(float, x[e] << 16), hi = __builtin_bit_cast(float, x[e] & 0xFFFF0000u);
+    r[e] = pack2<true>(lo, hi);
+  }
+  return r;
+}
+
 template <bool F16>
 __device__ __forceinline__ float to_f32(uint16_t h) {
   if constexpr (F16) return (float)__builtin_bit_cast(_Float16, h);

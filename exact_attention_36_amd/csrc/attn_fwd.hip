@@ -69,7 +69,7 @@ void fwd_kernel(const FwdArgs a) {
   if (p0 >= prows) return;  // idle slot of the packed grid (whole workgroup)
 
   const Band band(a.s, si);
-  const int i_lo = p0 / G, i_hi = (min(p0 + FWD_BM, prows) - 1) / G;
+  const int i_lo = div_group(p0, a.s), i_hi = div_group(min(p0 + FWD_BM, prows) - 1, a.s);
   const int kv_lo = band.kmin(i_lo), kv_hi = band.kmax(i_hi);
   int t_begin = 0, t_end = 0;
   if (kv_hi >= kv_lo) {
@@ -87,7 +87,7 @@ void fwd_kernel(const FwdArgs a) {
 
   // ---- this lane's query row
   const int my_p = p0 + wave * 32 + l32;
-  const int my_i = my_p / G;
+  const int my_i = div_group(my_p, a.s);
   const int my_hl = my_p - my_i * G;
   const int my_h = g * G + my_hl;
   const int my_kmin = band.kmin(my_i), my_kmax = band.kmax(my_i);
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
   const int G = a.s.group;
   const SeqInfo si = seq_info(a.s, seq);
   if (p >= si.lq * G) return;
-  const int i = p / G, hl = p - i * G, h = g * G + hl;
+  const int i = div_group(p, a.s), hl = p - i * G, h = g * G + hl;
   const int64_t split_stride = (int64_t)a.s.nseq * a.s.hkv * rows_bg;
 
   float mx = -INFINITY;
@@ -298,7 +298,9 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
 
 template <int D, bool F16>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  timing_begin(K_FWD, st);
   hipLaunchKernelGGL((fwd_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  timing_end(K_FWD, st);
   return hipGetLastError();
 }
 
@@ -310,7 +312,9 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f16, hipStream_t st) 
 template <int D, bool F16>
 static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.s.nseq * a.s.hkv * a.nmb * FWD_BM;
+  timing_begin(K_FWD_COMBINE, st);
   hipLaunchKernelGGL((fwd_combine_kernel<D, F16>), dim3((unsigned)((rows + 3) / 4)), dim3(THREADS), 0, st, a);
+  timing_end(K_FWD_COMBINE, st);
   return hipGetLastError();
 }
 

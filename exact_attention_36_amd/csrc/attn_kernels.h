@@ -24,6 +24,7 @@ struct SeqArgs {
   int32_t sq, sk;        // per-sequence lengths in batched mode
   int32_t total_q;       // tokens of q (lse row stride in packed mode)
   int32_t hq, hkv, group;
+  uint32_t group_magic;  // ceil(2^32 / group) for group >= 2 (fast division, see div_group)
   int32_t causal, wl, wr;  // window bounds, -1 = unbounded
 };
 
@@ -58,6 +59,12 @@ struct BwdArgs {
   int32_t nblk;           // linear kv blocks per kv head in packed mode
   int32_t total_ctas;
 };
+
+// Optional per-launch timing (attn_timing_enable): the launchers call these
+// around every kernel launch; they record HIP events only while enabled.
+enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_ZERO, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_COUNT };
+void timing_begin(int kid, hipStream_t st);
+void timing_end(int kid, hipStream_t st);
 
 // Launchers (defined in the .hip files).  Return hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f16, hipStream_t st);

@@ -125,3 +125,30 @@ def packed_workload(seed: int = 4, n: int = 64, total: int = 65536, hq: int = 16
     v = normal_bits(rng, (T, hkv, d), dtype)
     dout = normal_bits(rng, (T, hq, d), dtype) if grads else None
     return dict(q=q, k=k, v=v, dout=dout, sinks=None, cu_q=cu, cu_k=cu, lengths=L)
+
+
+def device_normal(seed: int, shapes, device="cuda", dtype: str = "bf16"):
+    """Large inputs drawn on the GPU: i.i.d. N(0,1) float32 from torch's seeded
+    device generator (Philox), rounded to bf16/fp16 (RNE), in the order of
+    `shapes`.  Returns device tensors; `host_bits` gives their uint16 encodings.
+    Used where drawing on the host would take minutes (multi-GB K/V caches).
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    td = torch.bfloat16 if dtype == "bf16" else torch.float16
+    out = []
+    for shp in shapes:
+        t = torch.empty(shp, dtype=td, device=device)
+        flat = t.view(-1)
+        for s in range(0, flat.numel(), _CHUNK):
+            e = min(flat.numel(), s + _CHUNK)
+            flat[s:e] = torch.randn(e - s, generator=g, device=device, dtype=torch.float32).to(td)
+        out.append(t)
+    return out
+
+
+def host_bits(t) -> np.ndarray:
+    """uint16 encodings of a 16-bit tensor, copied to the host."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -149,6 +149,28 @@ size_t attn_bwd_varlen_workspace_size(const attn_params *params, int32_t num_seq
                                       int64_t total_q, int64_t total_k, int32_t max_seqlen_q,
                                       int32_t max_seqlen_k, int32_t grad_dtype);
 
+/*
+ * Kernel timing, for profiling.  While enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the caller's
+ * stream.  attn_timing_read synchronises on the recorded events and returns,
+ * for one kernel, the number of launches and their total duration in
+ * milliseconds since the last attn_timing_enable call; it returns
+ * ATTN_EINVAL for an unknown kernel id.  Not thread safe: enable, run, read
+ * from one thread.  At most 16384 launches are recorded per enable (later
+ * ones are not timed; attn_timing_read then reports ATTN_ENOTSUP).
+ */
+typedef enum {
+    ATTN_KERNEL_FWD = 0,          /* fused forward */
+    ATTN_KERNEL_FWD_COMBINE = 1,  /* split-KV merge */
+    ATTN_KERNEL_BWD_ZERO = 2,     /* clears dsinks */
+    ATTN_KERNEL_BWD_PRE = 3,      /* D_i, lse with the sink, clears the dQ accumulator */
+    ATTN_KERNEL_BWD_DKDV = 4,     /* key-major backward main loop */
+    ATTN_KERNEL_BWD_DQ = 5,       /* dQ accumulator -> gradient dtype */
+    ATTN_KERNEL_COUNT = 6
+} attn_kernel_id;
+attn_status attn_timing_enable(int32_t on);
+attn_status attn_timing_read(int32_t kernel, int64_t *launches, double *total_ms);
+
 /* Message describing the last non-OK status returned on this thread. */
 const char *attn_last_error(void);
 
