@@ -9,6 +9,7 @@
 
 #include "../../include/attn.h"
 #include "attn_kernels.h"
+#include "attn_device.h"
 
 using namespace attn;
 
@@ -163,8 +164,8 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
       a.o_part = (float*)ws;
       a.lse_part = (float*)((char*)ws + align_up(rows * p->head_dim * 4));
     }
-    const int64_t ctas = (int64_t)a.nmb * ns * p->heads_kv * nseq;
-    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    const int64_t ctas = GroupGrid{(int)(ns * p->heads_kv * (int64_t)nseq), a.nmb}.grid_size();
+    if (ctas >= INT32_MAX || (int64_t)ns * p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = (int32_t)ctas;
   }
   if (a.total_ctas == 0) return ATTN_OK;
@@ -213,8 +214,8 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
     a.total_ctas = (int32_t)ctas;
   } else {
     a.nkb = (int32_t)cdiv(sk, BWD_BN);
-    const int64_t ctas = (int64_t)a.nkb * p->heads_kv * nseq;
-    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    const int64_t ctas = GroupGrid{(int)((int64_t)p->heads_kv * nseq), a.nkb}.grid_size();
+    if (ctas >= INT32_MAX || (int64_t)p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = (int32_t)ctas;
   }
   return launched(launch_bwd(a, p->head_dim, p->dtype == ATTN_FP16, (hipStream_t)stream));

@@ -114,19 +114,20 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
   const int G = a.s.group;
-  const int id = xcd_remap(blockIdx.x, a.total_ctas);
-
   int seq, g, nb;
   if (a.s.cu_q) {
+    const int id = xcd_remap(blockIdx.x, a.total_ctas);
     g = id / a.nblk;
     const int t = id - g * a.nblk;
     seq = find_sequence(a.s.cu_k, a.s.nseq, t, 1, BN);
     nb = t - packed_block_start(a.s.cu_k, seq, 1, BN);
   } else {
-    nb = id % a.nkb;
-    const int r = id / a.nkb;
-    g = r % a.s.hkv;
-    seq = r / a.s.hkv;
+    // groups are (sequence, kv head); rank 0 is key block 0, the one most
+    // query rows see under a causal mask
+    int grp;
+    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nkb}.decode(blockIdx.x, grp, nb)) return;
+    g = grp % a.s.hkv;
+    seq = grp / a.s.hkv;
   }
   const SeqInfo si = seq_info(a.s, seq);
   const int j0 = nb * BN;

@@ -34,16 +34,15 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // ---------------------------------------------------------------- conversions
-// Two floats -> two 16-bit values packed in one dword, round to nearest even.
+// Two floats -> two 16-bit values packed in one dword, round to nearest even
+// (one v_cvt_pk_{bf16,f16}_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 template <bool F16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  if constexpr (F16) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  } else {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  }
+  const f32x2 v{lo, hi};
+  if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // 8 bf16 values -> the same 8 values as fp16 (exact inside fp16's normal
@@ -153,5 +152,36 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   // XCDs < rem own per+1 logical ids, the others own per.
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
 }
+
+// Batched grids of ngroups x nranks workgroups, where rank 0 is the heaviest
+// block of a group.  With at least two groups per XCD, XCD x (which receives
+// workgroups x, x+8, x+16, ...) owns groups [x*gpx, (x+1)*gpx) and runs their
+// blocks heaviest rank first across those groups (longest-processing-time
+// order, and the blocks that share a group's K/V share an L2).  With fewer
+// groups the order is simply rank-major over the whole chip.  Returns false
+// for padding slots.  grid_size() gives the matching launch size.
+struct GroupGrid {
+  int ngroups, nranks;
+  __host__ __device__ bool grouped() const { return ngroups >= 16; }
+  __host__ __device__ int gpx() const { return (ngroups + 7) / 8; }
+  __host__ __device__ long long grid_size() const {
+    return grouped() ? 8LL * gpx() * nranks : (long long)ngroups * nranks;
+  }
+  __device__ bool decode(int bid, int& group, int& rank) const {
+    if (!grouped()) {
+      rank = bid / ngroups;
+      group = bid - rank * ngroups;
+      return rank < nranks;
+    }
+    const int per = gpx();
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int g0 = xcd * per;
+    const int cnt = min(per, ngroups - g0);
+    if (cnt <= 0 || slot >= cnt * nranks) return false;
+    rank = slot / cnt;
+    group = g0 + (slot - rank * cnt);
+    return true;
+  }
+};
 
 }  // namespace attn

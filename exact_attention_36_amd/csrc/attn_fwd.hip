@@ -26,6 +26,8 @@
 // and its log-sum-exp; a combine kernel merges them with weights
 // exp(lse_s - lse) (vllm-project/flash-attention README on the GitHub search
 // page, "2.2: Optimize for inference").
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace attn {
@@ -45,23 +47,24 @@ void fwd_kernel(const FwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.s.group;
-  const int id = xcd_remap(blockIdx.x, a.total_ctas);
-
   // ---- which work tile
   int seq, g, mb, sp = 0;
   if (a.s.cu_q) {
+    const int id = xcd_remap(blockIdx.x, a.total_ctas);
     g = id / a.nblk;
     const int t = id - g * a.nblk;
     seq = find_sequence(a.s.cu_q, a.s.nseq, t, G, FWD_BM);
     mb = t - packed_block_start(a.s.cu_q, seq, G, FWD_BM);
   } else {
-    const int mbi = id % a.nmb;
-    int r = id / a.nmb;
-    sp = r % a.n_split;
-    r /= a.n_split;
+    // groups are (sequence, kv head, split); rank 0 is the last m-block, the
+    // longest one under a causal mask
+    int grp, rank;
+    if (!GroupGrid{a.s.nseq * a.s.hkv * a.n_split, a.nmb}.decode(blockIdx.x, grp, rank)) return;
+    sp = grp % a.n_split;
+    const int r = grp / a.n_split;
     g = r % a.s.hkv;
     seq = r / a.s.hkv;
-    mb = a.nmb - 1 - mbi;  // causal: the longest tiles start first
+    mb = a.nmb - 1 - rank;
   }
   const SeqInfo si = seq_info(a.s, seq);
   const int prows = si.lq * G;
@@ -100,44 +103,66 @@ void fwd_kernel(const FwdArgs a) {
   const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
   const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2) : 0u;
   const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
-  const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
-  const auto rv = make_rsrc((const uint16_t*)a.v + kbase_e, kbytes);
 
   // Q^T as the B operand: lane holds 8 consecutive dims of its query row per k-step.
   u32x4 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; s++) qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
 
+  // ---- loop-invariant addressing
+  // K/V tile t is read through descriptors rebased to its first row, so the
+  // per-lane DMA offsets below do not change from tile to tile.
+  uint32_t dma_off[SLABS];
+#pragma unroll
+  for (int n = 0; n < SLABS; n++) {
+    const int byte = (wave * SLABS + n) * 1024 + lane * 16;
+    const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
+    dma_off[n] = (uint32_t)((r * krow + (pos ^ swz<D>(r)) * 8) * 2);
+  }
+  // K as the A operand: lane reads row (32 kb + l32), chunk (2 s + hh); the
+  // swizzle of row 32 kb + l32 equals that of l32, so kb is a constant offset.
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; s++) k_off[s] = tile_off<D>(l32, 2 * s + hh);
+  // V^T as the A operand through transposing reads: rows 16 t2 + 4 hh + esrc
+  // (+8 for the second half of the k-step), 4 columns starting at col.
+  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
+  int v_off[DB][2];
+#pragma unroll
+  for (int d = 0; d < DB; d++) {
+    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+#pragma unroll
+    for (int w = 0; w < 2; w++) v_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
+  }
+
   auto load_tile = [&](int t, int buf) {
     char* kd = smem + buf * 2 * TILE;
     char* vd = kd + TILE;
+    const int64_t skip = (int64_t)t * FWD_BN * krow;  // elements before tile t
+    const uint32_t left = kbytes - (uint32_t)(skip * 2);
+    const auto tk = make_rsrc((const uint16_t*)a.k + kbase_e + skip, left);
+    const auto tv = make_rsrc((const uint16_t*)a.v + kbase_e + skip, left);
 #pragma unroll
     for (int n = 0; n < SLABS; n++) {
       const int slab = wave * SLABS + n;
-      const int byte = slab * 1024 + lane * 16;
-      const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      const int c = pos ^ swz<D>(r);
-      const uint32_t goff = (uint32_t)((((int64_t)(t * FWD_BN + r)) * krow + c * 8) * 2);
-      buf_load_lds16(rk, kd + slab * 1024, goff);
-      buf_load_lds16(rv, vd + slab * 1024, goff);
+      buf_load_lds16(tk, kd + slab * 1024, dma_off[n]);
+      buf_load_lds16(tv, vd + slab * 1024, dma_off[n]);
     }
   };
 
   f32x16 acc[DB];
 #pragma unroll
   for (int d = 0; d < DB; d++) acc[d] = f32x16{};
+  // m_run: the reference max (raw score units) the accumulators are scaled to.
+  // It is raised only when a tile's max exceeds it by more than 8 in log2
+  // units, so p = 2^(s*c - m_run*c) stays below 2^8 and most tiles skip the
+  // rescale of the accumulators; O = acc / l is the same for any reference.
   float m_run = -INFINITY, l_part = 0.f;
   const float c = a.scale_log2;
+  constexpr float RESCALE_LOG2 = 8.f;
 
-  // transposing-read geometry of this lane (V^T as the A operand)
-  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
-
-  if (t_begin < t_end) load_tile(t_begin, 0);
-  for (int t = t_begin; t < t_end; t++) {
-    const int buf = (t - t_begin) & 1;
-    wait_vmcnt<0>();                 // this lane's part of tile t is in LDS
-    __builtin_amdgcn_s_barrier();    // everyone's part, and everyone is done with tile t-1
-    if (t + 1 < t_end) load_tile(t + 1, buf ^ 1);
+  auto tile = [&](int t, int buf, auto MASK) {
+    constexpr bool masked = decltype(MASK)::value;
     const char* kt = smem + buf * 2 * TILE;
     const char* vt = kt + TILE;
 
@@ -145,14 +170,12 @@ void fwd_kernel(const FwdArgs a) {
     f32x16 st[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; kb++) {
-      st[kb] = f32x16{};
+      st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[0]), qf[0], f32x16{});
 #pragma unroll
-      for (int s = 0; s < KS; s++)
-        st[kb] = mfma32<F16>(lds_read16(kt + tile_off<D>(kb * 32 + l32, 2 * s + hh)), qf[s], st[kb]);
+      for (int s = 1; s < KS; s++) st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], st[kb]);
     }
-
-    const int j0 = t * FWD_BN;
-    if (!(j0 >= full_lo && j0 + FWD_BN - 1 <= full_hi)) {
+    if constexpr (masked) {
+      const int j0 = t * FWD_BN;
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
 #pragma unroll
@@ -162,18 +185,24 @@ void fwd_kernel(const FwdArgs a) {
         }
     }
 
-    // online softmax update
+    // online softmax
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; kb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) mx = fmaxf(mx, st[kb][i]);
     mx = half_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2_fast((m_run - m_use) * c);
-    m_run = m_new;
-    const float mc = m_use * c;
+    const bool raise = mx * c > m_run * c + RESCALE_LOG2;  // false while both are -inf
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      // lanes that do not raise keep their reference (alpha = 1; their m_run
+      // may still be -inf); a first finite max gives alpha = 2^-inf = 0
+      const float alpha = raise ? exp2_fast((m_run - mx) * c) : 1.f;
+      m_run = raise ? mx : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; d++) acc[d] *= alpha;
+    }
+    const float mc = m_run == -INFINITY ? 0.f : m_run * c;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; kb++)
@@ -183,13 +212,11 @@ void fwd_kernel(const FwdArgs a) {
         st[kb][i] = p;
         rs += p;
       }
-    l_part = fmaf(l_part, alpha, rs);
-#pragma unroll
-    for (int d = 0; d < DB; d++) acc[d] *= alpha;
+    l_part += rs;
 
-    // P^T as the B operand: k-step u of block kb covers keys
-    // kb*32 + 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}, which are exactly the
-    // accumulator registers 8u..8u+7 of this lane.
+    // P^T as the B operand: k-step t2 = 2 kb + u covers keys
+    // 32 kb + 16 u + {4hh..4hh+3, 8+4hh..8+4hh+3}: accumulator registers
+    // 8u..8u+7 of this lane.
     u32x4 pf[PT];
 #pragma unroll
     for (int t2 = 0; t2 < PT; t2++) {
@@ -201,17 +228,37 @@ void fwd_kernel(const FwdArgs a) {
     }
     // O^T += V^T P^T, V^T read with the same key order as P.
 #pragma unroll
-    for (int d = 0; d < DB; d++) {
-      const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+    for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int t2 = 0; t2 < PT; t2++) {
-        const int kbase = t2 * 16 + 4 * hh + esrc;
-        const u32x2 a1 = lds_read_tr(vt + tile_off<D>(kbase, col >> 3) + (jsrc & 1) * 8);
-        const u32x2 a2 = lds_read_tr(vt + tile_off<D>(kbase + 8, col >> 3) + (jsrc & 1) * 8);
+        const u32x2 a1 = lds_read_tr(vt + t2 * 16 * ROWB + v_off[d][0]);
+        const u32x2 a2 = lds_read_tr(vt + t2 * 16 * ROWB + v_off[d][1]);
         acc[d] = mfma32<F16>(u32x4{a1[0], a1[1], a2[0], a2[1]}, pf[t2], acc[d]);
       }
+  };
+
+  // Tile t sits in buffer (t - t_begin) & 1 while tile t+1 is fetched into
+  // the other.  Three loops -- masked head, unmasked interior, masked tail --
+  // so that each loop has a single body.
+  auto run = [&](int t0, int t1, auto MASK) {
+    for (int t = t0; t < t1; t++) {
+      const int buf = (t - t_begin) & 1;
+      wait_vmcnt<0>();                 // this lane's part of tile t is in LDS
+      __builtin_amdgcn_s_barrier();    // everyone's part; everyone is done with tile t-1
+      if (t + 1 < t_end) load_tile(t + 1, buf ^ 1);
+      tile(t, buf, MASK);
     }
+  };
+  int ti0 = t_begin, ti1 = t_begin;  // interior tiles [ti0, ti1)
+  if (full_hi >= full_lo) {
+    ti0 = max(t_begin, (full_lo + FWD_BN - 1) / FWD_BN);
+    ti1 = min(t_end, (full_hi + 1) / FWD_BN);
+    if (ti1 <= ti0) ti0 = ti1 = t_begin;
   }
+  if (t_begin < t_end) load_tile(t_begin, 0);
+  run(t_begin, ti0, std::true_type{});
+  run(ti0, ti1, std::false_type{});
+  run(ti1, t_end, std::true_type{});
 
   // ---- epilogue
   const float l_tot = half_sum(l_part);
