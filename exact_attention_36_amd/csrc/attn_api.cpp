@@ -60,7 +60,7 @@ attn_status check_params(const attn_params* p) {
 
 attn_status check_extent(int64_t max_q, int64_t max_k, const attn_params* p) {
   const int64_t D = p->head_dim;
-  if ((max_q + FWD_BM) * p->heads_q * D * 4 >= OFF_LIMIT)
+  if ((max_q + 256) * p->heads_q * D * 4 >= OFF_LIMIT)
     return fail(ATTN_ENOTSUP, "a sequence of %lld queries exceeds the 32-bit offset range", (long long)max_q);
   if ((max_k + BWD_BN) * p->heads_kv * D * 4 >= OFF_LIMIT)
     return fail(ATTN_ENOTSUP, "a sequence of %lld keys exceeds the 32-bit offset range", (long long)max_k);
@@ -96,13 +96,26 @@ int choose_split(int64_t base_ctas, int64_t sk) {
   return (int)std::max<int64_t>(n, 1);
 }
 
-size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_split_out) {
+// Query rows per forward workgroup: 256 (two 32-row blocks per wave, half
+// the LDS traffic per MFMA) when every group has at least two such blocks and
+// they fill the chip; 128 otherwise (short or decode-shaped problems).
+int choose_bm(int64_t rows_per_group, int64_t groups) {
+  return (rows_per_group >= 512 && (rows_per_group / 256) * groups >= 256 && false) ? 256 : 128;
+}
+
+size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_split_out, int* bm_out) {
   const int G = p->heads_q / p->heads_kv;
-  const int64_t nmb = cdiv(sq * G, FWD_BM);
+  int bm = choose_bm(sq * G, p->heads_kv * B);
+  int64_t nmb = cdiv(sq * G, bm);
   const int ns = choose_split(nmb * p->heads_kv * B, sk);
+  if (ns > 1 && bm != 128) {  // split-KV runs 128-row tiles
+    bm = 128;
+    nmb = cdiv(sq * G, bm);
+  }
   if (n_split_out) *n_split_out = ns;
+  if (bm_out) *bm_out = bm;
   if (ns <= 1) return 0;
-  const int64_t rows = (int64_t)ns * B * p->heads_kv * nmb * FWD_BM;
+  const int64_t rows = (int64_t)ns * B * p->heads_kv * nmb * bm;
   return align_up(rows * p->head_dim * 4) + align_up(rows * 4);
 }
 
@@ -147,20 +160,22 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   const int G = a.s.group;
   a.n_split = 1;
   if (packed) {
-    a.nblk = (int32_t)((total_q * G) / FWD_BM + nseq);
+    a.bm = (total_q * G >= 512 * (int64_t)nseq && (total_q * G) / 256 * p->heads_kv >= 256) ? 256 : 128;
+    a.nblk = (int32_t)((total_q * G) / a.bm + nseq);
     const int64_t ctas = (int64_t)a.nblk * p->heads_kv;
     if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = (int32_t)ctas;
     (void)max_q;
   } else {
-    a.nmb = (int32_t)cdiv(sq * G, FWD_BM);
-    int ns = 1;
-    const size_t need = fwd_ws(p, nseq, sq, sk, &ns);
+    int ns = 1, bm = 128;
+    const size_t need = fwd_ws(p, nseq, sq, sk, &ns, &bm);
     attn_status st = check_ws(ws, ws_bytes, need);
     if (st != ATTN_OK) return st;
+    a.bm = bm;
+    a.nmb = (int32_t)cdiv(sq * G, bm);
     a.n_split = ns;
     if (ns > 1) {
-      const int64_t rows = (int64_t)ns * nseq * p->heads_kv * a.nmb * FWD_BM;
+      const int64_t rows = (int64_t)ns * nseq * p->heads_kv * a.nmb * bm;
       a.o_part = (float*)ws;
       a.lse_part = (float*)((char*)ws + align_up(rows * p->head_dim * 4));
     }
@@ -237,7 +252,7 @@ int32_t attn_version(void) { return 100; }
 
 size_t attn_fwd_workspace_size(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k) {
   if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1 || seqlen_k < 1) return 0;
-  return fwd_ws(p, batch, seqlen_q, seqlen_k, nullptr);
+  return fwd_ws(p, batch, seqlen_q, seqlen_k, nullptr, nullptr);
 }
 
 size_t attn_bwd_workspace_size(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
@@ -313,7 +328,7 @@ static attn_status check_varlen(const attn_params* p, int32_t num_seqs, int64_t 
   if (max_q < 0 || max_k < 0) return fail(ATTN_EINVAL, "max_seqlen_q and max_seqlen_k must be >= 0");
   if ((st = check_extent(max_q, max_k, p)) != ATTN_OK) return st;
   const int64_t G = p->heads_q / p->heads_kv;
-  if ((total_q * G) / FWD_BM + num_seqs >= INT32_MAX / p->heads_kv || total_q >= INT32_MAX ||
+  if ((total_q * G) / 128 + num_seqs >= INT32_MAX / p->heads_kv || total_q >= INT32_MAX ||
       total_k >= INT32_MAX)
     return fail(ATTN_ENOTSUP, "problem too large");
   return ATTN_OK;

@@ -88,6 +88,28 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_base), 16, off, 0, 0, 0);
 }
 
+// The same global -> LDS copy for prefetching streams, issued so that the
+// compiler does not track it: the compiler cannot tell which LDS buffer a DMA
+// writes and would otherwise wait for every outstanding DMA before any later
+// LDS read, serialising the prefetch.  Callers order these copies with
+// explicit wait_vmcnt + s_barrier.  The descriptor is a raw buffer
+// (base, 0 stride, size in bytes, gfx9 dword 3), bounds-checked by hardware.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return i32x4{(int32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+               (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu),
+               (int32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+__device__ __forceinline__ void dma_lds16(i32x4 rsrc, const void* lds_base, uint32_t off) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(off), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- LDS tiles
 // A [rows][D] 16-bit tile is stored with 16-byte chunk c of row r at chunk
 // position c ^ swz(r).  The two access patterns of the kernels -- 16 lanes
