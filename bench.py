@@ -149,12 +149,16 @@ def main():
     dom = max(kern, key=lambda n: kern[n][1])
     n_l, tot = kern[dom]
     avg_ms = tot / n_l
-    flop_of = {"fwd": fwd_flop, "bwd_dkdv": bwd_flop}
+    # MFMA work each kernel is built to do: the forward 2 products per visible
+    # pair, the key-major dK/dV kernel 4 (S, dP, dV, dK), the query-major dQ
+    # kernel 3 (S, dP, dQ); the step's value keeps the 4:10 convention.
+    flop_of = {"fwd": fwd_flop, "bwd_dkdv": 8.0 * D * pairs, "bwd_dq": 6.0 * D * pairs}
     roof = None
     if dom in flop_of:
         ach = flop_of[dom] / (avg_ms * 1e-3) / 1e12
         srcs = {"fwd": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
-                "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"]}[dom]
+                "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
+                "bwd_dq": ["exact_attention_36_amd/csrc/attn_bwd.hip"]}[dom]
         srcs = srcs + ["exact_attention_36_amd/csrc/attn_device.h", "exact_attention_36_amd/csrc/attn_common.h",
                        "exact_attention_36_amd/csrc/attn_kernels.h"]
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

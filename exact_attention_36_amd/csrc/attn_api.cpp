@@ -119,16 +119,17 @@ size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_sp
   return align_up(rows * p->head_dim * 4) + align_up(rows * 4);
 }
 
+// Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like lse.
 struct BwdWs {
-  size_t dq_acc, delta, lse2, total;
+  size_t delta, lse2, total;
 };
 BwdWs bwd_ws(const attn_params* p, int64_t tq, int32_t grad_dtype) {
+  (void)grad_dtype;
   BwdWs w{};
   const int64_t rows = tq * p->heads_q;
-  w.dq_acc = grad_dtype == ATTN_FP32 ? 0 : align_up(rows * p->head_dim * 4);
   w.delta = align_up(rows * 4);
   w.lse2 = align_up(rows * 4);
-  w.total = w.dq_acc + w.delta + w.lse2;
+  w.total = w.delta + w.lse2;
   return w;
 }
 
@@ -214,24 +215,29 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   a.dv = dv;
   a.grad_f32 = grad_dtype == ATTN_FP32;
   char* wp = (char*)ws;
-  a.dq_acc = a.grad_f32 ? (float*)dq : (float*)wp;
-  wp += w.dq_acc;
   a.delta = (float*)wp;
   wp += w.delta;
   a.lse2 = (float*)wp;
   const float scale = resolve_scale(p);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  const int64_t G = p->heads_q / p->heads_kv;
   if (packed) {
     a.nblk = (int32_t)(total_k / BWD_BN + nseq);
-    const int64_t ctas = (int64_t)a.nblk * p->heads_kv;
-    if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
-    a.total_ctas = (int32_t)ctas;
+    a.nblk_q = (int32_t)((total_q * G) / BWD_QBM + nseq);
+    const int64_t ctas = (int64_t)a.nblk * p->heads_kv, ctas_q = (int64_t)a.nblk_q * p->heads_kv;
+    if (ctas >= INT32_MAX || ctas_q >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    a.total_ctas = total_k > 0 ? (int32_t)ctas : 0;
+    a.total_ctas_q = total_q > 0 ? (int32_t)ctas_q : 0;
   } else {
+    if ((int64_t)p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.nkb = (int32_t)cdiv(sk, BWD_BN);
+    a.nmb = (int32_t)cdiv(sq * G, BWD_QBM);
     const int64_t ctas = GroupGrid{(int)((int64_t)p->heads_kv * nseq), a.nkb}.grid_size();
-    if (ctas >= INT32_MAX || (int64_t)p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
+    const int64_t ctas_q = GroupGrid{(int)((int64_t)p->heads_kv * nseq), a.nmb}.grid_size();
+    if (ctas >= INT32_MAX || ctas_q >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = (int32_t)ctas;
+    a.total_ctas_q = (int32_t)ctas_q;
   }
   return launched(launch_bwd(a, p->head_dim, p->dtype == ATTN_FP16, (hipStream_t)stream));
 }

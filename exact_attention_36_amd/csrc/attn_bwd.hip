@@ -18,16 +18,24 @@
 //
 // Kernels, in stream order:
 //   bwd_zero_kernel   clears dsinks
-//   bwd_pre_kernel    D_i, lse' (log2 units), dsink partials, clears dQ_acc
-//   bwd_dkdv_kernel   key-major main loop: one workgroup per 128-key block of
-//                     one kv head; dK and dV accumulate in registers over the
-//                     visible query rows of all the group's q heads (fp32
-//                     across the GQA group: fa4-jax page, restrictions
-//                     paragraph); dQ is accumulated with fp32 atomics
-//   bwd_dq_kernel     dQ_acc -> the gradient dtype
-// The packed (varlen) grid covers only the real key blocks: sequence i's
-// blocks start at floor(cu_k[i] / 128) + i and a workgroup finds its
-// sequence by binary search (dew-flash-attn page, packed-backward paragraph).
+//   bwd_pre_kernel    D_i, lse' (log2 units), dsink partials
+//   bwd_dq_kernel     query-major: one workgroup per 128 packed query rows
+//                     streams the visible K/V tiles (like the forward),
+//                     recomputes S, P, dP, dS and accumulates dQ in
+//                     registers; dQ is written once, no atomics
+//   bwd_dkdv_kernel   key-major: one workgroup per 128-key block of one kv
+//                     head streams the visible query blocks of all the
+//                     group's q heads, recomputes S, P, dP, dS and
+//                     accumulates dK and dV in registers (fp32 across the
+//                     GQA group: fa4-jax page, restrictions paragraph)
+// The two main kernels recompute S and dP each (7 products per visible
+// block instead of 5) in exchange for no fp32 atomics, no dS exchange
+// through LDS and two waves per SIMD in both.  The packed (varlen) grids
+// cover only the real blocks: sequence i's blocks start at
+// floor(cu[i] * rows / block) + i and a workgroup finds its sequence by
+// binary search (dew-flash-attn page, packed-backward paragraph).
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace attn {
@@ -59,14 +67,10 @@ __global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const BwdArgs a) {
       part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), to_f32<F16>((uint16_t)(gv[e] & 0xFFFF)), part);
       part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), to_f32<F16>((uint16_t)(gv[e] >> 16)), part);
     }
-    float* dq = a.dq_acc + row * D + sub * 8;
-    *(f32x4*)dq = f32x4{};
-    *(f32x4*)(dq + 4) = f32x4{};
   }
   // reduce over the LPR lanes of the row
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, LPR);
-  float dsink_part = 0.f;
   if (ok && sub == 0) {
     const int64_t t = row / a.s.hq;
     int64_t li;
@@ -83,37 +87,245 @@ __global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const BwdArgs a) {
       lse2 = mx + log2_fast(1.f + exp2_fast(mn - mx));  // log2(2^lse2 + 2^s2)
       // 1 - g = sigmoid(sink - lse): the sink's share of the denominator
       const float one_minus_g = lse == -INFINITY ? 1.f : 1.f / (1.f + exp2_fast(lse * LOG2E - s2));
-      dsink_part = -one_minus_g * part;
+      const float dsink_part = -one_minus_g * part;
+      if (a.dsinks && dsink_part != 0.f) atomicAdd(a.dsinks + h, dsink_part);
     }
     a.delta[li] = part;
     a.lse2[li] = lse == -INFINITY ? INFINITY : lse2;  // empty rows: P = 0
   }
-  if (a.sinks && a.dsinks) {
-    // rows of one block may span several heads: add per row-leader lane
-    if (ok && sub == 0 && dsink_part != 0.f) atomicAdd(a.dsinks + h, dsink_part);
+}
+
+// ------------------------------------------------------------------ dQ
+// Work tile as in the forward: 128 packed query rows of one kv group, 4 waves
+// of 32 rows; a lane owns one query row (S^T = K Q^T orientation).  Per K/V
+// tile of 64 keys:  S^T = K Q^T,  dP^T = V dO^T  (K, V natural 16-byte LDS
+// reads), P and dS lane-locally from the row's lse' and D, then
+// dQ^T += K^T dS^T with K^T through transposing LDS reads.
+template <int D, bool F16>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const BwdArgs a) {
+  constexpr int BM = BWD_QBM;
+  constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
+  constexpr int TILE = FWD_BN * ROWB;
+  constexpr int SLABS = TILE / 1024 / 4;
+  constexpr int KB = FWD_BN / 32, PT = FWD_BN / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int G = a.s.group;
+  int seq, g, mb;
+  if (a.s.cu_q) {
+    const int id = xcd_remap(blockIdx.x, a.total_ctas_q);
+    g = id / a.nblk_q;
+    const int t = id - g * a.nblk_q;
+    seq = find_sequence(a.s.cu_q, a.s.nseq, t, G, BM);
+    mb = t - packed_block_start(a.s.cu_q, seq, G, BM);
+  } else {
+    int grp, rank;
+    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nmb}.decode(blockIdx.x, grp, rank)) return;
+    g = grp % a.s.hkv;
+    seq = grp / a.s.hkv;
+    mb = a.nmb - 1 - rank;  // causal: the longest tiles start first
+  }
+  const SeqInfo si = seq_info(a.s, seq);
+  const int prows = si.lq * G;
+  const int p0 = mb * BM;
+  if (p0 >= prows) return;
+
+  const Band band(a.s, si);
+  const int i_lo = div_group(p0, a.s), i_hi = div_group(min(p0 + BM, prows) - 1, a.s);
+  const int kv_lo = band.kmin(i_lo), kv_hi = band.kmax(i_hi);
+  int t_begin = 0, t_end = 0;
+  if (kv_hi >= kv_lo) {
+    t_begin = kv_lo / FWD_BN;
+    t_end = kv_hi / FWD_BN + 1;
+  }
+  const int full_lo = band.kmin(i_hi), full_hi = band.kmax(i_lo);
+
+  const int my_p = p0 + wave * 32 + l32;
+  const int my_i = div_group(my_p, a.s);
+  const int my_hl = my_p - my_i * G;
+  const int my_h = g * G + my_hl;
+  const int my_kmin = band.kmin(my_i), my_kmax = band.kmax(my_i);
+
+  const int64_t qrow = (int64_t)a.s.hq * D, krow = (int64_t)a.s.hkv * D;
+  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * D;
+  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 2) : 0u;
+  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * D) * 2);
+  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
+  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2) : 0u;
+  const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
+  const auto rdo = make_rsrc((const uint16_t*)a.dout + qbase_e, qbytes);
+
+  u32x4 qf[KS], df[KS];
+#pragma unroll
+  for (int s = 0; s < KS; s++) {
+    qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+    df[s] = buf_load16(rdo, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+  }
+  float row_lse2 = INFINITY, row_d = 0.f;
+  if (my_p < prows) {
+    const int64_t li = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
+                                : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
+    row_lse2 = a.lse2[li];
+    row_d = a.delta[li];
+  }
+  const float c = a.scale_log2;
+  const float mlse = row_lse2 == INFINITY ? 0.f : row_lse2;  // empty rows are fully masked
+
+  uint32_t dma_off[SLABS];
+#pragma unroll
+  for (int n = 0; n < SLABS; n++) {
+    const int byte = (wave * SLABS + n) * 1024 + lane * 16;
+    const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
+    dma_off[n] = (uint32_t)((r * krow + (pos ^ swz<D>(r)) * 8) * 2);
+  }
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; s++) k_off[s] = tile_off<D>(l32, 2 * s + hh);
+  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
+  int t_off[DB][2];
+#pragma unroll
+  for (int d = 0; d < DB; d++) {
+    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+#pragma unroll
+    for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
+  }
+  auto load_tile = [&](int t) {
+    const int buf = (t - t_begin) & 1;
+    const int64_t skip = (int64_t)t * FWD_BN * krow;
+    const uint32_t left = kbytes - (uint32_t)(skip * 2);
+    const i32x4 rk = make_rsrc_words((const uint16_t*)a.k + kbase_e + skip, left);
+    const i32x4 rv = make_rsrc_words((const uint16_t*)a.v + kbase_e + skip, left);
+#pragma unroll
+    for (int n = 0; n < SLABS; n++) {
+      dma_lds16(rk, smem + buf * TILE + (wave * SLABS + n) * 1024, dma_off[n]);
+      dma_lds16(rv, smem + (2 + buf) * TILE + (wave * SLABS + n) * 1024, dma_off[n]);
+    }
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; d++) acc[d] = f32x16{};
+
+  auto tile = [&](int t, auto MASK) {
+    constexpr bool masked = decltype(MASK)::value;
+    const int buf = (t - t_begin) & 1;
+    const char* kt = smem + buf * TILE;
+    const char* vt = smem + (2 + buf) * TILE;
+    f32x16 st[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+      for (int s = 0; s < KS; s++) {
+        st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], s == 0 ? f32x16{} : st[kb]);
+        dp[kb] = mfma32<F16>(lds_read16(vt + kb * 32 * ROWB + k_off[s]), df[s], s == 0 ? f32x16{} : dp[kb]);
+      }
+    const int j0 = t * FWD_BN;
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float p = exp2_fast(fmaf(st[kb][i], c, -mlse));
+        if constexpr (masked) {
+          const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (j < my_kmin || j > my_kmax) p = 0.f;
+        }
+        st[kb][i] = p * (dp[kb][i] - row_d);  // dS
+      }
+    u32x4 sf[PT];
+#pragma unroll
+    for (int t2 = 0; t2 < PT; t2++) {
+      const int kb = t2 >> 1, u = t2 & 1;
+      sf[t2] = u32x4{pack2<F16>(st[kb][8 * u + 0], st[kb][8 * u + 1]), pack2<F16>(st[kb][8 * u + 2], st[kb][8 * u + 3]),
+                     pack2<F16>(st[kb][8 * u + 4], st[kb][8 * u + 5]), pack2<F16>(st[kb][8 * u + 6], st[kb][8 * u + 7])};
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int d = 0; d < DB; d++)
+#pragma unroll
+      for (int t2 = 0; t2 < PT; t2++) {
+        const u32x2 a1 = lds_read_tr(kt + t2 * 16 * ROWB + t_off[d][0]);
+        const u32x2 a2 = lds_read_tr(kt + t2 * 16 * ROWB + t_off[d][1]);
+        acc[d] = mfma32<F16>(u32x4{a1[0], a1[1], a2[0], a2[1]}, sf[t2], acc[d]);
+      }
+  };
+  auto run = [&](int t0, int t1, auto MASK) {
+    for (int t = t0; t < t1; t++) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (t + 1 < t_end) load_tile(t + 1);
+      tile(t, MASK);
+    }
+  };
+  int ti0 = t_begin, ti1 = t_begin;
+  if (full_hi >= full_lo) {
+    ti0 = max(t_begin, (full_lo + FWD_BN - 1) / FWD_BN);
+    ti1 = min(t_end, (full_hi + 1) / FWD_BN);
+    if (ti1 <= ti0) ti0 = ti1 = t_begin;
+  }
+  if (t_begin < t_end) load_tile(t_begin);
+  run(t_begin, ti0, std::true_type{});
+  run(ti0, ti1, std::false_type{});
+  run(ti1, t_end, std::true_type{});
+
+  // dQ = scale * acc; lane = query row, registers = dims 8(i/4) + 4hh + i%4 of each 32-block
+  if (a.grad_f32) {
+    const auto rw = make_rsrc((float*)a.dq + qbase_e, qbytes * 2);
+#pragma unroll
+    for (int d = 0; d < DB; d++)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const int dd = d * 32 + 8 * j4 + 4 * hh;
+        const u32x4 w{__builtin_bit_cast(uint32_t, acc[d][4 * j4] * a.scale),
+                      __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 1] * a.scale),
+                      __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 2] * a.scale),
+                      __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 3] * a.scale)};
+        buf_store16(w, rw, qoff * 2 + (uint32_t)(dd * 4));
+      }
+  } else {
+    const auto rw = make_rsrc((uint16_t*)a.dq + qbase_e, qbytes);
+#pragma unroll
+    for (int d = 0; d < DB; d++)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const int dd = d * 32 + 8 * j4 + 4 * hh;
+        const u32x2 w{pack2<F16>(acc[d][4 * j4] * a.scale, acc[d][4 * j4 + 1] * a.scale),
+                      pack2<F16>(acc[d][4 * j4 + 2] * a.scale, acc[d][4 * j4 + 3] * a.scale)};
+        buf_store8(w, rw, qoff + (uint32_t)(dd * 2));
+      }
   }
 }
 
+// ------------------------------------------------------------------ dK, dV
+// One workgroup per 128-key block of one kv head; wave w owns keys
+// 32w .. 32w+31 and keeps dK^T, dV^T (dims x its keys) in registers.  Per
+// block of 32 packed query rows: S = Q K^T and dP = dO V^T (lane = key
+// column, registers = query rows), P and dS with the rows' lse' and D from
+// LDS, dV^T += dO^T P and dK^T += Q^T dS (dO, Q through transposing LDS
+// reads).  dS is kept in fp16 (10 fraction bits) for dK; the Q tile is
+// therefore staged in LDS as fp16 (converted on the way in, exact for
+// inputs inside fp16's range) and K, used for S, is converted likewise.
 template <int D, bool F16>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
   constexpr int BN = BWD_BN, BM = BWD_BM;
-  constexpr int KTILE = BN * ROWB;          // K block in LDS (for dQ)
+  constexpr int VBLK = BN * ROWB;           // V block in LDS (B operand of dP)
   constexpr int QTILE = BM * ROWB;          // one Q (or dO) tile
-  constexpr int QSLABS = QTILE / 1024;      // 1 KB slabs per Q tile
-  constexpr int DST_ROWB = BM * 2;          // dS^T row: BM queries
-  __shared__ __attribute__((aligned(1024))) char smem[KTILE + 5 * QTILE + BN * DST_ROWB + 2 * 256];
-  char* const k_lds = smem;                              // K block (fp16 for the dQ product)
-  char* const q_lds = smem + KTILE;                      // [buf][Q, dO], input dtype
-  char* const qh_lds = q_lds + 4 * QTILE;                // Q tile as fp16 (bf16 inputs)
-  char* const ds_lds = qh_lds + QTILE;                   // dS^T [BN keys][BM queries], fp16
-  float* const st_lds = (float*)(ds_lds + BN * DST_ROWB);  // [buf][lse2 32 | delta 32]
+  constexpr int QCH = QTILE / 16 / THREADS; // 16-byte Q chunks per thread per tile
+  __shared__ __attribute__((aligned(1024))) char smem[VBLK + 4 * QTILE + 2 * 256];
+  char* const v_lds = smem;
+  char* const q_lds = smem + VBLK;              // [buf] fp16 Q tile
+  char* const do_lds = q_lds + 2 * QTILE;       // [buf] dO tile, input dtype
+  float* const st_lds = (float*)(do_lds + 2 * QTILE);  // [buf][lse2 32 | delta 32]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
   const int G = a.s.group;
+
   int seq, g, nb;
   if (a.s.cu_q) {
     const int id = xcd_remap(blockIdx.x, a.total_ctas);
@@ -149,57 +361,68 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
   const uint32_t kbytes = (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2);
   const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
-  const auto rdo = make_rsrc((const uint16_t*)a.dout + qbase_e, qbytes);
+  const i32x4 rdo = make_rsrc_words((const uint16_t*)a.dout + qbase_e, qbytes);
   const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
-  const auto rv = make_rsrc((const uint16_t*)a.v + kbase_e, kbytes);
-  // lse2 / delta of the group: index of packed row p is base + h*hstride + i
   const int64_t st_base = a.s.cu_q ? si.q0 : (int64_t)seq * a.s.hq * a.s.sq;
   const int64_t st_hs = a.s.cu_q ? a.s.total_q : a.s.sq;
   const int64_t st_total = a.s.cu_q ? (int64_t)a.s.hq * a.s.total_q : (int64_t)a.s.nseq * a.s.hq * a.s.sq;
-  const auto rl = make_rsrc(a.lse2, (uint32_t)(st_total * 4));
-  // dQ accumulator rows of this (sequence, kv group), fp32
-  const auto rdq = make_rsrc(a.dq_acc + qbase_e, si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 4) : 0u);
-  const auto rd = make_rsrc(a.delta, (uint32_t)(st_total * 4));
+  const i32x4 rl = make_rsrc_words(a.lse2, (uint32_t)(st_total * 4));
+  const i32x4 rd = make_rsrc_words(a.delta, (uint32_t)(st_total * 4));
 
-  // K block -> LDS (swizzled), for the transposing reads of dQ = dS K
+  // V block -> LDS (swizzled) once
   {
-    constexpr int SLABS = KTILE / 1024 / 4;
+    const i32x4 rv = make_rsrc_words((const uint16_t*)a.v + kbase_e, kbytes);
+    constexpr int SLABS = VBLK / 1024 / 4;
 #pragma unroll
     for (int n = 0; n < SLABS; n++) {
       const int slab = wave * SLABS + n;
       const int byte = slab * 1024 + lane * 16;
       const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      const int c = pos ^ swz<D>(r);
-      buf_load_lds16(rk, k_lds + slab * 1024, (uint32_t)((((int64_t)(j0 + r)) * krow + c * 8) * 2));
+      dma_lds16(rv, v_lds + slab * 1024, (uint32_t)((((int64_t)(j0 + r)) * krow + (pos ^ swz<D>(r)) * 8) * 2));
     }
   }
-  // this wave's 32 keys as B operands (lane: key, 8 dims per k-step)
+  // this wave's 32 keys as the B operand of S (lane: key, 8 dims per k-step), fp16
   const int my_key = j0 + wave * 32 + l32;
-  u32x4 kf[KS], vf[KS];
+  u32x4 kf[KS];
   {
-    const uint32_t ko = (uint32_t)((int64_t)(my_key)*krow * 2);
+    const uint32_t ko = (uint32_t)((int64_t)my_key * krow * 2);
 #pragma unroll
     for (int s = 0; s < KS; s++) {
-      kf[s] = buf_load16(rk, ko + (uint32_t)((16 * s + 8 * hh) * 2));
-      vf[s] = buf_load16(rv, ko + (uint32_t)((16 * s + 8 * hh) * 2));
+      const u32x4 k = buf_load16(rk, ko + (uint32_t)((16 * s + 8 * hh) * 2));
+      kf[s] = F16 ? k : bf16x8_to_f16x8(k);
     }
   }
 
-  auto load_q = [&](int pb, int buf) {
-    char* qd = q_lds + buf * 2 * QTILE;
-    char* dd = qd + QTILE;
-    constexpr int SL = QSLABS / 4;  // slabs per wave
+  // Q tile staging: thread t handles 16-byte chunks t, t+256, ... of the tile
+  auto q_fetch = [&](int pb, u32x4 (&stage)[QCH]) {
+#pragma unroll
+    for (int n = 0; n < QCH; n++) {
+      const int ch = threadIdx.x + n * THREADS;
+      const int r = ch / (D / 8), cc = ch % (D / 8);
+      const int p = pb * BM + r;
+      const int i = div_group(p, a.s), hl = p - i * G;
+      stage[n] = buf_load16(rq, (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + cc * 8) * 2));
+    }
+  };
+  auto q_store = [&](int buf, const u32x4 (&stage)[QCH]) {
+#pragma unroll
+    for (int n = 0; n < QCH; n++) {
+      const int ch = threadIdx.x + n * THREADS;
+      const int r = ch / (D / 8), cc = ch % (D / 8);
+      *LDS_PTR(u32x4, q_lds + buf * QTILE + tile_off<D>(r, cc)) = F16 ? stage[n] : bf16x8_to_f16x8(stage[n]);
+    }
+  };
+  auto do_fetch = [&](int pb, int buf) {
+    char* dd = do_lds + buf * QTILE;
+    constexpr int SL = QTILE / 1024 / 4;  // 1 KB slabs per wave
 #pragma unroll
     for (int n = 0; n < SL; n++) {
       const int slab = wave * SL + n;
       const int byte = slab * 1024 + lane * 16;
       const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      const int c = pos ^ swz<D>(r);
       const int p = pb * BM + r;
       const int i = div_group(p, a.s), hl = p - i * G;
-      const uint32_t off = (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + c * 8) * 2);
-      buf_load_lds16(rq, qd + slab * 1024, off);
-      buf_load_lds16(rdo, dd + slab * 1024, off);
+      dma_lds16(rdo, dd + slab * 1024, (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + (pos ^ swz<D>(r)) * 8) * 2));
     }
     if (wave == 0) {
       const int p = pb * BM + l32;
@@ -207,11 +430,29 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int64_t idx = st_base + (int64_t)(g * G + hl) * st_hs + i;
       // rows past the sequence read index 0 (valid memory); they are masked
       const uint32_t off = p < prows ? (uint32_t)(idx * 4) : 0u;
-      void* dst = st_lds + buf * 64;
-      if (hh == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, LDS_PTR(void, dst), 4, off, 0, 0, 0);
-      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, LDS_PTR(void, dst), 4, off, 0, 0, 0);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(st_lds + buf * 64));
+      // lanes 0-31 fetch lse', lanes 32-63 fetch D: lane l's dword lands at m0 + 4 l
+      if (hh == 0)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rl)
+                     : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rd)
+                     : "memory", "m0");
     }
   };
+
+  // loop-invariant LDS offsets
+  int q_off[KS];  // Q / dO as the A operand: row l32, chunk 2 s + hh
+#pragma unroll
+  for (int s = 0; s < KS; s++) q_off[s] = tile_off<D>(l32, 2 * s + hh);
+  int t_off[DB][2];  // transposing reads of Q / dO: rows 16 u + 4 hh + esrc (+8)
+#pragma unroll
+  for (int d = 0; d < DB; d++) {
+    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+#pragma unroll
+    for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
+  }
 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -220,148 +461,80 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     dv[d] = f32x16{};
   }
   const float c = a.scale_log2;
-  // key range fully visible to every row of q-block pb?  (checked per block)
-  const int my_kj = my_key;
-  // dQ step: wave -> (d block, key range)
-  constexpr int WPD = 4 / DB;                 // waves sharing one d block
-  const int dq_dblk = wave % DB, dq_kpart = wave / DB;
-  constexpr int DQ_KEYS = BN / WPD;           // keys summed by this wave
+  const char* vrow = v_lds + wave * 32 * ROWB;  // this wave's 32 V rows
 
-  if (pb_begin < pb_end) load_q(pb_begin, 0);
+  if (pb_begin < pb_end) {
+    u32x4 stage[QCH];
+    q_fetch(pb_begin, stage);
+    do_fetch(pb_begin, 0);
+    q_store(0, stage);
+  }
   for (int pb = pb_begin; pb < pb_end; pb++) {
     const int buf = (pb - pb_begin) & 1;
-    // tile pb was issued before the previous step's 16 dQ atomics
-    if (pb == pb_begin) wait_vmcnt<0>();
-    else wait_vmcnt<16>();
-    __builtin_amdgcn_s_barrier();
-    if (pb + 1 < pb_end) load_q(pb + 1, buf ^ 1);
-    const char* qt = q_lds + buf * 2 * QTILE;
-    const char* dot = qt + QTILE;
-    const float* stt = st_lds + buf * 64;
-    // dS is kept in fp16 (10 fraction bits instead of bf16's 7), so the dK and
-    // dQ products take fp16 copies of the Q tile and of the K block.
-    if constexpr (!F16) {
-      if (pb == pb_begin) {
-#pragma unroll
-        for (int n = 0; n < KTILE / 16 / THREADS; n++) {
-          char* p16 = k_lds + (threadIdx.x + n * THREADS) * 16;
-          *LDS_PTR(u32x4, p16) = bf16x8_to_f16x8(lds_read16(p16));
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < QTILE / 16 / THREADS; n++) {
-        const int off = (threadIdx.x + n * THREADS) * 16;
-        *LDS_PTR(u32x4, qh_lds + off) = bf16x8_to_f16x8(lds_read16(qt + off));
-      }
+    wait_vmcnt<0>();               // dO tile, row statistics (and V block) are in LDS
+    __builtin_amdgcn_s_barrier();  // everyone's writes visible; everyone is done with step pb-1
+    u32x4 stage[QCH];
+    const bool more = pb + 1 < pb_end;
+    if (more) {
+      q_fetch(pb + 1, stage);
+      do_fetch(pb + 1, buf ^ 1);
     }
-    const char* qh = F16 ? qt : qh_lds;
+    const char* qt = q_lds + buf * QTILE;
+    const char* dot = do_lds + buf * QTILE;
+    const float* stt = st_lds + buf * 64;
 
     // S and dP, [32 queries x 32 keys]: lane = key column, registers = query rows
-    f32x16 s_acc = f32x16{}, dp = f32x16{};
+    f32x16 s_acc, dp;
 #pragma unroll
     for (int s = 0; s < KS; s++) {
-      s_acc = mfma32<F16>(lds_read16(qt + tile_off<D>(l32, 2 * s + hh)), kf[s], s_acc);
-      dp = mfma32<F16>(lds_read16(dot + tile_off<D>(l32, 2 * s + hh)), vf[s], dp);
-    }
-    // row statistics of this lane's 16 rows: rows 8a + 4hh + 0..3
-    f32x4 l2[4], dl[4];
-#pragma unroll
-    for (int a4 = 0; a4 < 4; a4++) {
-      l2[a4] = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
-      dl[a4] = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
+      s_acc = mfma32<true>(lds_read16(qt + q_off[s]), kf[s], s == 0 ? f32x16{} : s_acc);
+      dp = mfma32<F16>(lds_read16(dot + q_off[s]), lds_read16(vrow + q_off[s]), s == 0 ? f32x16{} : dp);
     }
     const int p0 = pb * BM;
     const int qi_lo = div_group(p0, a.s), qi_hi = div_group(min(p0 + BM, prows) - 1, a.s);
     const bool interior = (p0 + BM <= prows) && j0 + wave * 32 >= band.kmin(qi_hi) &&
                           j0 + wave * 32 + 31 <= band.kmax(qi_lo);
-    f32x16 pm, dsm;
+    // row statistics of this lane's 16 rows: rows 8a + 4hh + 0..3
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int r = 8 * (i >> 2) + 4 * hh + (i & 3);
-      const float lse2 = l2[i >> 2][i & 3];
-      float p = exp2_fast(fmaf(s_acc[i], c, -lse2));
-      if (!interior) {
-        const int pr = p0 + r;
-        const int qi = div_group(pr, a.s);
-        const bool vis = pr < prows && my_kj < si.lk && my_kj >= band.kmin(qi) && my_kj <= band.kmax(qi);
-        if (!vis) p = 0.f;
+    for (int a4 = 0; a4 < 4; a4++) {
+      const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
+      const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = 4 * a4 + e;
+        float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
+        if (!interior) {
+          const int pr = p0 + 8 * a4 + 4 * hh + e;
+          const int qi = div_group(pr, a.s);
+          const bool vis = pr < prows && my_key < si.lk && my_key >= band.kmin(qi) && my_key <= band.kmax(qi);
+          if (!vis) p = 0.f;
+        }
+        s_acc[i] = p;
+        dp[i] = p * (dp[i] - dl[e]);  // dS
       }
-      pm[i] = p;
-      dsm[i] = p * (dp[i] - dl[i >> 2][i & 3]);
     }
-    // dV^T += dO^T P  (M = dims, N = this wave's keys, K = queries)
+    // P^T / dS^T as B operands: k-step u covers queries 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}
     u32x4 pf[2], sf[2];
 #pragma unroll
     for (int u = 0; u < 2; u++) {
-      pf[u] = u32x4{pack2<F16>(pm[8 * u + 0], pm[8 * u + 1]), pack2<F16>(pm[8 * u + 2], pm[8 * u + 3]),
-                    pack2<F16>(pm[8 * u + 4], pm[8 * u + 5]), pack2<F16>(pm[8 * u + 6], pm[8 * u + 7])};
-      sf[u] = u32x4{pack2<true>(dsm[8 * u + 0], dsm[8 * u + 1]), pack2<true>(dsm[8 * u + 2], dsm[8 * u + 3]),
-                    pack2<true>(dsm[8 * u + 4], dsm[8 * u + 5]), pack2<true>(dsm[8 * u + 6], dsm[8 * u + 7])};
+      pf[u] = u32x4{pack2<F16>(s_acc[8 * u + 0], s_acc[8 * u + 1]), pack2<F16>(s_acc[8 * u + 2], s_acc[8 * u + 3]),
+                    pack2<F16>(s_acc[8 * u + 4], s_acc[8 * u + 5]), pack2<F16>(s_acc[8 * u + 6], s_acc[8 * u + 7])};
+      sf[u] = u32x4{pack2<true>(dp[8 * u + 0], dp[8 * u + 1]), pack2<true>(dp[8 * u + 2], dp[8 * u + 3]),
+                    pack2<true>(dp[8 * u + 4], dp[8 * u + 5]), pack2<true>(dp[8 * u + 6], dp[8 * u + 7])};
     }
+    // dV^T += dO^T P,  dK^T += Q^T dS   (M = dims, N = this wave's keys, K = queries)
 #pragma unroll
-    for (int d = 0; d < DB; d++) {
-      const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+    for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        const int rb = u * 16 + 4 * hh + esrc;
-        const int off1 = tile_off<D>(rb, col >> 3) + (jsrc & 1) * 8;
-        const int off2 = tile_off<D>(rb + 8, col >> 3) + (jsrc & 1) * 8;
-        const u32x2 o1 = lds_read_tr(dot + off1), o2 = lds_read_tr(dot + off2);
+        const int rb = u * 16 * ROWB;
+        const u32x2 o1 = lds_read_tr(dot + rb + t_off[d][0]), o2 = lds_read_tr(dot + rb + t_off[d][1]);
         dv[d] = mfma32<F16>(u32x4{o1[0], o1[1], o2[0], o2[1]}, pf[u], dv[d]);
-      }
-    }
-    // dS^T -> LDS: row = key, 4 consecutive queries per 8-byte write
-    {
-      char* drow = ds_lds + (wave * 32 + l32) * DST_ROWB;
-#pragma unroll
-      for (int a4 = 0; a4 < 4; a4++) {
-        const int q4 = 8 * a4 + 4 * hh;  // first of 4 consecutive queries
-        *(u32x2*)(drow + q4 * 2) = u32x2{sf[a4 >> 1][2 * (a4 & 1)], sf[a4 >> 1][2 * (a4 & 1) + 1]};
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_s_barrier();
-    // dK^T += Q^T dS  (fp16)
-#pragma unroll
-    for (int d = 0; d < DB; d++) {
-      const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
-#pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int rb = u * 16 + 4 * hh + esrc;
-        const u32x2 q1 = lds_read_tr(qh + tile_off<D>(rb, col >> 3) + (jsrc & 1) * 8);
-        const u32x2 q2 = lds_read_tr(qh + tile_off<D>(rb + 8, col >> 3) + (jsrc & 1) * 8);
+        const u32x2 q1 = lds_read_tr(qt + rb + t_off[d][0]), q2 = lds_read_tr(qt + rb + t_off[d][1]);
         dk[d] = mfma32<true>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
       }
-    }
-    // dQ[32 q x 32 dims] += dS K over this wave's key range:
-    // A = dS (lane: query, 8 keys) via transposing reads of dS^T;
-    // B = K  (lane: dim, 8 keys) via transposing reads of the K block.
-    {
-      f32x16 dqa = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < DQ_KEYS / 16; ks++) {
-        const int kb = dq_kpart * DQ_KEYS + ks * 16 + 8 * hh + esrc;  // key row for this lane's source
-        const int qcol = 16 * (gq & 1) + 4 * jsrc;
-        const u32x2 s1 = lds_read_tr(ds_lds + kb * DST_ROWB + qcol * 2);
-        const u32x2 s2 = lds_read_tr(ds_lds + (kb + 4) * DST_ROWB + qcol * 2);
-        const int dcol = dq_dblk * 32 + 16 * (gq & 1) + 4 * jsrc;
-        const u32x2 k1 = lds_read_tr(k_lds + tile_off<D>(kb, dcol >> 3) + (jsrc & 1) * 8);
-        const u32x2 k2 = lds_read_tr(k_lds + tile_off<D>(kb + 4, dcol >> 3) + (jsrc & 1) * 8);
-        dqa = mfma32<true>(u32x4{s1[0], s1[1], s2[0], s2[1]}, u32x4{k1[0], k1[1], k2[0], k2[1]}, dqa);
-      }
-      // C: lane = dim column, registers = query rows.  Exactly 16 atomics per
-      // lane per step (rows past the sequence fall outside the buffer and are
-      // dropped by the hardware), so the next step can wait for its tile
-      // loads with vmcnt(16) without waiting for these atomics.
-      const int dcol = dq_dblk * 32 + l32;
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const int qi = div_group(pr, a.s), hl = pr - qi * G;
-        const uint32_t off = (uint32_t)((((int64_t)qi * a.s.hq + hl) * D + dcol) * 4);
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dqa[i] * a.scale, rdq, off, 0, 0);
-      }
-    }
+    // the next Q tile goes into the other buffer (last read in step pb-1)
+    if (more) q_store(buf ^ 1, stage);
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV; lane = key, registers = dims
@@ -386,16 +559,6 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
 }
 
-template <bool F16>
-__global__ __launch_bounds__(THREADS) void bwd_dq_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst,
-                                                         int64_t n4) {
-  const int64_t i = (int64_t)blockIdx.x * THREADS + threadIdx.x;
-  if (i < n4) {
-    const f32x4 v = ((const f32x4*)src)[i];
-    ((u32x2*)dst)[i] = u32x2{pack2<F16>(v[0], v[1]), pack2<F16>(v[2], v[3])};
-  }
-}
-
 template <int D, bool F16>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   if (a.sinks && a.dsinks) {
@@ -411,17 +574,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(THREADS), 0, st, a);
     timing_end(K_BWD_PRE, st);
   }
+  if (a.total_ctas_q > 0) {
+    timing_begin(K_BWD_DQ, st);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, F16>), dim3(a.total_ctas_q), dim3(THREADS), 0, st, a);
+    timing_end(K_BWD_DQ, st);
+  }
   if (a.total_ctas > 0) {
     timing_begin(K_BWD_DKDV, st);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
     timing_end(K_BWD_DKDV, st);
-  }
-  if (!a.grad_f32 && rows > 0) {
-    const int64_t n4 = rows * D / 4;
-    timing_begin(K_BWD_DQ, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<F16>), dim3((unsigned)((n4 + THREADS - 1) / THREADS)), dim3(THREADS), 0, st,
-                       (const float*)a.dq_acc, (uint16_t*)a.dq, n4);
-    timing_end(K_BWD_DQ, st);
   }
   return hipGetLastError();
 }

@@ -49,17 +49,22 @@ struct BwdArgs {
   const float* lse;       // sink-free log-sum-exp from the forward
   const float* sinks;     // [hq] or nullptr
   float* dsinks;          // [hq] or nullptr
-  float* dq_acc;          // fp32 [tokens_q][hq][D] accumulator
   float* delta;           // fp32, laid out like lse: D_i = <dO_i, O_i>
   float* lse2;            // fp32, laid out like lse: log-sum-exp with the sink, in log2 units
   void* dq; void* dk; void* dv;
   int32_t grad_f32;       // gradients written as fp32 (else the input dtype)
   float scale;            // softmax scale
   float scale_log2;       // scale * log2(e)
-  int32_t nkb;            // kv-blocks per (sequence, kv head) in batched mode
-  int32_t nblk;           // linear kv blocks per kv head in packed mode
+  // key-major dK/dV kernel
+  int32_t nkb;            // key blocks per (sequence, kv head) in batched mode
+  int32_t nblk;           // linear key blocks per kv head in packed mode
   int32_t total_ctas;
+  // query-major dQ kernel
+  int32_t nmb;            // query blocks per (sequence, kv head) in batched mode
+  int32_t nblk_q;         // linear query blocks per kv head in packed mode
+  int32_t total_ctas_q;
 };
+constexpr int BWD_QBM = 128;    // packed query rows per dQ workgroup
 
 // Optional per-launch timing (attn_timing_enable): the launchers call these
 // around every kernel launch; they record HIP events only while enabled.
