@@ -18,8 +18,9 @@
 //
 // Kernels, in stream order:
 //   bwd_zero_kernel   clears dsinks
-//   bwd_pre_kernel    D_i, lse' (log2 units), dsink partials
 //   bwd_dq_kernel     query-major: one workgroup per 128 packed query rows
+//                     computes the rows' D_i, lse' (log2 units, with the
+//                     sink) and dsink partials, then
 //                     streams the visible K/V tiles (like the forward),
 //                     recomputes S, P, dP, dS and accumulates dQ in
 //                     registers; dQ is written once, no atomics
@@ -43,56 +44,6 @@ namespace attn {
 __global__ void bwd_zero_kernel(float* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
-}
-
-// One group of D/8 lanes per (token, q head) row: each lane owns 8 dims.
-template <int D, bool F16>
-__global__ __launch_bounds__(THREADS) void bwd_pre_kernel(const BwdArgs a) {
-  constexpr int LPR = D / 8;            // lanes per row
-  constexpr int RPB = THREADS / LPR;    // rows per block
-  const int64_t rows = (int64_t)(a.s.cu_q ? a.s.total_q : a.s.nseq * a.s.sq) * a.s.hq;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
-  float part = 0.f;
-  int h = 0;
-  const bool ok = row < rows;
-  if (ok) {
-    const int64_t t = row / a.s.hq;  // token
-    h = (int)(row - t * a.s.hq);
-    const uint16_t* o = (const uint16_t*)a.o + row * D + sub * 8;
-    const uint16_t* g = (const uint16_t*)a.dout + row * D + sub * 8;
-    const u32x4 ov = *(const u32x4*)o, gv = *(const u32x4*)g;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), to_f32<F16>((uint16_t)(gv[e] & 0xFFFF)), part);
-      part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), to_f32<F16>((uint16_t)(gv[e] >> 16)), part);
-    }
-  }
-  // reduce over the LPR lanes of the row
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, LPR);
-  if (ok && sub == 0) {
-    const int64_t t = row / a.s.hq;
-    int64_t li;
-    if (a.s.cu_q) li = (int64_t)h * a.s.total_q + t;
-    else {
-      const int64_t b = t / a.s.sq, i = t - b * a.s.sq;
-      li = (b * a.s.hq + h) * a.s.sq + i;
-    }
-    const float lse = a.lse[li];
-    float lse2 = lse * LOG2E;
-    if (a.sinks) {
-      const float s2 = a.sinks[h] * LOG2E;
-      const float mx = fmaxf(lse2, s2), mn = fminf(lse2, s2);
-      lse2 = mx + log2_fast(1.f + exp2_fast(mn - mx));  // log2(2^lse2 + 2^s2)
-      // 1 - g = sigmoid(sink - lse): the sink's share of the denominator
-      const float one_minus_g = lse == -INFINITY ? 1.f : 1.f / (1.f + exp2_fast(lse * LOG2E - s2));
-      const float dsink_part = -one_minus_g * part;
-      if (a.dsinks && dsink_part != 0.f) atomicAdd(a.dsinks + h, dsink_part);
-    }
-    a.delta[li] = part;
-    a.lse2[li] = lse == -INFINITY ? INFINITY : lse2;  // empty rows: P = 0
-  }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -164,12 +115,61 @@ void bwd_dq_kernel(const BwdArgs a) {
     qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
     df[s] = buf_load16(rdo, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
   }
-  float row_lse2 = INFINITY, row_d = 0.f;
+  // Row statistics, computed here once per (query row, q head) and left in
+  // the workspace for the dK/dV kernel that runs after this one:
+  //   D = rowsum(dO * O), O being the stored (sink-gated) output;
+  //   lse' = log2(2^lse + 2^sink) in log2 units (+inf for an empty row, so
+  //   that P = 0 there);  dsink = -sum_rows (1 - gate) D, gate = sigmoid(lse - sink)
+  //   (dew-flash-attn page, sinks paragraph).
+  float row_d;
+  {
+    const auto ro = make_rsrc((const uint16_t*)a.o + qbase_e, qbytes);
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      const u32x4 ov = buf_load16(ro, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), part);
+        part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), to_f32<F16>((uint16_t)(df[s][e] >> 16)), part);
+      }
+    }
+    row_d = half_sum(part);  // the two lanes holding one row's halves
+  }
+  float row_lse2 = INFINITY, dsink_part = 0.f;
   if (my_p < prows) {
     const int64_t li = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
                                 : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
-    row_lse2 = a.lse2[li];
-    row_d = a.delta[li];
+    const float lse = a.lse[li];
+    if (lse != -INFINITY) {
+      row_lse2 = lse * LOG2E;
+      if (a.sinks) {
+        const float s2 = a.sinks[my_h] * LOG2E;
+        const float mx = fmaxf(row_lse2, s2), mn = fminf(row_lse2, s2);
+        dsink_part = -row_d / (1.f + exp2_fast(row_lse2 - s2));
+        row_lse2 = mx + log2_fast(1.f + exp2_fast(mn - mx));
+      }
+    } else {
+      dsink_part = -row_d;  // no visible key: the sink takes the whole denominator
+    }
+    if (hh == 0) {
+      a.delta[li] = row_d;
+      a.lse2[li] = row_lse2;
+    }
+  }
+  if (a.sinks && a.dsinks) {
+    // sum the block's rows per q head in LDS, then one global add per head;
+    // 128 consecutive packed rows hold at most 128 distinct heads, slot
+    // (p - p0) mod G names them without collisions
+    __shared__ float dsink_red[BM];
+    if (threadIdx.x < BM) dsink_red[threadIdx.x] = 0.f;
+    __syncthreads();
+    if (hh == 0 && dsink_part != 0.f) atomicAdd(&dsink_red[(my_p - p0) % G], dsink_part);
+    __syncthreads();
+    if ((int)threadIdx.x < min(G, BM)) {
+      const float v = dsink_red[threadIdx.x];
+      if (v != 0.f) atomicAdd(a.dsinks + g * G + (p0 + (int)threadIdx.x) % G, v);
+    }
   }
   const float c = a.scale_log2;
   const float mlse = row_lse2 == INFINITY ? 0.f : row_lse2;  // empty rows are fully masked
@@ -250,6 +250,10 @@ void bwd_dq_kernel(const BwdArgs a) {
         const u32x2 a2 = lds_read_tr(kt + t2 * 16 * ROWB + t_off[d][1]);
         acc[d] = mfma32<F16>(u32x4{a1[0], a1[1], a2[0], a2[1]}, sf[t2], acc[d]);
       }
+    // S/dP: 2 reads feed 2 MFMAs per step, reads 3 steps ahead; dQ: 2
+    // transposing reads per MFMA, 4 MFMAs ahead
+    sched_reads_ahead<KB * KS, 2, 2, 3>();
+    sched_reads_ahead<DB * PT, 1, 2, 4>();
   };
   auto run = [&](int t0, int t1, auto MASK) {
     for (int t = t0; t < t1; t++) {
@@ -533,6 +537,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         const u32x2 q1 = lds_read_tr(qt + rb + t_off[d][0]), q2 = lds_read_tr(qt + rb + t_off[d][1]);
         dk[d] = mfma32<true>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
       }
+    // S/dP: 3 reads (Q, dO, V) feed 2 MFMAs per step, 2 steps ahead;
+    // dV/dK: 4 transposing reads feed 2 MFMAs per step, 2 steps ahead
+    sched_reads_ahead<KS, 2, 3, 2>();
+    sched_reads_ahead<2 * DB, 2, 4, 2>();
     // the next Q tile goes into the other buffer (last read in step pb-1)
     if (more) q_store(buf ^ 1, stage);
   }
@@ -565,14 +573,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     timing_begin(K_BWD_ZERO, st);
     hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.s.hq + 255) / 256), dim3(256), 0, st, a.dsinks, a.s.hq);
     timing_end(K_BWD_ZERO, st);
-  }
-  const int64_t tq = a.s.cu_q ? a.s.total_q : (int64_t)a.s.nseq * a.s.sq;
-  const int64_t rows = tq * a.s.hq;
-  constexpr int RPB = THREADS / (D / 8);
-  if (rows > 0) {
-    timing_begin(K_BWD_PRE, st);
-    hipLaunchKernelGGL((bwd_pre_kernel<D, F16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(THREADS), 0, st, a);
-    timing_end(K_BWD_PRE, st);
   }
   if (a.total_ctas_q > 0) {
     timing_begin(K_BWD_DQ, st);

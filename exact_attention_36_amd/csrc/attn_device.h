@@ -161,6 +161,25 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Instruction-scheduling hints (sched_group_barrier masks): the compiler
+// otherwise issues each LDS operand read right before the MFMA that consumes
+// it and waits out the LDS latency on every MFMA.
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100, SG_VALU = 0x002;
+#define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+// `steps` MFMA steps of `m` MFMAs each consuming `r` LDS reads, with the reads
+// issued `ahead` steps before their MFMAs.
+template <int steps, int m, int r, int ahead>
+__device__ __forceinline__ void sched_reads_ahead() {
+  static_assert(ahead >= 1 && ahead <= steps, "prefetch distance");
+  SCHED_GROUP(SG_DS_READ, r * ahead);
+#pragma unroll
+  for (int i = 0; i < steps - ahead; i++) {
+    SCHED_GROUP(SG_MFMA, m);
+    SCHED_GROUP(SG_DS_READ, r);
+  }
+  SCHED_GROUP(SG_MFMA, m * ahead);
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -279,6 +279,10 @@ void fwd_kernel(const FwdArgs a) {
 #pragma unroll
         for (int n = 0; n < QB; n++) acc[n][d] = mfma32<F16>(vf, pf[n][t2], acc[n][d]);
       }
+    // S of the next tile: 1 K read feeds QB MFMAs per step, 4 steps ahead;
+    // PV: 2 transposing reads feed QB MFMAs per step, 4 steps ahead
+    if constexpr (!last) sched_reads_ahead<KB * KS, QB, 1, 4>();
+    sched_reads_ahead<DB * PT, QB, 2, 4>();
     if constexpr (!last) {
 #pragma unroll
       for (int n = 0; n < QB; n++)

@@ -68,7 +68,7 @@ constexpr int BWD_QBM = 128;    // packed query rows per dQ workgroup
 
 // Optional per-launch timing (attn_timing_enable): the launchers call these
 // around every kernel launch; they record HIP events only while enabled.
-enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_ZERO, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_COUNT };
+enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_ZERO, K_BWD_DQ, K_BWD_DKDV, K_COUNT };
 void timing_begin(int kid, hipStream_t st);
 void timing_end(int kid, hipStream_t st);
 

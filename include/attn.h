@@ -163,10 +163,9 @@ typedef enum {
     ATTN_KERNEL_FWD = 0,          /* fused forward */
     ATTN_KERNEL_FWD_COMBINE = 1,  /* split-KV merge */
     ATTN_KERNEL_BWD_ZERO = 2,     /* clears dsinks */
-    ATTN_KERNEL_BWD_PRE = 3,      /* D_i, lse with the sink, clears the dQ accumulator */
-    ATTN_KERNEL_BWD_DKDV = 4,     /* key-major backward main loop */
-    ATTN_KERNEL_BWD_DQ = 5,       /* dQ accumulator -> gradient dtype */
-    ATTN_KERNEL_COUNT = 6
+    ATTN_KERNEL_BWD_DQ = 3,       /* query-major backward: row statistics, dsinks, dQ */
+    ATTN_KERNEL_BWD_DKDV = 4,     /* key-major backward: dK, dV */
+    ATTN_KERNEL_COUNT = 5
 } attn_kernel_id;
 attn_status attn_timing_enable(int32_t on);
 attn_status attn_timing_read(int32_t kernel, int64_t *launches, double *total_ms);
