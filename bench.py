@@ -43,24 +43,58 @@ def visible_pairs(B, sq, sk, hq, causal, window):
     return int(keep.sum()) * B * hq
 
 
-def traffic_from_profile(kernel: str, source_files):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+KERNEL_SOURCES = {
+    "fwd": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
+    "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
+    "bwd_dq": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
+}
+COMMON_SOURCES = ["exact_attention_36_amd/csrc/attn_device.h", "exact_attention_36_amd/csrc/attn_common.h",
+                  "exact_attention_36_amd/csrc/attn_kernels.h", "exact_attention_36_amd/csrc/attn_api.cpp"]
 
-    The summary records a hash of the kernel sources it was measured with; if
-    they changed since, the counters no longer describe this kernel.
-    """
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % kernel)
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 over the source files a kernel is built from."""
     h = hashlib.sha256()
-    for p in source_files:
+    for p in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
-    if rec.get("source_sha256") != h.hexdigest():
+    return h.hexdigest()
+
+
+def traffic_from_profile(kernel: str):
+    """HBM bytes per launch of `kernel` from its committed counter summary, or None.
+
+    profiles/counters_<kernel>.txt holds `key: value` lines: the FETCH_SIZE and
+    WRITE_SIZE readings per dispatch, each scaled by the factor a plain copy
+    kernel of known size gave in the same run, and the hash of the kernel
+    sources they were measured with; if the sources changed since, the
+    counters no longer describe this kernel and the result is None.
+    """
+    path = os.path.join(ROOT, "profiles", "counters_%s.txt" % kernel)
+    if not os.path.exists(path):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return int(float(rec["hbm_bytes_per_launch"]))
+
+
+def copy_calibration():
+    """A plain elementwise copy of known size (read 256 MiB, write 256 MiB),
+    run before the steps so that a counter run sees it beside the kernels."""
+    import torch
+    n = 128 << 20  # bf16 elements
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(inp, w, seconds_target=15.0):
@@ -98,6 +132,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 256 MiB elementwise copy first (reference for HBM counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this "
@@ -115,6 +151,8 @@ def main():
     dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration()
 
     def step():
         o, lse = ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"])
@@ -153,17 +191,18 @@ def main():
     # pair, the key-major dK/dV kernel 4 (S, dP, dV, dK), the query-major dQ
     # kernel 3 (S, dP, dQ); the step's value keeps the 4:10 convention.
     flop_of = {"fwd": fwd_flop, "bwd_dkdv": 8.0 * D * pairs, "bwd_dq": 6.0 * D * pairs}
+    # compulsory HBM bytes per launch (each tensor read or written once)
+    qt, kvt, rows = B * S * HQ * D * 2, B * S * HKV * D * 2, B * HQ * S
+    algo_bytes = {"fwd": 2 * qt + 2 * kvt + 4 * rows,              # Q K V in, O out, lse out
+                  "bwd_dq": 4 * qt + 2 * kvt + 12 * rows,          # Q O dO K V in, dQ out; lse in, D lse' out
+                  "bwd_dkdv": 2 * qt + 4 * kvt + 8 * rows}         # Q dO K V in, dK dV out; D lse' in
     roof = None
     if dom in flop_of:
         ach = flop_of[dom] / (avg_ms * 1e-3) / 1e12
-        srcs = {"fwd": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
-                "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
-                "bwd_dq": ["exact_attention_36_amd/csrc/attn_bwd.hip"]}[dom]
-        srcs = srcs + ["exact_attention_36_amd/csrc/attn_device.h", "exact_attention_36_amd/csrc/attn_common.h",
-                       "exact_attention_36_amd/csrc/attn_kernels.h"]
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profile(dom, srcs), "avg_launch_ms": round(avg_ms, 5)}
+                "traffic": traffic_from_profile(dom), "traffic_unit": "bytes per launch",
+                "algorithmic_bytes": algo_bytes[dom], "avg_launch_ms": round(avg_ms, 5)}
 
     out = {
         "metric": "attention fwd+bwd TFLOPS (and % of MFMA bf16 peak), 1 MI355X",

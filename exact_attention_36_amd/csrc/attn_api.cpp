@@ -96,22 +96,11 @@ int choose_split(int64_t base_ctas, int64_t sk) {
   return (int)std::max<int64_t>(n, 1);
 }
 
-// Query rows per forward workgroup: 256 (two 32-row blocks per wave, half
-// the LDS traffic per MFMA) when every group has at least two such blocks and
-// they fill the chip; 128 otherwise (short or decode-shaped problems).
-int choose_bm(int64_t rows_per_group, int64_t groups) {
-  return (rows_per_group >= 512 && (rows_per_group / 256) * groups >= 256 && false) ? 256 : 128;
-}
-
 size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_split_out, int* bm_out) {
   const int G = p->heads_q / p->heads_kv;
-  int bm = choose_bm(sq * G, p->heads_kv * B);
-  int64_t nmb = cdiv(sq * G, bm);
+  const int bm = FWD_BM;
+  const int64_t nmb = cdiv(sq * G, bm);
   const int ns = choose_split(nmb * p->heads_kv * B, sk);
-  if (ns > 1 && bm != 128) {  // split-KV runs 128-row tiles
-    bm = 128;
-    nmb = cdiv(sq * G, bm);
-  }
   if (n_split_out) *n_split_out = ns;
   if (bm_out) *bm_out = bm;
   if (ns <= 1) return 0;
@@ -161,7 +150,7 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   const int G = a.s.group;
   a.n_split = 1;
   if (packed) {
-    a.bm = (total_q * G >= 512 * (int64_t)nseq && (total_q * G) / 256 * p->heads_kv >= 256) ? 256 : 128;
+    a.bm = FWD_BM;
     a.nblk = (int32_t)((total_q * G) / a.bm + nseq);
     const int64_t ctas = (int64_t)a.nblk * p->heads_kv;
     if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");

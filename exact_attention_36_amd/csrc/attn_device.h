@@ -208,7 +208,7 @@ struct GroupGrid {
   __host__ __device__ long long grid_size() const {
     return grouped() ? 8LL * gpx() * nranks : (long long)ngroups * nranks;
   }
-  __device__ bool decode(int bid, int& group, int& rank) const {
+  __device__ __forceinline__ bool decode(int bid, int& group, int& rank) const {
     if (!grouped()) {
       rank = bid / ngroups;
       group = bid - rank * ngroups;

@@ -10,20 +10,18 @@
 // one value-less logit per q head to each row's denominator, which scales
 // the output by sigmoid(lse - sink) (dew-flash-attn page, sinks paragraph).
 //
-// Work tile: 128*QB packed query rows (the G q heads of one kv head, query
-// major) x one kv head x one sequence, 4 waves of 32*QB rows each.  Each wave
-// computes S^T = K Q^T with v_mfma_f32_32x32x16 so that a lane owns query
-// rows: the row max needs one cross-half exchange and the row sum none until
-// the end, and the output O^T = V^T P^T keeps the same lane ownership, so
-// the rescale is lane-local.  P never leaves registers.  With QB = 2 every K
-// read and every transposing V read from LDS feeds two MFMAs (one per
-// 32-row query block), halving LDS traffic per MFMA -- the transposing read
-// (ds_read_b64_tr_b16) moves half the bytes per instruction of ds_read_b128,
-// so V dominates LDS time.  K/V tiles of 64 keys are streamed global -> LDS
-// directly (buffer_load ... lds) in an XOR-swizzled layout that the 16-byte K
-// reads and the transposing V reads both hit without bank conflicts; K runs
-// one tile ahead of V so that S of tile t+1 is computed on the MFMA pipe
-// while the softmax of tile t runs on the VALU.
+// Work tile: 128 packed query rows (the G q heads of one kv head, query
+// major) x one kv head x one sequence, 4 waves of 32 rows, two workgroups per
+// CU.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16 so that a lane
+// owns a query row: the row max needs one cross-half exchange and the row sum
+// none until the end, and the output O^T = V^T P^T keeps the same lane
+// ownership, so the rescale is lane-local.  P never leaves registers.  K/V
+// tiles of 64 keys are streamed global -> LDS directly (buffer_load ... lds)
+// in an XOR-swizzled layout that the 16-byte K reads and the transposing V
+// reads (ds_read_b64_tr_b16) both hit without bank conflicts; K runs one tile
+// ahead of V so that S of tile t+1 is computed on the MFMA pipe while the
+// softmax of tile t runs on the VALU.  O leaves through LDS so that the
+// stores write whole rows.
 //
 // Split-KV (decode shapes): the visible tiles of a work tile are divided
 // among n_split workgroups, each writing a normalised fp32 partial output
@@ -36,25 +34,24 @@
 
 namespace attn {
 
-template <int QB>
-struct FwdOcc;
-template <>
-struct FwdOcc<1> { static constexpr int waves = 2; };
-template <>
-struct FwdOcc<2> { static constexpr int waves = 1; };
-
-template <int D, bool F16, int QB>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(FwdOcc<QB>::waves, FwdOcc<QB>::waves)))
+template <int D, bool F16>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const FwdArgs a) {
-  constexpr int BM = 128 * QB;             // packed query rows per workgroup
+  // Two workgroups per CU, each with two K and two V buffers (64 KB of LDS
+  // for D = 128).  The waits and loads below are written for NST buffers.
+  constexpr int NW = THREADS / 64;         // waves per workgroup
+  constexpr int NST = 2;                   // K buffers = V buffers
+  constexpr int BM = 32 * NW;              // packed query rows per workgroup
+  static_assert(BM == FWD_BM, "work tile");
   constexpr int KS = D / 16;               // MFMA k-steps over the head dim
   constexpr int DB = D / 32;               // 32-wide blocks of the head dim
   constexpr int ROWB = D * 2;              // bytes per K/V row
   constexpr int TILE = FWD_BN * ROWB;      // bytes per K (or V) tile
-  constexpr int SLABS = TILE / 1024 / 4;   // 1 KB wave-loads per tile per wave
+  constexpr int SLABS = TILE / 1024 / NW;  // 1 KB wave-loads per tile per wave
   constexpr int KB = FWD_BN / 32;          // 32-key blocks per tile
   constexpr int PT = FWD_BN / 16;          // 16-key MFMA steps per tile
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
+  static_assert(SLABS >= 1 && (NST & (NST - 1)) == 0, "tile split");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TILE];  // K slots, then V slots
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -108,20 +105,20 @@ void fwd_kernel(const FwdArgs a) {
   const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2) : 0u;
   const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
 
-  // ---- this lane's query rows: block n of the wave holds rows p0 + 32 (QB wave + n) + l32
-  int my_p[QB], my_i[QB], my_hl[QB], my_kmin[QB], my_kmax[QB];
-  uint32_t qoff[QB];
-  u32x4 qf[QB][KS];  // Q^T as the B operand: 8 consecutive dims of the row per k-step
+  // ---- this lane's query row: p0 + 32 wave + l32
+  const int my_p = p0 + 32 * wave + l32;
+  const int my_i = div_group(my_p, a.s);
+  const int my_hl = my_p - my_i * G;
+  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * D) * 2);
+  u32x4 qf[KS];  // Q^T as the B operand: 8 consecutive dims of the row per k-step
 #pragma unroll
-  for (int n = 0; n < QB; n++) {
-    my_p[n] = p0 + 32 * (QB * wave + n) + l32;
-    my_i[n] = div_group(my_p[n], a.s);
-    my_hl[n] = my_p[n] - my_i[n] * G;
-    my_kmin[n] = band.kmin(my_i[n]);
-    my_kmax[n] = band.kmax(my_i[n]);
-    qoff[n] = (uint32_t)(((int64_t)my_i[n] * qrow + (int64_t)my_hl[n] * D) * 2);
-#pragma unroll
-    for (int s = 0; s < KS; s++) qf[n][s] = buf_load16(rq, qoff[n] + (uint32_t)((16 * s + 8 * hh) * 2));
+  for (int s = 0; s < KS; s++) qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+  // Visibility of key j0 + o for this lane's row, o = the key's offset in the
+  // tile minus 4 hh:  0 <= o - lo_base + j0 <= span  (unsigned compare).
+  int lo_base = band.kmin(my_i) - 4 * hh, span = band.kmax(my_i) - band.kmin(my_i);
+  if (span < 0) {  // no visible key: nothing passes
+    lo_base = -1 - 4 * hh;
+    span = 0;
   }
 
   // ---- loop-invariant addressing
@@ -150,149 +147,118 @@ void fwd_kernel(const FwdArgs a) {
     for (int w = 0; w < 2; w++) v_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
   }
 
-  // Buffers K0 K1 V0 V1; tile t uses K and V buffer (t - t_begin) & 1.
-  auto load_rows = [&](const void* src, int t, char* dst) {
+  // Tile t lives in K slot and V slot (t - t_begin) mod NST.
+  auto load_rows = [&](const void* src, int t, char* dst) __attribute__((always_inline)) {
     const int64_t skip = (int64_t)t * FWD_BN * krow;  // elements before tile t
     const i32x4 r = make_rsrc_words((const uint16_t*)src + kbase_e + skip, kbytes - (uint32_t)(skip * 2));
 #pragma unroll
     for (int n = 0; n < SLABS; n++) dma_lds16(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
   };
-  auto kbuf = [&](int t) { return smem + ((t - t_begin) & 1) * TILE; };
-  auto vbuf = [&](int t) { return smem + (2 + ((t - t_begin) & 1)) * TILE; };
+  auto kslot = [&](int t) { return smem + ((t - t_begin) & (NST - 1)) * TILE; };
+  auto vslot = [&](int t) { return smem + (NST + ((t - t_begin) & (NST - 1))) * TILE; };
 
-  f32x16 acc[QB][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int n = 0; n < QB; n++)
-#pragma unroll
-    for (int d = 0; d < DB; d++) acc[n][d] = f32x16{};
+  for (int d = 0; d < DB; d++) acc[d] = f32x16{};
   // m_run: the reference max (raw score units) the accumulators are scaled to.
   // It is raised only when a tile's max exceeds it by more than 8 in log2
   // units, so p = 2^(s*c - m_run*c) stays below 2^8 and most tiles skip the
   // rescale of the accumulators; O = acc / l is the same for any reference.
-  float m_run[QB], l_part[QB];
-#pragma unroll
-  for (int n = 0; n < QB; n++) {
-    m_run[n] = -INFINITY;
-    l_part[n] = 0.f;
-  }
+  float m_run = -INFINITY, l_part = 0.f;
   const float c = a.scale_log2;
   constexpr float RESCALE_LOG2 = 8.f;
 
   // S^T = K Q^T for one tile (raw scores; the scale is folded into the exponent)
-  auto s_tile = [&](const char* kt, f32x16 (&st)[QB][KB]) {
+  auto s_tile = [&](const char* kt, f32x16 (&st)[KB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-      for (int s = 0; s < KS; s++) {
-        const u32x4 kf = lds_read16(kt + kb * 32 * ROWB + k_off[s]);
-#pragma unroll
-        for (int n = 0; n < QB; n++) st[n][kb] = mfma32<F16>(kf, qf[n][s], s == 0 ? f32x16{} : st[n][kb]);
-      }
+      for (int s = 0; s < KS; s++)
+        st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], s == 0 ? f32x16{} : st[kb]);
   };
 
-  f32x16 st[QB][KB];
-  // One step: softmax and PV of tile t (scores in st), overlapped with S of tile t+1.
-  auto step = [&](int t, auto MASK, auto LAST) {
+  // One step: softmax and PV of tile t (scores in st), overlapped with S of
+  // tile t+1 (into sn).  At its top the step needs V(t) and K(t+1); the loads
+  // issued after them are those of the NST-2 steps before (2 tiles each).
+  auto step = [&](int t, f32x16 (&st)[KB], f32x16 (&sn)[KB], auto MASK, auto LAST) __attribute__((always_inline)) {
     constexpr bool masked = decltype(MASK)::value;
     constexpr bool last = decltype(LAST)::value;
-    wait_vmcnt<0>();               // V(t) and K(t+1) are in LDS (this lane's part)
-    __builtin_amdgcn_s_barrier();  // everyone's part; everyone is done with step t-1
+    if (t + NST - 1 < t_end) wait_vmcnt<2 * (NST - 2) * SLABS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // everyone's part is in; everyone is done with step t-1
     if (!last) {
-      if (t + 2 < t_end) load_rows(a.k, t + 2, kbuf(t));  // K(t) was consumed in step t-1
-      load_rows(a.v, t + 1, vbuf(t + 1));                  // V(t-1) was consumed in step t-1
+      if (t + NST < t_end) load_rows(a.k, t + NST, kslot(t + NST));    // slot of K(t), used in step t-1
+      if (t + NST - 1 < t_end) load_rows(a.v, t + NST - 1, vslot(t + NST - 1));  // slot of V(t-1)
     }
     if constexpr (masked) {
-      const int j0 = t * FWD_BN;
-#pragma unroll
-      for (int n = 0; n < QB; n++)
-#pragma unroll
-        for (int kb = 0; kb < KB; kb++)
-#pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (j < my_kmin[n] || j > my_kmax[n]) st[n][kb][i] = -INFINITY;
-          }
-    }
-    bool any_raise = false;
-    float mx[QB];
-    bool raise[QB];
-#pragma unroll
-    for (int n = 0; n < QB; n++) {
-      mx[n] = -INFINITY;
+      const int lo = lo_base - t * FWD_BN;
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) mx[n] = fmaxf(mx[n], st[n][kb][i]);
-      mx[n] = half_max(mx[n]);
-      raise[n] = mx[n] * c > m_run[n] * c + RESCALE_LOG2;  // false while both are -inf
-      any_raise |= raise[n];
+        for (int i = 0; i < 16; i++) {
+          const int o = kb * 32 + 8 * (i >> 2) + (i & 3);
+          if ((unsigned)(o - lo) > (unsigned)span) st[kb][i] = -INFINITY;
+        }
     }
-    if (__builtin_amdgcn_ballot_w64(any_raise)) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int n = 0; n < QB; n++) {
-        // lanes that do not raise keep their reference (alpha = 1; their m_run
-        // may still be -inf); a first finite max gives alpha = 2^-inf = 0
-        const float alpha = raise[n] ? exp2_fast((m_run[n] - mx[n]) * c) : 1.f;
-        m_run[n] = raise[n] ? mx[n] : m_run[n];
-        l_part[n] *= alpha;
+    for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-        for (int d = 0; d < DB; d++) acc[n][d] *= alpha;
-      }
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, st[kb][i]);
+    mx = half_max(mx);
+    const bool raise = mx * c > m_run * c + RESCALE_LOG2;  // false while both are -inf
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      // lanes that do not raise keep their reference (alpha = 1; their m_run
+      // may still be -inf); a first finite max gives alpha = 2^-inf = 0
+      const float alpha = raise ? exp2_fast((m_run - mx) * c) : 1.f;
+      m_run = raise ? mx : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; d++) acc[d] *= alpha;
     }
-    f32x16 sn[QB][KB];
-    if constexpr (!last) s_tile(kbuf(t + 1), sn);
-    u32x4 pf[QB][PT];
-#pragma unroll
-    for (int n = 0; n < QB; n++) {
-      const float mc = m_run[n] == -INFINITY ? 0.f : m_run[n] * c;
+    if constexpr (!last) s_tile(kslot(t + 1), sn);
+    u32x4 pf[PT];
+    {
+      const float mc = m_run == -INFINITY ? 0.f : m_run * c;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-          const float p = exp2_fast(fmaf(st[n][kb][i], c, -mc));
-          st[n][kb][i] = p;
+          const float p = exp2_fast(fmaf(st[kb][i], c, -mc));
+          st[kb][i] = p;
           rs += p;
         }
-      l_part[n] += rs;
+      l_part += rs;
       // P^T as the B operand: k-step t2 = 2 kb + u covers keys
       // 32 kb + 16 u + {4hh..4hh+3, 8+4hh..8+4hh+3}: accumulator registers
       // 8u..8u+7 of this lane.
 #pragma unroll
       for (int t2 = 0; t2 < PT; t2++) {
         const int kb = t2 >> 1, u = t2 & 1;
-        pf[n][t2] = u32x4{pack2<F16>(st[n][kb][8 * u + 0], st[n][kb][8 * u + 1]),
-                          pack2<F16>(st[n][kb][8 * u + 2], st[n][kb][8 * u + 3]),
-                          pack2<F16>(st[n][kb][8 * u + 4], st[n][kb][8 * u + 5]),
-                          pack2<F16>(st[n][kb][8 * u + 6], st[n][kb][8 * u + 7])};
+        pf[t2] = u32x4{pack2<F16>(st[kb][8 * u + 0], st[kb][8 * u + 1]), pack2<F16>(st[kb][8 * u + 2], st[kb][8 * u + 3]),
+                       pack2<F16>(st[kb][8 * u + 4], st[kb][8 * u + 5]), pack2<F16>(st[kb][8 * u + 6], st[kb][8 * u + 7])};
       }
     }
     // O^T += V^T P^T, V^T read with the same key order as P.
-    const char* vt = vbuf(t);
+    const char* vt = vslot(t);
 #pragma unroll
     for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int t2 = 0; t2 < PT; t2++) {
         const u32x2 a1 = lds_read_tr(vt + t2 * 16 * ROWB + v_off[d][0]);
         const u32x2 a2 = lds_read_tr(vt + t2 * 16 * ROWB + v_off[d][1]);
-        const u32x4 vf{a1[0], a1[1], a2[0], a2[1]};
-#pragma unroll
-        for (int n = 0; n < QB; n++) acc[n][d] = mfma32<F16>(vf, pf[n][t2], acc[n][d]);
+        acc[d] = mfma32<F16>(u32x4{a1[0], a1[1], a2[0], a2[1]}, pf[t2], acc[d]);
       }
-    // S of the next tile: 1 K read feeds QB MFMAs per step, 4 steps ahead;
-    // PV: 2 transposing reads feed QB MFMAs per step, 4 steps ahead
-    if constexpr (!last) sched_reads_ahead<KB * KS, QB, 1, 4>();
-    sched_reads_ahead<DB * PT, QB, 2, 4>();
-    if constexpr (!last) {
-#pragma unroll
-      for (int n = 0; n < QB; n++)
-#pragma unroll
-        for (int kb = 0; kb < KB; kb++) st[n][kb] = sn[n][kb];
-    }
+    // S of the next tile: 1 K read per MFMA, 4 MFMAs ahead; PV: 2 transposing
+    // reads per MFMA, 4 MFMAs ahead
+    if constexpr (!last) sched_reads_ahead<KB * KS, 1, 1, 4>();
+    sched_reads_ahead<DB * PT, 1, 2, 4>();
   };
 
-  // Masked head, unmasked interior and masked tail loops (one body each);
-  // the last tile is peeled off (no next tile to start).
+  // Masked head, unmasked interior and masked tail loops; each runs two steps
+  // per iteration so that the current and next score tiles swap registers
+  // instead of being copied.  The last tile is peeled off (no next tile).
   int ti0 = t_begin, ti1 = t_begin;  // interior tiles [ti0, ti1)
   if (full_hi >= full_lo) {
     ti0 = max(t_begin, (full_lo + FWD_BN - 1) / FWD_BN);
@@ -300,58 +266,86 @@ void fwd_kernel(const FwdArgs a) {
     if (ti1 <= ti0) ti0 = ti1 = t_begin;
   }
   if (t_begin < t_end) {
-    load_rows(a.k, t_begin, kbuf(t_begin));
-    load_rows(a.v, t_begin, vbuf(t_begin));
-    if (t_begin + 1 < t_end) load_rows(a.k, t_begin + 1, kbuf(t_begin + 1));
-    wait_vmcnt<0>();
+    // prologue: K(b), V(b), K(b+1), V(b+1), ..., K(b+NST-1), then S(b)
+#pragma unroll
+    for (int j = 0; j < NST; j++) {
+      if (t_begin + j < t_end) load_rows(a.k, t_begin + j, kslot(t_begin + j));
+      if (j < NST - 1 && t_begin + j < t_end) load_rows(a.v, t_begin + j, vslot(t_begin + j));
+    }
+    if (t_begin + NST - 1 < t_end) wait_vmcnt<(2 * NST - 2) * SLABS>();
+    else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    s_tile(kbuf(t_begin), st);
+    f32x16 sa[KB], sb[KB];
+    s_tile(kslot(t_begin), sa);
     const int tl = t_end - 1;
-    for (int t = t_begin; t < min(ti0, tl); t++) step(t, std::true_type{}, std::false_type{});
-    for (int t = max(ti0, t_begin); t < min(ti1, tl); t++) step(t, std::false_type{}, std::false_type{});
-    for (int t = max(ti1, t_begin); t < tl; t++) step(t, std::true_type{}, std::false_type{});
-    step(tl, std::true_type{}, std::true_type{});
+    auto run = [&](int t0, int t1, auto MASK) __attribute__((always_inline)) {
+      int t = t0;
+      for (; t + 1 < t1; t += 2) {
+        step(t, sa, sb, MASK, std::false_type{});
+        step(t + 1, sb, sa, MASK, std::false_type{});
+      }
+      if (t < t1) {
+        step(t, sa, sb, MASK, std::false_type{});
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++) sa[kb] = sb[kb];
+      }
+    };
+    run(t_begin, min(ti0, tl), std::true_type{});
+    run(max(ti0, t_begin), min(ti1, tl), std::false_type{});
+    run(max(ti1, t_begin), tl, std::true_type{});
+    step(tl, sa, sb, std::true_type{}, std::true_type{});
   }
 
-  // ---- epilogue, per query block of the wave
-  const auto ro = make_rsrc((uint16_t*)a.o + qbase_e, qbytes);
-#pragma unroll
-  for (int n = 0; n < QB; n++) {
-    const float l_tot = half_sum(l_part[n]);
-    const float lse_v = l_tot > 0.f ? (m_run[n] * c + log2_fast(l_tot)) * LN2 : -INFINITY;
-    if (a.n_split > 1) {
-      const int64_t pidx = ((int64_t)(sp * a.s.nseq + seq) * a.s.hkv + g) * ((int64_t)a.nmb * BM) + my_p[n];
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* op = a.o_part + pidx * D;
-#pragma unroll
-      for (int d = 0; d < DB; d++)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; j4++) {
-          const int dd = d * 32 + 8 * j4 + 4 * hh;
-          *(f32x4*)(op + dd) = f32x4{acc[n][d][4 * j4] * inv, acc[n][d][4 * j4 + 1] * inv,
-                                     acc[n][d][4 * j4 + 2] * inv, acc[n][d][4 * j4 + 3] * inv};
-        }
-      if (hh == 0) a.lse_part[pidx] = lse_v;
-      continue;
-    }
-    const int my_h = g * G + my_hl[n];
-    float denom = l_tot;
-    if (a.sinks && l_tot > 0.f) denom += exp2_fast(fmaf(a.sinks[my_h], LOG2E, -m_run[n] * c));
-    const float inv = l_tot > 0.f ? 1.f / denom : 0.f;
+  // ---- epilogue
+  const float l_tot = half_sum(l_part);
+  const float lse_v = l_tot > 0.f ? (m_run * c + log2_fast(l_tot)) * LN2 : -INFINITY;
+  if (a.n_split > 1) {
+    const int64_t pidx = ((int64_t)(sp * a.s.nseq + seq) * a.s.hkv + g) * ((int64_t)a.nmb * BM) + my_p;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* op = a.o_part + pidx * D;
 #pragma unroll
     for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int dd = d * 32 + 8 * j4 + 4 * hh;
-        const u32x2 w{pack2<F16>(acc[n][d][4 * j4] * inv, acc[n][d][4 * j4 + 1] * inv),
-                      pack2<F16>(acc[n][d][4 * j4 + 2] * inv, acc[n][d][4 * j4 + 3] * inv)};
-        buf_store8(w, ro, qoff[n] + (uint32_t)(dd * 2));
+        *(f32x4*)(op + dd) = f32x4{acc[d][4 * j4] * inv, acc[d][4 * j4 + 1] * inv, acc[d][4 * j4 + 2] * inv,
+                                   acc[d][4 * j4 + 3] * inv};
       }
-    if (hh == 0 && my_p[n] < prows) {
-      const int64_t li_ = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i[n]
-                                   : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i[n];
-      a.lse[li_] = lse_v;
-    }
+    if (hh == 0) a.lse_part[pidx] = lse_v;
+    return;
+  }
+  const int my_h = g * G + my_hl;
+  float denom = l_tot;
+  if (a.sinks && l_tot > 0.f) denom += exp2_fast(fmaf(a.sinks[my_h], LOG2E, -m_run * c));
+  const float inv = l_tot > 0.f ? 1.f / denom : 0.f;
+  if (hh == 0 && my_p < prows) {
+    const int64_t li_ = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
+                                 : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
+    a.lse[li_] = lse_v;
+  }
+  // O goes out through LDS so that every store writes whole rows: the wave
+  // puts its 32 rows (swizzled like the K/V tiles) in its own 32-row region,
+  // then each store instruction writes 1 KB of consecutive 16-byte chunks.
+  __builtin_amdgcn_s_barrier();  // all waves are done reading the K/V slots
+  char* const ost = smem + wave * 32 * ROWB;
+#pragma unroll
+  for (int d = 0; d < DB; d++)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; j4++)
+      *LDS_PTR(u32x2, ost + tile_off<D>(l32, 4 * d + j4) + 8 * hh) =
+          u32x2{pack2<F16>(acc[d][4 * j4] * inv, acc[d][4 * j4 + 1] * inv),
+                pack2<F16>(acc[d][4 * j4 + 2] * inv, acc[d][4 * j4 + 3] * inv)};
+  const auto ro = make_rsrc((uint16_t*)a.o + qbase_e, qbytes);
+  constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+#pragma unroll
+  for (int it = 0; it < 32 / (64 / CPR); it++) {
+    const int r = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+    const u32x4 v = *LDS_PTR(const u32x4, ost + tile_off<D>(r, ch));
+    const int p = p0 + 32 * wave + r;
+    const int i = div_group(p, a.s), hl = p - i * G;
+    // rows past the work tile fall outside the descriptor (dropped)
+    const uint32_t off = p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + ch * 8) * 2) : 0xFFFFFFF0u;
+    buf_store16(v, ro, off);
   }
 }
 
@@ -400,8 +394,7 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
 template <int D, bool F16>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   timing_begin(K_FWD, st);
-  if (a.bm == 256) hipLaunchKernelGGL((fwd_kernel<D, F16, 2>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-  else hipLaunchKernelGGL((fwd_kernel<D, F16, 1>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
   timing_end(K_FWD, st);
   return hipGetLastError();
 }

@@ -36,7 +36,7 @@ struct FwdArgs {
   float* o_part;          // split-KV partial outputs (fp32) or nullptr
   float* lse_part;        // split-KV partial log-sum-exps
   float scale_log2;       // softmax scale * log2(e)
-  int32_t bm;             // packed query rows per workgroup: 128 or 256
+  int32_t bm;             // packed query rows per workgroup (FWD_BM)
   int32_t nmb;            // m-blocks per (sequence, kv head) in batched mode
   int32_t nblk;           // linear blocks per kv head in packed mode
   int32_t n_split;
