@@ -108,9 +108,11 @@ size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_sp
   return align_up(rows * p->head_dim * 4) + align_up(rows * 4);
 }
 
-// Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like lse.
+// Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like
+// lse, and for bf16 inputs an fp16 copy of Q (layout of Q) that the dQ kernel
+// writes and the dK/dV kernel reads.
 struct BwdWs {
-  size_t delta, lse2, total;
+  size_t delta, lse2, q16, total;
 };
 BwdWs bwd_ws(const attn_params* p, int64_t tq, int32_t grad_dtype) {
   (void)grad_dtype;
@@ -118,7 +120,8 @@ BwdWs bwd_ws(const attn_params* p, int64_t tq, int32_t grad_dtype) {
   const int64_t rows = tq * p->heads_q;
   w.delta = align_up(rows * 4);
   w.lse2 = align_up(rows * 4);
-  w.total = w.delta + w.lse2;
+  w.q16 = p->dtype == ATTN_BF16 ? align_up(rows * p->head_dim * 2) : 0;
+  w.total = w.delta + w.lse2 + w.q16;
   return w;
 }
 
@@ -207,6 +210,8 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   a.delta = (float*)wp;
   wp += w.delta;
   a.lse2 = (float*)wp;
+  wp += w.lse2;
+  a.q16 = w.q16 ? (uint16_t*)wp : nullptr;
   const float scale = resolve_scale(p);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -115,6 +115,13 @@ void bwd_dq_kernel(const BwdArgs a) {
     qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
     df[s] = buf_load16(rdo, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
   }
+  // The fp16 copy of Q that the dK/dV kernel stages (bf16 inputs): every
+  // (query, q head) row is in exactly one of these work tiles.
+  if (a.q16) {
+    const auto rq16 = make_rsrc(a.q16 + qbase_e, qbytes);
+#pragma unroll
+    for (int s = 0; s < KS; s++) buf_store16(bf16x8_to_f16x8(qf[s]), rq16, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+  }
   // Row statistics, computed here once per (query row, q head) and left in
   // the workspace for the dK/dV kernel that runs after this one:
   //   D = rowsum(dO * O), O being the stored (sink-gated) output;
@@ -308,9 +315,10 @@ void bwd_dq_kernel(const BwdArgs a) {
 // block of 32 packed query rows: S = Q K^T and dP = dO V^T (lane = key
 // column, registers = query rows), P and dS with the rows' lse' and D from
 // LDS, dV^T += dO^T P and dK^T += Q^T dS (dO, Q through transposing LDS
-// reads).  dS is kept in fp16 (10 fraction bits) for dK; the Q tile is
-// therefore staged in LDS as fp16 (converted on the way in, exact for
-// inputs inside fp16's range) and K, used for S, is converted likewise.
+// reads).  dS is kept in fp16 (10 fraction bits) for dK; the Q tiles are
+// therefore fp16 (for bf16 inputs, the copy the dQ kernel wrote; exact for
+// inputs inside fp16's range) and K, used for S, is converted likewise.  Q,
+// dO and the row statistics reach LDS by DMA, double buffered.
 template <int D, bool F16>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const BwdArgs a) {
@@ -318,7 +326,6 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int BN = BWD_BN, BM = BWD_BM;
   constexpr int VBLK = BN * ROWB;           // V block in LDS (B operand of dP)
   constexpr int QTILE = BM * ROWB;          // one Q (or dO) tile
-  constexpr int QCH = QTILE / 16 / THREADS; // 16-byte Q chunks per thread per tile
   __shared__ __attribute__((aligned(1024))) char smem[VBLK + 4 * QTILE + 2 * 256];
   char* const v_lds = smem;
   char* const q_lds = smem + VBLK;              // [buf] fp16 Q tile
@@ -364,7 +371,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 2) : 0u;
   const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
   const uint32_t kbytes = (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2);
-  const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
+  const i32x4 rq16 = make_rsrc_words((F16 ? (const uint16_t*)a.q : (const uint16_t*)a.q16) + qbase_e, qbytes);
   const i32x4 rdo = make_rsrc_words((const uint16_t*)a.dout + qbase_e, qbytes);
   const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
   const int64_t st_base = a.s.cu_q ? si.q0 : (int64_t)seq * a.s.hq * a.s.sq;
@@ -397,27 +404,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
 
-  // Q tile staging: thread t handles 16-byte chunks t, t+256, ... of the tile
-  auto q_fetch = [&](int pb, u32x4 (&stage)[QCH]) {
-#pragma unroll
-    for (int n = 0; n < QCH; n++) {
-      const int ch = threadIdx.x + n * THREADS;
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      const int p = pb * BM + r;
-      const int i = div_group(p, a.s), hl = p - i * G;
-      stage[n] = buf_load16(rq, (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + cc * 8) * 2));
-    }
-  };
-  auto q_store = [&](int buf, const u32x4 (&stage)[QCH]) {
-#pragma unroll
-    for (int n = 0; n < QCH; n++) {
-      const int ch = threadIdx.x + n * THREADS;
-      const int r = ch / (D / 8), cc = ch % (D / 8);
-      *LDS_PTR(u32x4, q_lds + buf * QTILE + tile_off<D>(r, cc)) = F16 ? stage[n] : bf16x8_to_f16x8(stage[n]);
-    }
-  };
-  auto do_fetch = [&](int pb, int buf) {
-    char* dd = do_lds + buf * QTILE;
+  // Q (fp16) and dO tiles of one block of BM packed rows -> LDS by DMA, and
+  // the rows' lse' and D; rows past the sequence read as 0 (and are masked).
+  auto tile_dma = [&](const i32x4& rs, char* dst, int pb) __attribute__((always_inline)) {
     constexpr int SL = QTILE / 1024 / 4;  // 1 KB slabs per wave
 #pragma unroll
     for (int n = 0; n < SL; n++) {
@@ -426,8 +415,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
       const int p = pb * BM + r;
       const int i = div_group(p, a.s), hl = p - i * G;
-      dma_lds16(rdo, dd + slab * 1024, (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + (pos ^ swz<D>(r)) * 8) * 2));
+      dma_lds16(rs, dst + slab * 1024, (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + (pos ^ swz<D>(r)) * 8) * 2));
     }
+  };
+  auto do_fetch = [&](int pb, int buf) __attribute__((always_inline)) {
+    tile_dma(rq16, q_lds + buf * QTILE, pb);
+    tile_dma(rdo, do_lds + buf * QTILE, pb);
     if (wave == 0) {
       const int p = pb * BM + l32;
       const int i = div_group(p, a.s), hl = p - i * G;
@@ -467,22 +460,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const float c = a.scale_log2;
   const char* vrow = v_lds + wave * 32 * ROWB;  // this wave's 32 V rows
 
-  if (pb_begin < pb_end) {
-    u32x4 stage[QCH];
-    q_fetch(pb_begin, stage);
-    do_fetch(pb_begin, 0);
-    q_store(0, stage);
-  }
+  if (pb_begin < pb_end) do_fetch(pb_begin, 0);
   for (int pb = pb_begin; pb < pb_end; pb++) {
     const int buf = (pb - pb_begin) & 1;
-    wait_vmcnt<0>();               // dO tile, row statistics (and V block) are in LDS
+    wait_vmcnt<0>();               // Q, dO tiles, row statistics (and V block) are in LDS
     __builtin_amdgcn_s_barrier();  // everyone's writes visible; everyone is done with step pb-1
-    u32x4 stage[QCH];
-    const bool more = pb + 1 < pb_end;
-    if (more) {
-      q_fetch(pb + 1, stage);
-      do_fetch(pb + 1, buf ^ 1);
-    }
+    if (pb + 1 < pb_end) do_fetch(pb + 1, buf ^ 1);  // buffers of step pb-1, which everyone has left
     const char* qt = q_lds + buf * QTILE;
     const char* dot = do_lds + buf * QTILE;
     const float* stt = st_lds + buf * 64;
@@ -541,8 +524,6 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     // dV/dK: 4 transposing reads feed 2 MFMAs per step, 2 steps ahead
     sched_reads_ahead<KS, 2, 3, 2>();
     sched_reads_ahead<2 * DB, 2, 4, 2>();
-    // the next Q tile goes into the other buffer (last read in step pb-1)
-    if (more) q_store(buf ^ 1, stage);
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV; lane = key, registers = dims
