@@ -5,8 +5,10 @@ N(0,1) inputs resident in HBM), through the C ABI.
 Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s
 (14 * D * visible (query, key) pairs per step: 4*D forward, 10*D backward).
 `roofline` reports the kernel with the most time in the timed region, timed
-with HIP events on its own stream; `cpu_baseline` times the fp64 CPU oracle
-on a bounded sample of the same workload.
+with HIP events on its own stream; `decode` measures the decode-shaped
+forward (B=32, s_q=16, s_kv=32768, Hq=64, Hkv=8) as K/V HBM GB/s;
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
+prefill workload.  `--workload decode` runs only the decode shape.
 """
 from __future__ import annotations
 
@@ -45,6 +47,7 @@ def visible_pairs(B, sq, sk, hq, causal, window):
 
 KERNEL_SOURCES = {
     "fwd": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
+    "fwd_decode": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
     "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
     "bwd_dq": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
 }
@@ -97,6 +100,45 @@ def copy_calibration():
     del src, dst
 
 
+DECODE = dict(name="decode / chunked-prefill fwd B32 s_q16 s_kv32768 Hq64 Hkv8 D128 bf16 causal", B=32, SQ=16,
+              SK=32768, HQ=64, HKV=8, D=128)
+
+
+def run_decode(steps, warmup):
+    """The decode-shaped forward (split-KV): time per call (split kernel +
+    combine, HIP events on the library's stream) and the K/V bytes it must
+    stream from HBM, as GB/s and a fraction of the 8 TB/s peak."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    d = DECODE
+    q, k, v = synth.device_normal(5, [(d["B"], d["SQ"], d["HQ"], d["D"]), (d["B"], d["SK"], d["HKV"], d["D"]),
+                                      (d["B"], d["SK"], d["HKV"], d["D"])])
+    o, lse = ea.attn_fwd(q, k, v, causal=True)
+    for _ in range(warmup):
+        ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ea.attn_timing_enable(True)
+    for _ in range(steps):
+        ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    n_s, ms_s = ea.attn_timing_read("fwd")
+    n_c, ms_c = ea.attn_timing_read("fwd_combine")
+    ea.attn_timing_enable(False)
+    per_call_ms = (ms_s + ms_c) / steps
+    kv_bytes = 2 * d["B"] * d["SK"] * d["HKV"] * d["D"] * 2
+    gbps = kv_bytes / (per_call_ms * 1e-3) / 1e9
+    pairs = visible_pairs(d["B"], d["SQ"], d["SK"], d["HQ"], True, (-1, -1))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": d["name"], "ms_per_call": round(per_call_ms, 4),
+            "split_kernel_ms": round(ms_s / max(n_s, 1), 4), "combine_ms": round(ms_c / max(n_c, 1), 4),
+            "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1), "hbm_peak_GBps": HBM_PEAK_GBS,
+            "frac": round(gbps / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile("fwd_decode"), "traffic_unit": "bytes per split-kernel launch",
+            "tflops": round(4.0 * d["D"] * pairs / (per_call_ms * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(inp, w, seconds_target=15.0):
     """Time the fp64 oracle on whole (batch, head) slices of the workload."""
     import numpy as np
@@ -132,6 +174,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
+    ap.add_argument("--workload", choices=("step", "decode"), default="step",
+                    help="step: the fwd+bwd line (default, also measures the decode shape); "
+                         "decode: only the decode-shaped forward (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB elementwise copy first (reference for HBM counter runs)")
     args = ap.parse_args()
@@ -144,6 +190,17 @@ def main():
     import torch
     import exact_attention_36_amd as ea
     from exact_attention_36_amd import synth
+
+    if args.workload == "decode":
+        if args.copy_calibration:
+            copy_calibration()
+        dec = run_decode(args.steps, args.warmup)
+        print(json.dumps({"metric": "decode-shaped forward, K/V HBM GB/s, 1 MI355X", "value": dec["kv_GBps"],
+                          "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": dec["ms_per_call"], "higher_is_better": True, "scaling": "weak",
+                          "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) rounded to bf16",
+                          "config": {"workload": dec["workload"]}, "decode": dec}))
+        return
 
     w = WORKLOAD
     B, S, HQ, HKV, D = w["B"], w["S"], w["HQ"], w["HKV"], w["D"]
@@ -194,7 +251,7 @@ def main():
     # compulsory HBM bytes per launch (each tensor read or written once)
     qt, kvt, rows = B * S * HQ * D * 2, B * S * HKV * D * 2, B * HQ * S
     algo_bytes = {"fwd": 2 * qt + 2 * kvt + 4 * rows,              # Q K V in, O out, lse out
-                  "bwd_dq": 4 * qt + 2 * kvt + 12 * rows,          # Q O dO K V in, dQ out; lse in, D lse' out
+                  "bwd_dq": 5 * qt + 2 * kvt + 12 * rows,          # Q O dO K V in, dQ and fp16 Q out; lse in, D lse' out
                   "bwd_dkdv": 2 * qt + 4 * kvt + 8 * rows}         # Q dO K V in, dK dV out; D lse' in
     roof = None
     if dom in flop_of:
@@ -225,6 +282,8 @@ def main():
         "roofline": roof,
         "wall_s": round(wall, 3),
     }
+    if not args.no_decode:
+        out["decode"] = run_decode(max(3, args.steps // 4), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out))
