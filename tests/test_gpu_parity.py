@@ -27,6 +27,14 @@ BATCHED = [
     ("two_sided_fp16", 1, 257, 190, 2, 2, 64, False, (20, 13), False, "fp16", True),
     ("sinks_fp16_full", 1, 100, 100, 2, 1, 128, False, (-1, -1), True, "fp16", True),
     ("split_kv_decode", 2, 3, 5000, 8, 2, 128, True, (-1, -1), True, "bf16", True),
+    # 16 q heads per kv head (8 queries fill a 128-row tile), left window only, no causal
+    ("mqa_g16_left_window", 1, 96, 200, 16, 1, 64, False, (50, -1), True, "bf16", True),
+    # right window only, no causal: keys up to 7 past the diagonal
+    ("right_window_only", 2, 65, 65, 2, 2, 128, False, (-1, 7), False, "bf16", True),
+    # one query, one key per sequence
+    ("single_token", 3, 1, 1, 2, 1, 128, True, (-1, -1), True, "bf16", True),
+    # 32 q heads on one kv head, 4 queries over 3000 keys (split-KV with a full 128-row tile)
+    ("g32_decode_split", 1, 4, 3000, 32, 1, 128, True, (-1, -1), False, "bf16", True),
 ]
 
 
@@ -58,6 +66,11 @@ def test_batched_matches_oracle(case):
                                      grad_dtype=gd)
         torch.cuda.synchronize()
         od = "f32" if gd == torch.float32 else dt
+        if gd != torch.float32:  # dQ, dK, dV accumulate without atomics: bitwise repeatable
+            dq2, dk2, dv2, _ = ea.attn_bwd(q, k, v, o, lse, do, causal=causal, window=window, sinks=s_dev,
+                                           grad_dtype=gd)
+            torch.cuda.synchronize()
+            assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), "backward not repeatable"
         assert_close(name + ".dq", host(dq).reshape(B * sq, hq, d), ref["dq"], od)
         assert_close(name + ".dk", host(dk).reshape(B * sk, hkv, d), ref["dk"], od)
         assert_close(name + ".dv", host(dv).reshape(B * sk, hkv, d), ref["dv"], od)
@@ -80,6 +93,10 @@ VARLEN = [
     ("varlen_gqa_sinks", [0, 17, 283, 128, 1, 0, 77], None, 4, 2, 128, True, (-1, -1), True, "bf16"),
     ("varlen_mixed_pack", [5, 0, 130, 64, 9], [200, 3, 130, 0, 9], 2, 2, 64, True, (50, 0), False, "bf16"),
     ("varlen_noncausal_fp16", [33, 190, 1], [64, 190, 300], 6, 2, 128, False, (-1, -1), False, "fp16"),
+    # every sequence empty but one, which is shorter than one tile, with a window
+    ("varlen_one_live", [0, 0, 45, 0], [0, 0, 45, 0], 8, 4, 128, True, (10, 0), True, "bf16"),
+    # queries and keys of different lengths per sequence, bottom-right aligned, GQA 8
+    ("varlen_q_shorter_g8", [7, 64, 3], [300, 64, 129], 8, 1, 64, True, (-1, -1), False, "bf16"),
 ]
 
 
