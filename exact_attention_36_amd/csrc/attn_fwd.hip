@@ -20,8 +20,9 @@
 // in an XOR-swizzled layout that the 16-byte K reads and the transposing V
 // reads (ds_read_b64_tr_b16) both hit without bank conflicts; K runs one tile
 // ahead of V so that S of tile t+1 is computed on the MFMA pipe while the
-// softmax of tile t runs on the VALU.  O leaves through LDS so that the
-// stores write whole rows.
+// softmax of tile t runs on the VALU.  Each wave computes only the tiles its
+// 32 rows can see (on the others it just takes part in the loads and
+// barriers).  O leaves through LDS so that the stores write whole rows.
 //
 // Split-KV (decode shapes): the visible tiles of a work tile are divided
 // among n_split workgroups, each writing a normalised fp32 partial output
@@ -53,7 +54,8 @@ void fwd_kernel(const FwdArgs a) {
   static_assert(SLABS >= 1 && (NST & (NST - 1)) == 0, "tile split");
   __shared__ __attribute__((aligned(1024))) char smem[2 * NST * TILE];  // K slots, then V slots
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.s.group;
   // ---- which work tile
@@ -96,6 +98,19 @@ void fwd_kernel(const FwdArgs a) {
   }
   // Tiles inside [full_lo, full_hi] are visible to every row of the work tile.
   const int full_lo = band.kmin(i_hi), full_hi = band.kmax(i_lo);
+  // Tiles this wave's 32 rows can see at all: [w_begin, w_end).  Outside it
+  // the wave only takes part in the loads and barriers of the workgroup.
+  int w_begin = t_end, w_end = t_end;
+  {
+    const int wp0 = p0 + 32 * wave, wp1 = min(wp0 + 32, prows) - 1;
+    if (wp0 < prows) {
+      const int klo = band.kmin(div_group(wp0, a.s)), khi = band.kmax(div_group(wp1, a.s));
+      if (khi >= klo) {
+        w_begin = min(t_end, max(t_begin, klo / FWD_BN));
+        w_end = max(w_begin, min(t_end, khi / FWD_BN + 1));
+      }
+    }
+  }
 
   const int64_t qrow = (int64_t)a.s.hq * D;   // elements per q/o token
   const int64_t krow = (int64_t)a.s.hkv * D;  // elements per k/v token
@@ -177,6 +192,25 @@ void fwd_kernel(const FwdArgs a) {
         st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], s == 0 ? f32x16{} : st[kb]);
   };
 
+  // Loads issued at the top of step t (after its barrier): K(t+NST) into the
+  // slot of K(t), which step t-1 used, and V(t+NST-1) into the slot of V(t-1).
+  auto refill = [&](int t) __attribute__((always_inline)) {
+    if (t + NST < t_end) load_rows(a.k, t + NST, kslot(t + NST));
+    if (t + NST - 1 < t_end) load_rows(a.v, t + NST - 1, vslot(t + NST - 1));
+  };
+  // A step of a tile this wave does not compute: its share of the loads and
+  // the barrier, and with NEXT the scores of tile t+1.
+  auto idle_step = [&](int t, f32x16 (&sn)[KB], auto NEXT) __attribute__((always_inline)) {
+    if (t + NST - 1 < t_end) wait_vmcnt<2 * (NST - 2) * SLABS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    refill(t);
+    if constexpr (decltype(NEXT)::value) {
+      s_tile(kslot(t + 1), sn);
+      sched_reads_ahead<KB * KS, 1, 1, 4>();
+    }
+  };
+
   // One step: softmax and PV of tile t (scores in st), overlapped with S of
   // tile t+1 (into sn).  At its top the step needs V(t) and K(t+1); the loads
   // issued after them are those of the NST-2 steps before (2 tiles each).
@@ -186,10 +220,7 @@ void fwd_kernel(const FwdArgs a) {
     if (t + NST - 1 < t_end) wait_vmcnt<2 * (NST - 2) * SLABS>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // everyone's part is in; everyone is done with step t-1
-    if (!last) {
-      if (t + NST < t_end) load_rows(a.k, t + NST, kslot(t + NST));    // slot of K(t), used in step t-1
-      if (t + NST - 1 < t_end) load_rows(a.v, t + NST - 1, vslot(t + NST - 1));  // slot of V(t-1)
-    }
+    refill(t);
     if constexpr (masked) {
       const int lo = lo_base - t * FWD_BN;
 #pragma unroll
@@ -276,24 +307,33 @@ void fwd_kernel(const FwdArgs a) {
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     f32x16 sa[KB], sb[KB];
-    s_tile(kslot(t_begin), sa);
-    const int tl = t_end - 1;
-    auto run = [&](int t0, int t1, auto MASK) __attribute__((always_inline)) {
-      int t = t0;
-      for (; t + 1 < t1; t += 2) {
-        step(t, sa, sb, MASK, std::false_type{});
-        step(t + 1, sb, sa, MASK, std::false_type{});
-      }
-      if (t < t1) {
-        step(t, sa, sb, MASK, std::false_type{});
+    // steps before this wave's first tile; the last of them computes S of it
+    int t = t_begin;
+    for (; t + 1 < w_begin; t++) idle_step(t, sa, std::false_type{});
+    if (w_begin < w_end) {
+      if (w_begin == t_begin) s_tile(kslot(t_begin), sa);
+      else idle_step(t++, sa, std::true_type{});
+      const int tl = w_end - 1;
+      auto run = [&](int t0, int t1, auto MASK) __attribute__((always_inline)) {
+        int u = t0;
+        for (; u + 1 < t1; u += 2) {
+          step(u, sa, sb, MASK, std::false_type{});
+          step(u + 1, sb, sa, MASK, std::false_type{});
+        }
+        if (u < t1) {
+          step(u, sa, sb, MASK, std::false_type{});
 #pragma unroll
-        for (int kb = 0; kb < KB; kb++) sa[kb] = sb[kb];
-      }
-    };
-    run(t_begin, min(ti0, tl), std::true_type{});
-    run(max(ti0, t_begin), min(ti1, tl), std::false_type{});
-    run(max(ti1, t_begin), tl, std::true_type{});
-    step(tl, sa, sb, std::true_type{}, std::true_type{});
+          for (int kb = 0; kb < KB; kb++) sa[kb] = sb[kb];
+        }
+      };
+      run(w_begin, min(ti0, tl), std::true_type{});
+      run(max(ti0, w_begin), min(ti1, tl), std::false_type{});
+      run(max(ti1, w_begin), tl, std::true_type{});
+      step(tl, sa, sb, std::true_type{}, std::true_type{});
+      t = w_end;
+    }
+    // steps after this wave's last tile
+    for (; t < t_end; t++) idle_step(t, sa, std::false_type{});
   }
 
   // ---- epilogue
