@@ -139,6 +139,41 @@ def run_decode(steps, warmup):
             "tflops": round(4.0 * d["D"] * pairs / (per_call_ms * 1e-3) / 1e12, 2)}
 
 
+def run_sweep(steps, warmup):
+    """Context sweep shaped like the jax-flash-attn3 README table: S = 512 ... 16384,
+    B = 16384 / S, H = 16, D = 128, bf16, causal and not; forward and fwd+bwd
+    TFLOP/s from the library's own kernel timing (HIP events)."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    rows = []
+    for causal in (False, True):
+        for S in (512, 1024, 2048, 4096, 8192, 16384):
+            B, H, D = 16384 // S, 16, 128
+            q, k, v, do = synth.device_normal(S, [(B, S, H, D)] * 4)
+            o, lse = ea.attn_fwd(q, k, v, causal=causal)
+            for _ in range(warmup):
+                ea.attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+                ea.attn_bwd(q, k, v, o, lse, do, causal=causal)
+            torch.cuda.synchronize()
+            ea.attn_timing_enable(True)
+            for _ in range(steps):
+                ea.attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+                ea.attn_bwd(q, k, v, o, lse, do, causal=causal)
+            torch.cuda.synchronize()
+            t = {n: ea.attn_timing_read(n)[1] / steps for n in ea._lib.KERNELS}
+            ea.attn_timing_enable(False)
+            fwd_ms = t["fwd"] + t["fwd_combine"]
+            bwd_ms = t["bwd_zero"] + t["bwd_dq"] + t["bwd_dkdv"]
+            pairs = visible_pairs(B, S, S, H, causal, (-1, -1))
+            rows.append({"S": S, "B": B, "causal": causal, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                         "fwd_tflops": round(4.0 * D * pairs / (fwd_ms * 1e-3) / 1e12, 1),
+                         "fwdbwd_tflops": round(14.0 * D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1)})
+            print(json.dumps(rows[-1]), flush=True)
+            del q, k, v, do, o, lse
+    return rows
+
+
 def cpu_baseline(inp, w, seconds_target=15.0):
     """Time the fp64 oracle on whole (batch, head) slices of the workload."""
     import numpy as np
@@ -175,9 +210,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
-    ap.add_argument("--workload", choices=("step", "decode"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
-                         "decode: only the decode-shaped forward (for profiling it alone)")
+                         "decode: only the decode-shaped forward (for profiling it alone); "
+                         "sweep: context sweep over S = 512..16384 (one JSON line per shape)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB elementwise copy first (reference for HBM counter runs)")
     args = ap.parse_args()
@@ -191,6 +227,9 @@ def main():
     import exact_attention_36_amd as ea
     from exact_attention_36_amd import synth
 
+    if args.workload == "sweep":
+        run_sweep(args.steps, args.warmup)
+        return
     if args.workload == "decode":
         if args.copy_calibration:
             copy_calibration()

@@ -82,18 +82,16 @@ __device__ __forceinline__ void buf_store8(u32x2 v, __amdgpu_buffer_rsrc_t r, ui
 __device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
-// 16 bytes straight from global memory into LDS: lane l's bytes land at
-// lds_base + 16*l (lds_base must be wave-uniform).
-__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_base), 16, off, 0, 0, 0);
-}
-
-// The same global -> LDS copy for prefetching streams, issued so that the
-// compiler does not track it: the compiler cannot tell which LDS buffer a DMA
+// 16 bytes straight from global memory into LDS (buffer_load ... lds): lane
+// l's bytes land at M0 + 16*l, M0 = the wave-uniform LDS address.  Issued
+// through inline assembly so that the compiler does not track it: the compiler cannot tell which LDS buffer a DMA
 // writes and would otherwise wait for every outstanding DMA before any later
 // LDS read, serialising the prefetch.  Callers order these copies with
 // explicit wait_vmcnt + s_barrier.  The descriptor is a raw buffer
 // (base, 0 stride, size in bytes, gfx9 dword 3), bounds-checked by hardware.
+// M0 is set inside the statement; the compiler does not preserve M0 across
+// it, and no other instruction of these kernels uses M0 (the only M0
+// references in their generated code are these writes).
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
