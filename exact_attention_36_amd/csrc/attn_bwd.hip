@@ -296,16 +296,14 @@ void bwd_dq_kernel(const BwdArgs a) {
         buf_store16(w, rw, qoff * 2 + (uint32_t)(dd * 4));
       }
   } else {
+    static_assert(4 * 32 * ROWB <= 4 * TILE, "dQ staging fits in the tile space");
+    __syncthreads();  // all waves are done reading the K/V tiles
     const auto rw = make_rsrc((uint16_t*)a.dq + qbase_e, qbytes);
-#pragma unroll
-    for (int d = 0; d < DB; d++)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; j4++) {
-        const int dd = d * 32 + 8 * j4 + 4 * hh;
-        const u32x2 w{pack2<F16>(acc[d][4 * j4] * a.scale, acc[d][4 * j4 + 1] * a.scale),
-                      pack2<F16>(acc[d][4 * j4 + 2] * a.scale, acc[d][4 * j4 + 3] * a.scale)};
-        buf_store8(w, rw, qoff + (uint32_t)(dd * 2));
-      }
+    store_rows16<D, F16>(acc, a.scale, smem + wave * 32 * ROWB, rw, [&](int r) {
+      const int p = p0 + wave * 32 + r;
+      const int i = div_group(p, a.s), hl = p - i * G;
+      return p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D) * 2) : DROP_ROW;
+    });
   }
 }
 
@@ -527,23 +525,26 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV; lane = key, registers = dims
-  if (my_key < si.lk) {
+  if (!a.grad_f32) {
+    __syncthreads();  // all waves are done reading the V block and the Q/dO tiles
+    static_assert(4 * 2 * 32 * ROWB <= VBLK + 4 * QTILE, "dK/dV staging fits in the tile space");
+    char* const stg = smem + wave * 2 * 32 * ROWB;  // this wave's dK and dV rows
+    auto row_off = [&](int r) {
+      const int kk = j0 + wave * 32 + r;
+      return kk < si.lk ? (uint32_t)((int64_t)kk * krow * 2) : DROP_ROW;
+    };
+    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes), row_off);
+    store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes), row_off);
+  } else if (my_key < si.lk) {
     const int64_t ob = ((int64_t)(si.k0 + my_key) * a.s.hkv + g) * D;
 #pragma unroll
     for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int dd = d * 32 + 8 * j4 + 4 * hh;
-        const float k0v = dk[d][4 * j4] * a.scale, k1v = dk[d][4 * j4 + 1] * a.scale;
-        const float k2v = dk[d][4 * j4 + 2] * a.scale, k3v = dk[d][4 * j4 + 3] * a.scale;
-        if (a.grad_f32) {
-          *(f32x4*)((float*)a.dk + ob + dd) = f32x4{k0v, k1v, k2v, k3v};
-          *(f32x4*)((float*)a.dv + ob + dd) = f32x4{dv[d][4 * j4], dv[d][4 * j4 + 1], dv[d][4 * j4 + 2], dv[d][4 * j4 + 3]};
-        } else {
-          *(u32x2*)((uint16_t*)a.dk + ob + dd) = u32x2{pack2<F16>(k0v, k1v), pack2<F16>(k2v, k3v)};
-          *(u32x2*)((uint16_t*)a.dv + ob + dd) =
-              u32x2{pack2<F16>(dv[d][4 * j4], dv[d][4 * j4 + 1]), pack2<F16>(dv[d][4 * j4 + 2], dv[d][4 * j4 + 3])};
-        }
+        *(f32x4*)((float*)a.dk + ob + dd) = f32x4{dk[d][4 * j4] * a.scale, dk[d][4 * j4 + 1] * a.scale,
+                                                  dk[d][4 * j4 + 2] * a.scale, dk[d][4 * j4 + 3] * a.scale};
+        *(f32x4*)((float*)a.dv + ob + dd) = f32x4{dv[d][4 * j4], dv[d][4 * j4 + 1], dv[d][4 * j4 + 2], dv[d][4 * j4 + 3]};
       }
   }
 }

@@ -124,6 +124,19 @@ __device__ __forceinline__ constexpr int tile_off(int r, int chunk) {  // byte o
   return r * (D * 2) + ((chunk ^ swz<D>(r)) << 4);
 }
 
+// Rows held MFMA-style by a wave -- lane l32 holds row l32, register i of
+// block d holds column 32 d + 8 (i/4) + 4 hh + i%4 -- scaled, rounded to 16
+// bits and stored through LDS so that every store instruction writes whole
+// rows: the wave's 32 rows go to `stage` (32 rows x 2D bytes, swizzled like
+// the K/V tiles) and come back 16 bytes per lane.  row_off(r) is the byte
+// offset of row r in the descriptor, or DROP_ROW for a row not to store (the
+// chunk offsets added to it stay past any descriptor's end).  Only this wave
+// touches `stage`.
+constexpr uint32_t DROP_ROW = 0x80000000u;
+template <int D, bool F16, class RowOff>
+__device__ __forceinline__ void store_rows16(const f32x16 (&v)[D / 32], float scale, char* stage,
+                                             __amdgpu_buffer_rsrc_t rs, RowOff row_off);
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes every lane supplies the address of 4 consecutive 16-bit values; lane
 // i receives, as its element e (e = 0..3), value i%4 of the 4 values
@@ -136,6 +149,25 @@ __device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const void* p) { return *LDS_PTR(const u32x4, p); }
+
+template <int D, bool F16, class RowOff>
+__device__ __forceinline__ void store_rows16(const f32x16 (&v)[D / 32], float scale, char* stage,
+                                             __amdgpu_buffer_rsrc_t rs, RowOff row_off) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < D / 32; d++)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; j4++)
+      *LDS_PTR(u32x2, stage + tile_off<D>(l32, 4 * d + j4) + 8 * hh) =
+          u32x2{pack2<F16>(v[d][4 * j4] * scale, v[d][4 * j4 + 1] * scale),
+                pack2<F16>(v[d][4 * j4 + 2] * scale, v[d][4 * j4 + 3] * scale)};
+  constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+  for (int it = 0; it < 32 / (64 / CPR); it++) {
+    const int r = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
+    buf_store16(*LDS_PTR(const u32x4, stage + tile_off<D>(r, ch)), rs, row_off(r) + (uint32_t)(ch * 16));
+  }
+}
 
 // ---------------------------------------------------------------- wave reductions
 // Lanes l and l^32 exchange a value; returns op(own, partner) on every lane.

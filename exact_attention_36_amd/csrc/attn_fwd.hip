@@ -384,7 +384,7 @@ void fwd_kernel(const FwdArgs a) {
     const int p = p0 + 32 * wave + r;
     const int i = div_group(p, a.s), hl = p - i * G;
     // rows past the work tile fall outside the descriptor (dropped)
-    const uint32_t off = p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + ch * 8) * 2) : 0xFFFFFFF0u;
+    const uint32_t off = p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + ch * 8) * 2) : DROP_ROW;
     buf_store16(v, ro, off);
   }
 }
