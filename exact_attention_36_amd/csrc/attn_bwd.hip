@@ -199,12 +199,14 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
   }
+  // (byte offsets inside one sequence's K/V fit in 31 bits)
+  const uint32_t tile_stride = (uint32_t)(FWD_BN * krow * 2);
   auto load_tile = [&](int t) {
     const int buf = (t - t_begin) & 1;
-    const int64_t skip = (int64_t)t * FWD_BN * krow;
-    const uint32_t left = kbytes - (uint32_t)(skip * 2);
-    const i32x4 rk = make_rsrc_words((const uint16_t*)a.k + kbase_e + skip, left);
-    const i32x4 rv = make_rsrc_words((const uint16_t*)a.v + kbase_e + skip, left);
+    const uint32_t skip = (uint32_t)t * tile_stride;  // bytes before tile t
+    const uint32_t left = kbytes - skip;
+    const i32x4 rk = make_rsrc_words((const char*)((const uint16_t*)a.k + kbase_e) + skip, left);
+    const i32x4 rv = make_rsrc_words((const char*)((const uint16_t*)a.v + kbase_e) + skip, left);
 #pragma unroll
     for (int n = 0; n < SLABS; n++) {
       dma_lds16(rk, smem + buf * TILE + (wave * SLABS + n) * 1024, dma_off[n]);
@@ -425,8 +427,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int64_t idx = st_base + (int64_t)(g * G + hl) * st_hs + i;
       // rows past the sequence read index 0 (valid memory); they are masked
       const uint32_t off = p < prows ? (uint32_t)(idx * 4) : 0u;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(st_lds + buf * 64));
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(st_lds + buf * 64));
       // lanes 0-31 fetch lse', lanes 32-63 fetch D: lane l's dword lands at m0 + 4 l
       if (hh == 0)
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rl)

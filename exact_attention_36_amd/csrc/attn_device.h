@@ -99,9 +99,11 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t byte
                (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu),
                (int32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
+// LDS byte address of a pointer into a __shared__ array: a generic pointer to
+// LDS carries the aperture in its high half and the LDS offset in its low half.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ void dma_lds16(i32x4 rsrc, const void* lds_base, uint32_t off) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_base);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(m0), "v"(off), "s"(rsrc)

@@ -163,9 +163,11 @@ void fwd_kernel(const FwdArgs a) {
   }
 
   // Tile t lives in K slot and V slot (t - t_begin) mod NST.
+  // (byte offsets inside one sequence's K/V fit in 31 bits)
+  const uint32_t tile_stride = (uint32_t)(FWD_BN * krow * 2);
   auto load_rows = [&](const void* src, int t, char* dst) __attribute__((always_inline)) {
-    const int64_t skip = (int64_t)t * FWD_BN * krow;  // elements before tile t
-    const i32x4 r = make_rsrc_words((const uint16_t*)src + kbase_e + skip, kbytes - (uint32_t)(skip * 2));
+    const uint32_t skip = (uint32_t)t * tile_stride;  // bytes before tile t
+    const i32x4 r = make_rsrc_words((const char*)((const uint16_t*)src + kbase_e) + skip, kbytes - skip);
 #pragma unroll
     for (int n = 0; n < SLABS; n++) dma_lds16(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
   };
