@@ -203,6 +203,82 @@ def cpu_baseline(inp, w, seconds_target=15.0):
                       "%.1f s" % (slices, S, S, t_used)}
 
 
+def read_power_clock():
+    """One `amd-smi metric -p -c` reading: socket power (W) and the mean of the
+    per-XCD shader clocks (MHz), or None where the tool is missing."""
+    import re
+    import subprocess
+    try:
+        txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+    clks = [float(m) for m in re.findall(r"^\s*CLK:\s*([0-9.]+)\s*MHz", txt, re.M)]
+    # the GFX_i blocks come first; other clock domains follow under their own names
+    gfx = []
+    for block in re.split(r"\n\s*(?=GFX_\d+:|MEM_\d+:|VCLK_\d+:|DCLK_\d+:|[A-Z]+_\d+:)", txt):
+        if block.strip().startswith("GFX_"):
+            m = re.search(r"^\s*CLK:\s*([0-9.]+)\s*MHz", block, re.M)
+            if m:
+                gfx.append(float(m.group(1)))
+    if not pw or not (gfx or clks):
+        return None
+    return float(pw.group(1)), sum(gfx) / len(gfx) if gfx else None
+
+
+def run_power(seconds):
+    """Socket power and shader clock while the workload's forward, backward
+    and whole step each run back to back for `seconds` (sampled after the
+    first 2 s), next to each phase's call rate."""
+    import threading
+    import numpy as np
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    w = WORKLOAD
+    inp = synth.batched_inputs(2, w["B"], w["S"], w["S"], w["HQ"], w["HKV"], w["D"], grads=True)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
+    o, lse = ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"])
+    phases = {
+        "fwd": lambda: ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"], out=o, lse=lse),
+        "bwd": lambda: ea.attn_bwd(q, k, v, o, lse, do, causal=w["causal"], window=w["window"]),
+        "step": lambda: (ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"], out=o, lse=lse),
+                         ea.attn_bwd(q, k, v, o, lse, do, causal=w["causal"], window=w["window"])),
+    }
+    res = []
+    for name, fn in phases.items():
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            if stop.wait(2.0):
+                return
+            while not stop.is_set():
+                r = read_power_clock()
+                if r:
+                    samples.append(r)
+                stop.wait(0.5)
+
+        th = threading.Thread(target=sampler)
+        th.start()
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            n += 20
+        dt = time.perf_counter() - t0
+        stop.set()
+        th.join()
+        pw = [s[0] for s in samples]
+        ck = [s[1] for s in samples if s[1] is not None]
+        res.append({"phase": name, "calls": n, "ms_per_call": round(dt / n * 1e3, 4),
+                    "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
+                    "gfx_clock_mhz": round(sum(ck) / len(ck), 1) if ck else None, "samples": len(samples)})
+        print(json.dumps(res[-1]), flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,10 +286,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
-    ap.add_argument("--workload", choices=("step", "decode", "sweep"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep", "power"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
-                         "sweep: context sweep over S = 512..16384 (one JSON line per shape)")
+                         "sweep: context sweep over S = 512..16384 (one JSON line per shape); "
+                         "power: socket power and shader clock (amd-smi) under the step's kernels")
+    ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB elementwise copy first (reference for HBM counter runs)")
     args = ap.parse_args()
@@ -229,6 +307,9 @@ def main():
 
     if args.workload == "sweep":
         run_sweep(args.steps, args.warmup)
+        return
+    if args.workload == "power":
+        run_power(args.seconds)
         return
     if args.workload == "decode":
         if args.copy_calibration:
