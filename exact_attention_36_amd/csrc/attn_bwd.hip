@@ -62,7 +62,8 @@ void bwd_dq_kernel(const BwdArgs a) {
   constexpr int KB = FWD_BN / 32, PT = FWD_BN / 16;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.s.group;
   int seq, g, mb;
@@ -332,7 +333,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   char* const do_lds = q_lds + 2 * QTILE;       // [buf] dO tile, input dtype
   float* const st_lds = (float*)(do_lds + 2 * QTILE);  // [buf][lse2 32 | delta 32]
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
   const int G = a.s.group;
@@ -480,25 +482,32 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const int qi_lo = div_group(p0, a.s), qi_hi = div_group(min(p0 + BM, prows) - 1, a.s);
     const bool interior = (p0 + BM <= prows) && j0 + wave * 32 >= band.kmin(qi_hi) &&
                           j0 + wave * 32 + 31 <= band.kmax(qi_lo);
-    // row statistics of this lane's 16 rows: rows 8a + 4hh + 0..3
+    // P and dS from the row statistics of this lane's 16 rows (rows
+    // 8a + 4hh + 0..3); only steps that straddle the band, the last query
+    // rows or the last keys mask (per element, with branches that keep the
+    // masked version's registers within the budget)
+    auto p_ds = [&](auto MASKED) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a4 = 0; a4 < 4; a4++) {
-      const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
-      const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
+      for (int a4 = 0; a4 < 4; a4++) {
+        const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
+        const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int i = 4 * a4 + e;
-        float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
-        if (!interior) {
-          const int pr = p0 + 8 * a4 + 4 * hh + e;
-          const int qi = div_group(pr, a.s);
-          const bool vis = pr < prows && my_key < si.lk && my_key >= band.kmin(qi) && my_key <= band.kmax(qi);
-          if (!vis) p = 0.f;
+        for (int e = 0; e < 4; e++) {
+          const int i = 4 * a4 + e;
+          float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
+          if constexpr (decltype(MASKED)::value) {
+            const int pr = p0 + 8 * a4 + 4 * hh + e;
+            const int qi = div_group(pr, a.s);
+            const bool vis = pr < prows && my_key < si.lk && my_key >= band.kmin(qi) && my_key <= band.kmax(qi);
+            if (!vis) p = 0.f;
+          }
+          s_acc[i] = p;
+          dp[i] = p * (dp[i] - dl[e]);  // dS
         }
-        s_acc[i] = p;
-        dp[i] = p * (dp[i] - dl[e]);  // dS
       }
-    }
+    };
+    if (interior) p_ds(std::false_type{});
+    else p_ds(std::true_type{});
     // P^T / dS^T as B operands: k-step u covers queries 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}
     u32x4 pf[2], sf[2];
 #pragma unroll
