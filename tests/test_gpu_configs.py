@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times: sampled outputs against the fp64 oracle (random rows and
-columns plus the edges), whole slices where the oracle is fast enough, and
-gradient sum rules on the full tensors:
+columns plus the edges), whole slices where the oracle is fast enough, the
+input-dtype gradients (the benchmark's) bit-equal to the rounded fp32 ones,
+and gradient sum rules on the full tensors:
     sum_j dV_j = sum_{h in group, i} g_i dO_i
     sum_j dK_j = scale * sum_{h in group, i} (1 - g_i) D_i q_i
 (per sequence and kv head; g_i = sigmoid(lse_i - sink_h), 1 without sinks),
@@ -54,6 +55,14 @@ def _sum_rules(name, q, do, dk, dv, lse, o, sinks, scale, q_rows, k_rows, hkv):
                 name, qs, g, wk, got_dk[wk], exp_dk[wk], tol_k[wk])
 
 
+def _input_dtype_grads_match(name, g32, g16):
+    """The gradients in the input dtype (the benchmark's launch) come from the
+    same accumulators as the fp32 ones and are their round-to-nearest-even:
+    bit-exact."""
+    for n, a32, a16 in zip(("dq", "dk", "dv"), g32, g16):
+        assert torch.equal(a16, a32.to(a16.dtype)), "%s: %s in the input dtype is not the rounded fp32 one" % (name, n)
+
+
 def _check_rows(name, p, o, lse_hq_t, dq, seqs, heads, rows, tok):
     r = oracle.rows(p, seqs, heads, rows, grads=dq is not None)
     assert_close(name + ".o[rows]", o[tok, heads], r["o"], "bf16")
@@ -84,6 +93,10 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
     if bwd:
         grads = ea.attn_bwd(q, k, v, o, lse, tens[3], causal=causal, window=window, sinks=s_dev,
                             grad_dtype=torch.float32)
+        g16 = ea.attn_bwd(q, k, v, o, lse, tens[3], causal=causal, window=window, sinks=s_dev)
+        torch.cuda.synchronize()
+        _input_dtype_grads_match(name, grads[:3], g16[:3])
+        del g16
     torch.cuda.synchronize()
     print("gpu done", flush=True)
     del q, k, v, tens
@@ -158,7 +171,10 @@ def test_config4_packed_varlen():
     o, lse = ea.attn_fwd_varlen(q, k, v, cu_d, cu_d, mx, mx, causal=True)
     dq, dk, dv, _ = ea.attn_bwd_varlen(q, k, v, o, lse, do, cu_d, cu_d, mx, mx, causal=True,
                                       grad_dtype=torch.float32)
+    g16 = ea.attn_bwd_varlen(q, k, v, o, lse, do, cu_d, cu_d, mx, mx, causal=True)
     torch.cuda.synchronize()
+    _input_dtype_grads_match("cfg4", (dq, dk, dv), g16[:3])
+    del g16
     print("gpu done", flush=True)
     T = int(cu[-1])
     oh, lh, dqh, dkh, dvh = host(o), host(lse), host(dq), host(dk), host(dv)
