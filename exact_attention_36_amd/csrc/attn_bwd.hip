@@ -460,6 +460,19 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
   const float c = a.scale_log2;
   const char* vrow = v_lds + wave * 32 * ROWB;  // this wave's 32 V rows
+  // The packed rows that see this lane's key form one range,
+  // [pr_lo, pr_lo + pr_span] (the queries [qmin, qmax] of the key times the
+  // group); the mask of a row is then one unsigned compare.  A key past the
+  // sequence is seen by no row.
+  int pr_lo = 1 << 30;
+  uint32_t pr_span = 0;
+  {
+    const int qlo = qband.qmin(my_key), qhi = qband.qmax(my_key);
+    if (my_key < si.lk && qhi >= qlo) {
+      pr_lo = qlo * G;
+      pr_span = (uint32_t)((qhi + 1) * G - 1 - pr_lo);
+    }
+  }
 
   if (pb_begin < pb_end) do_fetch(pb_begin, 0);
   for (int pb = pb_begin; pb < pb_end; pb++) {
@@ -484,30 +497,27 @@ void bwd_dkdv_kernel(const BwdArgs a) {
                           j0 + wave * 32 + 31 <= band.kmax(qi_lo);
     // P and dS from the row statistics of this lane's 16 rows (rows
     // 8a + 4hh + 0..3); only steps that straddle the band, the last query
-    // rows or the last keys mask (per element, with branches that keep the
-    // masked version's registers within the budget)
-    auto p_ds = [&](auto MASKED) __attribute__((always_inline)) {
+    // rows or the last keys mask
+    if (!interior) {
+      // scores of invisible (row, key) pairs -> -inf, so that P = 0 there
 #pragma unroll
-      for (int a4 = 0; a4 < 4; a4++) {
-        const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
-        const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int i = 4 * a4 + e;
-          float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
-          if constexpr (decltype(MASKED)::value) {
-            const int pr = p0 + 8 * a4 + 4 * hh + e;
-            const int qi = div_group(pr, a.s);
-            const bool vis = pr < prows && my_key < si.lk && my_key >= band.kmin(qi) && my_key <= band.kmax(qi);
-            if (!vis) p = 0.f;
-          }
-          s_acc[i] = p;
-          dp[i] = p * (dp[i] - dl[e]);  // dS
-        }
+      for (int i = 0; i < 16; i++) {
+        const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if ((uint32_t)(pr - pr_lo) > pr_span) s_acc[i] = -INFINITY;
       }
-    };
-    if (interior) p_ds(std::false_type{});
-    else p_ds(std::true_type{});
+    }
+#pragma unroll
+    for (int a4 = 0; a4 < 4; a4++) {
+      const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
+      const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = 4 * a4 + e;
+        const float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
+        s_acc[i] = p;
+        dp[i] = p * (dp[i] - dl[e]);  // dS
+      }
+    }
     // P^T / dS^T as B operands: k-step u covers queries 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}
     u32x4 pf[2], sf[2];
 #pragma unroll
