@@ -99,7 +99,14 @@ void bwd_dq_kernel(const BwdArgs a) {
   const int my_i = div_group(my_p, a.s);
   const int my_hl = my_p - my_i * G;
   const int my_h = g * G + my_hl;
-  const int my_kmin = band.kmin(my_i), my_kmax = band.kmax(my_i);
+  // this row's keys [kmin, kmin + span] as one unsigned compare (none for a
+  // row that sees no key)
+  int my_kmin = band.kmin(my_i);
+  uint32_t my_kspan = (uint32_t)(band.kmax(my_i) - my_kmin);
+  if (band.kmax(my_i) < my_kmin) {
+    my_kmin = 1 << 30;
+    my_kspan = 0;
+  }
 
   const int64_t qrow = (int64_t)a.s.hq * D, krow = (int64_t)a.s.hkv * D;
   const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * D;
@@ -232,16 +239,21 @@ void bwd_dq_kernel(const BwdArgs a) {
         st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], s == 0 ? f32x16{} : st[kb]);
         dp[kb] = mfma32<F16>(lds_read16(vt + kb * 32 * ROWB + k_off[s]), df[s], s == 0 ? f32x16{} : dp[kb]);
       }
-    const int j0 = t * FWD_BN;
+    if constexpr (masked) {  // scores of invisible keys -> -inf, so that P = 0 there
+      const int lo = my_kmin - t * FWD_BN - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int o = kb * 32 + 8 * (i >> 2) + (i & 3);
+          if ((uint32_t)(o - lo) > my_kspan) st[kb][i] = -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; kb++)
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        float p = exp2_fast(fmaf(st[kb][i], c, -mlse));
-        if constexpr (masked) {
-          const int j = j0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (j < my_kmin || j > my_kmax) p = 0.f;
-        }
+        const float p = exp2_fast(fmaf(st[kb][i], c, -mlse));
         st[kb][i] = p * (dp[kb][i] - row_d);  // dS
       }
     u32x4 sf[PT];
