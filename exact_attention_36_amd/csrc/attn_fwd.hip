@@ -392,12 +392,14 @@ void fwd_kernel(const FwdArgs a) {
 }
 
 // Merge split-KV partials: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s,
-// then the sink gate sigmoid(lse - sink).  One wave per packed row.
+// then the sink gate sigmoid(lse - sink).  D/4 lanes per packed row, each
+// reading 16 bytes (4 dims) of every split's partial; 64/(D/4) rows per wave.
 template <int D, bool F16>
 __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
-  constexpr int PER = D / 64;  // dims per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int LPR = D / 4;     // lanes per row
+  constexpr int RPW = 64 / LPR;  // rows per wave
+  const int lane = threadIdx.x & 63, sub = lane % LPR;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
   const int rows_bg = a.nmb * a.bm;
   const int64_t total = (int64_t)a.s.nseq * a.s.hkv * rows_bg;
   if (row >= total) return;
@@ -409,28 +411,28 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
   if (p >= si.lq * G) return;
   const int i = div_group(p, a.s), hl = p - i * G, h = g * G + hl;
   const int64_t split_stride = (int64_t)a.s.nseq * a.s.hkv * rows_bg;
+  const int ns = a.n_split;
 
   float mx = -INFINITY;
-  for (int s = 0; s < a.n_split; s++) mx = fmaxf(mx, a.lse_part[row + s * split_stride]);
+  for (int s = 0; s < ns; s++) mx = fmaxf(mx, a.lse_part[row + s * split_stride]);
   float sum = 0.f;
   if (mx != -INFINITY)
-    for (int s = 0; s < a.n_split; s++) sum += exp2_fast((a.lse_part[row + s * split_stride] - mx) * LOG2E);
+    for (int s = 0; s < ns; s++) sum += exp2_fast((a.lse_part[row + s * split_stride] - mx) * LOG2E);
   const float lse = mx == -INFINITY ? -INFINITY : mx + log2_fast(sum) * LN2;
-  float o[PER] = {};
+  f32x4 o{};
   if (mx != -INFINITY) {
-    for (int s = 0; s < a.n_split; s++) {
+    const float* op = a.o_part + row * D + sub * 4;
+#pragma unroll 4
+    for (int s = 0; s < ns; s++) {
       const float w = exp2_fast((a.lse_part[row + s * split_stride] - lse) * LOG2E);
-      const float* op = a.o_part + (row + s * split_stride) * D + lane * PER;
-#pragma unroll
-      for (int e = 0; e < PER; e++) o[e] = fmaf(w, op[e], o[e]);
+      o += w * *(const f32x4*)(op + s * split_stride * D);
     }
   }
   float gate = mx == -INFINITY ? 0.f : 1.f;
   if (a.sinks && mx != -INFINITY) gate = 1.f / (1.f + exp2_fast((a.sinks[h] - lse) * LOG2E));
-  uint16_t* ob = (uint16_t*)a.o + ((int64_t)(si.q0 + i) * a.s.hq + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; e += 2) *(uint32_t*)(ob + e) = pack2<F16>(o[e] * gate, o[e + 1] * gate);
-  if (lane == 0) a.lse[((int64_t)seq * a.s.hq + h) * a.s.sq + i] = lse;
+  uint16_t* ob = (uint16_t*)a.o + ((int64_t)(si.q0 + i) * a.s.hq + h) * D + sub * 4;
+  *(u32x2*)ob = u32x2{pack2<F16>(o[0] * gate, o[1] * gate), pack2<F16>(o[2] * gate, o[3] * gate)};
+  if (sub == 0) a.lse[((int64_t)seq * a.s.hq + h) * a.s.sq + i] = lse;
 }
 
 template <int D, bool F16>
@@ -450,7 +452,9 @@ template <int D, bool F16>
 static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.s.nseq * a.s.hkv * a.nmb * a.bm;
   timing_begin(K_FWD_COMBINE, st);
-  hipLaunchKernelGGL((fwd_combine_kernel<D, F16>), dim3((unsigned)((rows + 3) / 4)), dim3(THREADS), 0, st, a);
+  const int64_t per_block = 4 * (64 / (D / 4));  // rows per workgroup: 4 waves
+  hipLaunchKernelGGL((fwd_combine_kernel<D, F16>), dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(THREADS),
+                     0, st, a);
   timing_end(K_FWD_COMBINE, st);
   return hipGetLastError();
 }
