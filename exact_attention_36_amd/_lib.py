@@ -21,6 +21,7 @@ ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 
 EXPORTED = (
     "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
+    "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
     "attn_fwd_varlen", "attn_fwd_varlen_workspace_size", "attn_bwd_varlen",
     "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable",
     "attn_timing_read",
@@ -63,6 +64,8 @@ def load_library():
     lib.attn_fwd_workspace_size.argtypes = [P, i64, i64, i64]
     lib.attn_bwd.argtypes = [P, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.attn_bwd_workspace_size.argtypes = [P, i64, i64, i64, i32]
+    lib.attn_fwd_kvcache.argtypes = [P, i64, i64, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, sz, vp]
+    lib.attn_fwd_kvcache_workspace_size.argtypes = [P, i64, i64, vp, i32, i32, i64]
     lib.attn_fwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_fwd_varlen_workspace_size.argtypes = [P, i32, i64, i64, i32, i32]
     lib.attn_bwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -174,6 +177,28 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, s
                         _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _dtype_code(gd),
                         _ptr(ws), n, _stream(q.device)))
     return dq, dk, dv, dsinks
+
+
+def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causal=False, window=(-1, -1),
+                     sinks=None, softmax_scale=None, out=None, lse=None):
+    """Forward over a KV cache: q [B,Sq,Hq,D]; cache_seqlens int32 [B] (used keys per slot);
+    k_cache, v_cache [B,capacity,Hkv,D], or pages [num_blocks,page,Hkv,D] with
+    block_table int32 [B,max_blocks] -> (o, lse [B,Hq,Sq])."""
+    lib = load_library()
+    B, sq, hq, d = q.shape
+    p = make_params(q, k_cache, causal, window, sinks, softmax_scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, hq, sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if block_table is not None:
+        nblk, page, cap = int(block_table.shape[1]), int(k_cache.shape[1]), 0
+    else:
+        nblk, page, cap = 0, 0, int(k_cache.shape[1])
+    n = lib.attn_fwd_kvcache_workspace_size(ctypes.byref(p), B, sq, _ptr(block_table), nblk, page, cap)
+    ws = _workspace(n, q.device)
+    _check(lib.attn_fwd_kvcache(ctypes.byref(p), B, sq, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                _ptr(block_table), nblk, page, cap, _ptr(o), _ptr(lse), _ptr(ws), n,
+                                _stream(q.device)))
+    return o, lse
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,

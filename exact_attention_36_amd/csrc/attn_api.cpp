@@ -137,12 +137,23 @@ attn_status check_ws(const void* ws, size_t have, size_t need) {
   return ATTN_OK;
 }
 
+// KV-cache addressing of a batched forward (all null / 0: plain K, V).
+struct KvCache {
+  const int32_t* seqused_k = nullptr;
+  const int32_t* block_table = nullptr;
+  int32_t page_rows = 0, pages_per_seq = 0;
+};
+
 attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int64_t sq,
                     int64_t sk, int64_t total_q, int64_t max_q, const void* q, const void* k, const void* v, void* o,
-                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+                    float* lse, void* ws, size_t ws_bytes, void* stream, const KvCache& kvc = KvCache{}) {
   const bool packed = cu_q != nullptr;
   FwdArgs a{};
   a.s = seq_args(p, cu_q, cu_k, nseq, sq, sk, total_q);
+  a.s.seqused_k = kvc.seqused_k;
+  a.s.block_table = kvc.block_table;
+  a.s.page_rows = kvc.page_rows;
+  a.s.pages_per_seq = kvc.pages_per_seq;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -260,6 +271,54 @@ size_t attn_bwd_workspace_size(const attn_params* p, int64_t batch, int64_t seql
   (void)seqlen_k;
   if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1) return 0;
   return bwd_ws(p, batch * seqlen_q, grad_dtype).total;
+}
+
+// Bound on a KV-cache call's keys per slot: the slot capacity, or the pages
+// of one block-table row.
+static int64_t kvcache_max_keys(const int32_t* block_table, int32_t max_blocks_per_seq, int32_t page_block_size,
+                         int64_t cache_capacity) {
+  return block_table ? (int64_t)max_blocks_per_seq * page_block_size : cache_capacity;
+}
+
+size_t attn_fwd_kvcache_workspace_size(const attn_params* p, int64_t batch, int64_t seqlen_q,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       int32_t page_block_size, int64_t cache_capacity) {
+  const int64_t max_k = kvcache_max_keys(block_table, max_blocks_per_seq, page_block_size, cache_capacity);
+  if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1 || max_k < 1) return 0;
+  return fwd_ws(p, batch, seqlen_q, max_k, nullptr, nullptr);
+}
+
+attn_status attn_fwd_kvcache(const attn_params* p, int64_t batch, int64_t seqlen_q, const void* q,
+                             const void* k_cache, const void* v_cache, const int32_t* cache_seqlens,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, int32_t page_block_size,
+                             int64_t cache_capacity, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if (batch < 1 || seqlen_q < 1)
+    return fail(ATTN_EINVAL, "batch and seqlen_q must be >= 1 (got %lld, %lld)", (long long)batch,
+                (long long)seqlen_q);
+  if (!q || !k_cache || !v_cache || !o || !lse || !cache_seqlens)
+    return fail(ATTN_EINVAL, "q, k_cache, v_cache, cache_seqlens, o and lse must be non-NULL");
+  if (block_table) {
+    if (max_blocks_per_seq < 1) return fail(ATTN_EINVAL, "max_blocks_per_seq must be >= 1 (got %d)", max_blocks_per_seq);
+    if (page_block_size < FWD_BN || page_block_size % FWD_BN != 0)
+      return fail(ATTN_EINVAL, "page_block_size must be a positive multiple of %d (got %d)", FWD_BN, page_block_size);
+  } else if (cache_capacity < 1) {
+    return fail(ATTN_EINVAL, "cache_capacity must be >= 1 without a block table (got %lld)", (long long)cache_capacity);
+  }
+  const int64_t max_k = kvcache_max_keys(block_table, max_blocks_per_seq, page_block_size, cache_capacity);
+  if ((st = check_extent(seqlen_q, max_k, p)) != ATTN_OK) return st;
+  if (batch * seqlen_q * (p->heads_q / p->heads_kv) >= INT32_MAX || batch >= INT32_MAX ||
+      batch * max_blocks_per_seq >= INT32_MAX)
+    return fail(ATTN_ENOTSUP, "problem too large");
+  KvCache kvc;
+  kvc.seqused_k = cache_seqlens;
+  kvc.block_table = block_table;
+  kvc.page_rows = block_table ? page_block_size : 0;
+  kvc.pages_per_seq = block_table ? max_blocks_per_seq : 0;
+  // without a block table, slot b's keys start at row b * cache_capacity
+  return run_fwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, max_k, batch * seqlen_q, seqlen_q, q, k_cache,
+                 v_cache, o, lse, ws, ws_bytes, stream, kvc);
 }
 
 size_t attn_fwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,

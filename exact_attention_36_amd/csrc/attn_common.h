@@ -31,7 +31,7 @@ __device__ __forceinline__ SeqInfo seq_info(const SeqArgs& s, int seq) {
     r.q0 = seq * s.sq;
     r.lq = s.sq;
     r.k0 = seq * s.sk;
-    r.lk = s.sk;
+    r.lk = s.seqused_k ? s.seqused_k[seq] : s.sk;  // a KV-cache slot: its used keys
   }
   return r;
 }

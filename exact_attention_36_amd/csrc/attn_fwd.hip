@@ -166,8 +166,19 @@ void fwd_kernel(const FwdArgs a) {
   // (byte offsets inside one sequence's K/V fit in 31 bits)
   const uint32_t tile_stride = (uint32_t)(FWD_BN * krow * 2);
   auto load_rows = [&](const void* src, int t, char* dst) __attribute__((always_inline)) {
-    const uint32_t skip = (uint32_t)t * tile_stride;  // bytes before tile t
-    const i32x4 r = make_rsrc_words((const char*)((const uint16_t*)src + kbase_e) + skip, kbytes - skip);
+    i32x4 r;
+    if (a.s.block_table) {
+      // paged KV cache: the tile's page, and the bytes up to its last valid key
+      // (a tile never crosses a page: page_rows is a multiple of the tile)
+      const int key0 = t * FWD_BN, page = key0 / a.s.page_rows;
+      const int64_t phys = a.s.block_table[(int64_t)seq * a.s.pages_per_seq + page];
+      const int64_t row0 = phys * a.s.page_rows + (key0 - page * a.s.page_rows);
+      r = make_rsrc_words((const uint16_t*)src + (row0 * a.s.hkv + g) * D,
+                          (uint32_t)(((int64_t)(min(FWD_BN, si.lk - key0) - 1) * krow + D) * 2));
+    } else {
+      const uint32_t skip = (uint32_t)t * tile_stride;  // bytes before tile t
+      r = make_rsrc_words((const char*)((const uint16_t*)src + kbase_e) + skip, kbytes - skip);
+    }
 #pragma unroll
     for (int n = 0; n < SLABS; n++) dma_lds16(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
   };

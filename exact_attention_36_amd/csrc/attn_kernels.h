@@ -26,6 +26,12 @@ struct SeqArgs {
   int32_t hq, hkv, group;
   uint32_t group_magic;  // ceil(2^32 / group) for group >= 2 (fast division, see div_group)
   int32_t causal, wl, wr;  // window bounds, -1 = unbounded
+  // KV cache (batched forward only): slot seq uses its first seqused_k[seq]
+  // keys of sk; with a block table, key j of slot seq is row j % page_rows of
+  // page block_table[seq * pages_per_seq + j / page_rows] ([page][row][hkv][D])
+  const int32_t* seqused_k;    // [nseq] or nullptr
+  const int32_t* block_table;  // [nseq][pages_per_seq] or nullptr
+  int32_t page_rows, pages_per_seq;
 };
 
 struct FwdArgs {

@@ -100,6 +100,30 @@ def batched_inputs(seed: int, B: int, sq: int, sk: int, hq: int, hkv: int, d: in
     return dict(q=q, k=k, v=v, dout=dout, sinks=s)
 
 
+def kvcache_inputs(seed: int, B: int, sq: int, hq: int, hkv: int, d: int, lens, capacity: int,
+                   page: int = 0, sinks: bool = False, dtype: str = "bf16"):
+    """q [B,sq,hq,d] and a KV cache holding lens[b] used keys per slot (uint16 bits).
+
+    page == 0: k_cache, v_cache [B, capacity, hkv, d]; else pages of `page` rows,
+    ceil(capacity / page) per slot, dealt to the slots in a seeded random order:
+    k_cache, v_cache [B * pages, page, hkv, d] and block_table int32 [B, pages].
+    Rows past a slot's used length hold random values too (they must stay
+    invisible)."""
+    rng = np.random.default_rng(seed)
+    q = normal_bits(rng, (B, sq, hq, d), dtype)
+    if page:
+        npg = -(-capacity // page)
+        k = normal_bits(rng, (B * npg, page, hkv, d), dtype)
+        v = normal_bits(rng, (B * npg, page, hkv, d), dtype)
+        table = rng.permutation(B * npg).astype(np.int32).reshape(B, npg)
+    else:
+        k = normal_bits(rng, (B, capacity, hkv, d), dtype)
+        v = normal_bits(rng, (B, capacity, hkv, d), dtype)
+        table = None
+    s = rng.standard_normal(hq, dtype=np.float32) if sinks else None
+    return dict(q=q, k=k, v=v, lens=np.asarray(lens, np.int32), block_table=table, sinks=s)
+
+
 def varlen_inputs(seed: int, lengths_q, lengths_k, hq: int, hkv: int, d: int,
                   grads: bool = True, sinks: bool = False, dtype: str = "bf16"):
     """Packed q, k, v, dout ([T,H,D] uint16 bits), cu_seqlens and sinks for given lengths."""

@@ -120,6 +120,34 @@ size_t attn_bwd_workspace_size(const attn_params *params, int64_t batch, int64_t
                                int64_t seqlen_k, int32_t grad_dtype);
 
 /*
+ * Forward over a KV cache (decode / chunked prefill; forward only).  q is
+ * [B, seqlen_q, Hq, D]; slot b of the cache holds cache_seqlens[b] valid keys
+ * (device int32 [B]): later keys are invisible and the causal / window band
+ * is aligned to that used length (fa4-jax page, varlen semantics paragraph:
+ * seqused_k).  Without block_table, k_cache and v_cache are
+ * [B, cache_capacity, Hkv, D].  With block_table (device int32
+ * [B, max_blocks_per_seq]) they are pages [num_blocks, page_block_size, Hkv, D]
+ * and key j of slot b is row j % page_block_size of page
+ * block_table[b][j / page_block_size] (vllm-project/flash-attention README on
+ * the GitHub search page, flash_attn_with_kvcache: paged KV cache;
+ * page_block_size here: any positive multiple of 64, the page's 256
+ * included).  cache_seqlens and block_table contents are NOT checked: each
+ * cache_seqlens[b] must be within [0, capacity] (capacity = cache_capacity,
+ * or max_blocks_per_seq * page_block_size), and every page a used key needs
+ * must exist.  o, lse as in attn_fwd; workspace from
+ * attn_fwd_kvcache_workspace_size with the same cache arguments
+ * (cache_capacity is ignored when block_table is given).
+ */
+attn_status attn_fwd_kvcache(const attn_params *params, int64_t batch, int64_t seqlen_q, const void *q,
+                             const void *k_cache, const void *v_cache, const int32_t *cache_seqlens,
+                             const int32_t *block_table, int32_t max_blocks_per_seq,
+                             int32_t page_block_size, int64_t cache_capacity, void *o, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
+size_t attn_fwd_kvcache_workspace_size(const attn_params *params, int64_t batch, int64_t seqlen_q,
+                                       const int32_t *block_table, int32_t max_blocks_per_seq,
+                                       int32_t page_block_size, int64_t cache_capacity);
+
+/*
  * Forward, packed [T,H,D] with device int32 cu_seqlens_q/k [num_seqs+1].
  * total_q / total_k are the token counts (cu_seqlens_*[num_seqs]);
  * max_seqlen_q / max_seqlen_k bound every sequence's length.  lse is fp32

@@ -168,6 +168,36 @@ def varlen(q, k, v, cu_q, cu_k, scale, causal=False, window=(-1, -1), dout=None,
                    window=window, dout=dout, sinks=sinks, dtype=dtype)
 
 
+def kvcache(q, k_cache, v_cache, cache_seqlens, scale, block_table=None, causal=False, window=(-1, -1),
+            sinks=None, dtype="bf16"):
+    """A forward over a KV cache as a Problem.  Slot b's queries q[b] attend to
+    the first cache_seqlens[b] keys of its slot, the band aligned to that used
+    length (fa4-jax page, varlen semantics paragraph: seqused_k).  Without a
+    block table the slot is k_cache[b] ([B, capacity, Hkv, D]); with one, key j
+    of slot b is row j % page of page block_table[b][j // page] of the paged
+    cache [num_blocks, page, Hkv, D] (vllm-project/flash-attention README on
+    the GitHub search page, flash_attn_with_kvcache: paged KV cache).  The used
+    keys are gathered into packed form; the attention itself is the packed
+    Problem's."""
+    B, sq, hq, d = q.shape
+    lens = np.asarray(cache_seqlens, np.int64)
+    rows_per = k_cache.shape[1]  # slot capacity, or page size with a block table
+    kf = k_cache.reshape(-1, k_cache.shape[2], d)
+    vf = v_cache.reshape(-1, v_cache.shape[2], d)
+    idx = []
+    for b in range(B):
+        j = np.arange(lens[b], dtype=np.int64)
+        if block_table is None:
+            idx.append(b * rows_per + j)
+        else:
+            idx.append(np.asarray(block_table[b], np.int64)[j // rows_per] * rows_per + j % rows_per)
+    idx = np.concatenate(idx)
+    return Problem(q=q.reshape(B * sq, hq, d), k=kf[idx], v=vf[idx],
+                   q_start=np.arange(B, dtype=np.int64) * sq, q_len=np.full(B, sq, np.int64),
+                   k_start=np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64), k_len=lens,
+                   scale=scale, causal=causal, window=window, sinks=sinks, dtype=dtype)
+
+
 def visible(causal, left, right, lq, lk, i, j) -> bool:
     """The bottom-right aligned causal/window predicate, as the oracle applies it."""
     return bool(_load().oracle_visible(int(causal), int(left), int(right), int(lq), int(lk),

@@ -104,6 +104,24 @@ def test_bwd_rejects_bad_arguments():
     assert call(p, ws=None, nws=0) == _lib.ATTN_EINVAL
 
 
+def test_kvcache_rejects_bad_arguments():
+    lib = ea.load_library()
+    p = _params()
+    call = lambda q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, bt=None, nb=0, page=0, cap=64, o=FAKE, lse=FAKE, sq=4: \
+        lib.attn_fwd_kvcache(ctypes.byref(p), 2, sq, q, kc, vc, sl, bt, nb, page, cap, o, lse, None, 0, None)
+    assert call(sl=None) == _lib.ATTN_EINVAL
+    assert "cache_seqlens" in ea.last_error()
+    assert call(cap=0) == _lib.ATTN_EINVAL            # no block table: the slot capacity is needed
+    assert call(bt=FAKE, nb=0, page=256) == _lib.ATTN_EINVAL
+    assert call(bt=FAKE, nb=4, page=100) == _lib.ATTN_EINVAL   # pages hold whole 64-key tiles
+    assert "page_block_size" in ea.last_error()
+    assert call(sq=0) == _lib.ATTN_EINVAL
+    assert call(bt=FAKE, nb=1 << 20, page=1 << 10) == _lib.ATTN_ENOTSUP
+    # the workspace query follows the same cache arguments
+    assert lib.attn_fwd_kvcache_workspace_size(ctypes.byref(p), 2, 4, None, 0, 0, 0) == 0
+    assert lib.attn_fwd_kvcache_workspace_size(ctypes.byref(p), 2, 4, FAKE, 128, 256, 0) > 0
+
+
 def test_varlen_rejects_bad_arguments():
     lib = ea.load_library()
     p = _params()

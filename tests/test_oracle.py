@@ -263,6 +263,48 @@ def test_varlen_equals_per_sequence_calls_and_isolation():
         np.testing.assert_array_equal(r[key][sl0], r2[key][sl0])
 
 
+# ---------------------------------------------------------------- KV cache (seqused_k, paged)
+
+def test_kvcache_gather_pins():
+    """The KV-cache wrapper against independent constructions: slot b equals a
+    plain call on its first cache_seqlens[b] keys (band aligned to that length),
+    and a paged cache built by scattering the slots' rows over shuffled pages
+    gives bit-identical results."""
+    rng = np.random.default_rng(11)
+    B, sq, hq, hkv, d, cap, page = 3, 4, 4, 2, 8, 300, 64
+    q = rng.standard_normal((B, sq, hq, d))
+    kc = rng.standard_normal((B, cap, hkv, d))
+    vc = rng.standard_normal((B, cap, hkv, d))
+    lens = np.array([cap, 137, 1])
+    sinks = rng.standard_normal(hq)
+    for causal, window in ((True, (-1, -1)), (False, (20, 5)), (True, (50, 0))):
+        got = oracle.full(oracle.kvcache(q, kc, vc, lens, 0.3, causal=causal, window=window, sinks=sinks,
+                                         dtype="f64"), grads=False)
+        for b in range(B):
+            L = int(lens[b])
+            one = oracle.full(oracle.batched(q[b:b + 1], kc[b:b + 1, :L], vc[b:b + 1, :L], 0.3, causal=causal,
+                                             window=window, sinks=sinks, dtype="f64"), grads=False)
+            rows = slice(b * sq, (b + 1) * sq)
+            np.testing.assert_array_equal(got["o"][rows], one["o"])
+            np.testing.assert_array_equal(got["lse"][:, rows], one["lse"])
+        # the same cache, paged: slot b's pages scattered over a shuffled page pool
+        npg = -(-cap // page)
+        phys = rng.permutation(B * npg)
+        table = phys.reshape(B, npg)
+        kp = np.zeros((B * npg, page, hkv, d))
+        vp = np.zeros((B * npg, page, hkv, d))
+        for b in range(B):
+            for i in range(npg):
+                r = slice(i * page, min(cap, (i + 1) * page))
+                n = r.stop - r.start
+                kp[table[b, i], :n] = kc[b, r]
+                vp[table[b, i], :n] = vc[b, r]
+        paged = oracle.full(oracle.kvcache(q, kp, vp, lens, 0.3, block_table=table, causal=causal, window=window,
+                                           sinks=sinks, dtype="f64"), grads=False)
+        np.testing.assert_array_equal(paged["o"], got["o"])
+        np.testing.assert_array_equal(paged["lse"], got["lse"])
+
+
 # ---------------------------------------------------------------- T10, T11: invariances
 
 def test_key_shift_invariance():
