@@ -139,6 +139,43 @@ def run_decode(steps, warmup):
             "tflops": round(4.0 * d["D"] * pairs / (per_call_ms * 1e-3) / 1e12, 2)}
 
 
+def run_kvcache(steps, warmup, page=256):
+    """The decode shape served from a paged KV cache (attn_fwd_kvcache): every
+    slot full (cache_seqlens = 32768), pages of `page` rows dealt to the slots
+    in a seeded random order; time per call and K/V GB/s as run_decode."""
+    import numpy as np
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    d = DECODE
+    npg = d["SK"] // page
+    q, k, v = synth.device_normal(5, [(d["B"], d["SQ"], d["HQ"], d["D"]), (d["B"] * npg, page, d["HKV"], d["D"]),
+                                      (d["B"] * npg, page, d["HKV"], d["D"])])
+    table = torch.from_numpy(np.random.default_rng(5).permutation(d["B"] * npg).astype(np.int32)
+                             .reshape(d["B"], npg)).cuda()
+    lens = torch.full((d["B"],), d["SK"], dtype=torch.int32, device="cuda")
+    o, lse = ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True)
+    for _ in range(warmup):
+        ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ea.attn_timing_enable(True)
+    for _ in range(steps):
+        ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    n_s, ms_s = ea.attn_timing_read("fwd")
+    n_c, ms_c = ea.attn_timing_read("fwd_combine")
+    ea.attn_timing_enable(False)
+    per_call_ms = (ms_s + ms_c) / steps
+    kv_bytes = 2 * d["B"] * d["SK"] * d["HKV"] * d["D"] * 2
+    gbps = kv_bytes / (per_call_ms * 1e-3) / 1e9
+    del q, k, v, o, lse, table
+    torch.cuda.empty_cache()
+    return {"workload": d["name"] + " paged KV cache (pages of %d rows, shuffled)" % page,
+            "ms_per_call": round(per_call_ms, 4), "split_kernel_ms": round(ms_s / max(n_s, 1), 4),
+            "combine_ms": round(ms_c / max(n_c, 1), 4), "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1),
+            "hbm_peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 def run_sweep(steps, warmup):
     """Context sweep shaped like the jax-flash-attn3 README table: S = 512 ... 16384,
     B = 16384 / S, H = 16, D = 128, bf16, causal and not; forward and fwd+bwd
@@ -315,6 +352,7 @@ def main():
         if args.copy_calibration:
             copy_calibration()
         dec = run_decode(args.steps, args.warmup)
+        dec["paged"] = run_kvcache(args.steps, args.warmup)
         print(json.dumps({"metric": "decode-shaped forward, K/V HBM GB/s, 1 MI355X", "value": dec["kv_GBps"],
                           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                           "ms_per_step": dec["ms_per_call"], "higher_is_better": True, "scaling": "weak",
@@ -404,6 +442,7 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = run_decode(max(3, args.steps // 4), 2)
+        out["decode"]["paged"] = run_kvcache(max(3, args.steps // 4), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out))

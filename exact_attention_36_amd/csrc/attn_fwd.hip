@@ -165,13 +165,27 @@ void fwd_kernel(const FwdArgs a) {
   // Tile t lives in K slot and V slot (t - t_begin) mod NST.
   // (byte offsets inside one sequence's K/V fit in 31 bits)
   const uint32_t tile_stride = (uint32_t)(FWD_BN * krow * 2);
+  // Paged KV cache: the block-table entries of 64 consecutive pages of this
+  // slot, one per lane, [tbl_base, tbl_base + 64); a tile's page is then a
+  // readlane, and the window moves (one global load) only every 64 pages.
+  // Requested pages never fall more than one below the latest request.
+  int tbl_base = -(1 << 30), tbl = 0;
+  auto page_phys = [&](int page) __attribute__((always_inline)) {
+    if (page >= tbl_base + 64) {
+      tbl_base = max(page - 1, 0);
+      const int idx = tbl_base + lane;
+      tbl = idx < a.s.pages_per_seq ? a.s.block_table[(int64_t)seq * a.s.pages_per_seq + idx] : 0;
+      wait_vmcnt<0>();  // the entries land before use (and no table load stays in the DMA counts)
+    }
+    return (int64_t)__builtin_amdgcn_readlane(tbl, page - tbl_base);
+  };
   auto load_rows = [&](const void* src, int t, char* dst) __attribute__((always_inline)) {
     i32x4 r;
     if (a.s.block_table) {
       // paged KV cache: the tile's page, and the bytes up to its last valid key
       // (a tile never crosses a page: page_rows is a multiple of the tile)
       const int key0 = t * FWD_BN, page = key0 / a.s.page_rows;
-      const int64_t phys = a.s.block_table[(int64_t)seq * a.s.pages_per_seq + page];
+      const int64_t phys = page_phys(page);
       const int64_t row0 = phys * a.s.page_rows + (key0 - page * a.s.page_rows);
       r = make_rsrc_words((const uint16_t*)src + (row0 * a.s.hkv + g) * D,
                           (uint32_t)(((int64_t)(min(FWD_BN, si.lk - key0) - 1) * krow + D) * 2));

@@ -24,6 +24,9 @@ CASES = [
     ("paged128_noncausal_gqa8", 2, 7, 16, 2, 128, [129, 1000], 1024, 128, False, (-1, -1), True, "bf16"),
     ("contig_decode_q1", 8, 1, 8, 1, 128, [4096, 1, 64, 65, 2000, 3333, 0, 4095], 4096, 0, True, (-1, -1), False,
      "bf16"),
+    # 4688 pages of one tile over at most 64 splits: every split's range spans more than the 64
+    # block-table entries held at a time
+    ("paged64_long_split", 1, 4, 2, 1, 64, [300000], 300032, 64, True, (-1, -1), False, "bf16"),
 ]
 
 
@@ -57,3 +60,27 @@ def test_kvcache_equals_plain_forward_on_full_slots():
     o2, lse2 = ea.attn_fwd(q, kc, vc, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_kvcache_paged_unsplit_rows_sampled():
+    """Enough work tiles that the forward does not split the keys: each
+    workgroup walks 100+ pages of 64 rows itself (block-table window moves);
+    sampled rows plus the edges against the oracle."""
+    B, sq, hq, hkv, d, page = 2, 2048, 16, 16, 128, 64
+    lens = [8192, 5000]
+    inp = synth.kvcache_inputs(21, B, sq, hq, hkv, d, lens, 8192, page=page)
+    q, kc, vc = (dev_tensor(inp[n]) for n in ("q", "k", "v"))
+    seqlens = torch.from_numpy(inp["lens"]).cuda()
+    table = torch.from_numpy(inp["block_table"]).cuda()
+    o, lse = ea.attn_fwd_kvcache(q, kc, vc, seqlens, block_table=table, causal=True)
+    torch.cuda.synchronize()
+    p = oracle.kvcache(inp["q"], inp["k"], inp["v"], inp["lens"], scale_of(d), block_table=inp["block_table"],
+                       causal=True)
+    rng = np.random.default_rng(22)
+    seqs = np.r_[rng.integers(0, B, 256), 0, 0, 1, 1]
+    heads = np.r_[rng.integers(0, hq, 256), 0, hq - 1, 0, hq - 1]
+    rows = np.r_[rng.integers(0, sq, 256), 0, sq - 1, 0, sq - 1]
+    r = oracle.rows(p, seqs, heads, rows)
+    tok = seqs * sq + rows
+    assert_close("paged_unsplit.o[rows]", host(o).reshape(B * sq, hq, d)[tok, heads], r["o"], "bf16")
+    assert_lse("paged_unsplit.lse[rows]", host(lse).transpose(1, 0, 2).reshape(hq, B * sq)[heads, tok], r["lse"])
