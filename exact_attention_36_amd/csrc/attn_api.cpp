@@ -31,6 +31,10 @@ constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Head dim of the kernel tiles that serve head_dim: the next of 64, 128 (the
+// tile columns past head_dim are zero).
+int tile_dim(int head_dim) { return head_dim <= 64 ? 64 : 128; }
+
 float resolve_scale(const attn_params* p) {
   const float s = p->softmax_scale;
   if (!(s > 0.f) || std::isnan(s)) return 1.0f / std::sqrt((float)p->head_dim);
@@ -41,11 +45,10 @@ attn_status check_params(const attn_params* p) {
   if (!p) return fail(ATTN_EINVAL, "params is NULL");
   if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16)
     return fail(ATTN_EINVAL, "dtype must be ATTN_BF16 or ATTN_FP16 (got %d)", p->dtype);
-  if (p->head_dim != 64 && p->head_dim != 128) {
-    if (p->head_dim > 0 && p->head_dim <= 256 && p->head_dim % 8 == 0)
-      return fail(ATTN_ENOTSUP, "head_dim %d is valid but not built (built: 64, 128)", p->head_dim);
+  if (p->head_dim < 8 || p->head_dim > 256 || p->head_dim % 8)
     return fail(ATTN_EINVAL, "head_dim must be a multiple of 8 in [8, 256] (got %d)", p->head_dim);
-  }
+  if (p->head_dim > 128)
+    return fail(ATTN_ENOTSUP, "head_dim %d is valid but not built (built: multiples of 8 up to 128)", p->head_dim);
   if (p->heads_q < 1 || p->heads_kv < 1)
     return fail(ATTN_EINVAL, "heads_q and heads_kv must be >= 1 (got %d, %d)", p->heads_q, p->heads_kv);
   if (p->heads_q % p->heads_kv)
@@ -79,6 +82,7 @@ SeqArgs seq_args(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
   s.hq = p->heads_q;
   s.hkv = p->heads_kv;
   s.group = p->heads_q / p->heads_kv;
+  s.dg = p->head_dim;
   s.group_magic = s.group >= 2 ? (uint32_t)((((uint64_t)1 << 32) + s.group - 1) / s.group) : 0u;
   s.causal = p->causal;
   s.wl = p->window_left;
@@ -105,7 +109,7 @@ size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_sp
   if (bm_out) *bm_out = bm;
   if (ns <= 1) return 0;
   const int64_t rows = (int64_t)ns * B * p->heads_kv * nmb * bm;
-  return align_up(rows * p->head_dim * 4) + align_up(rows * 4);
+  return align_up(rows * tile_dim(p->head_dim) * 4) + align_up(rows * 4);
 }
 
 // Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like
@@ -181,7 +185,7 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
     if (ns > 1) {
       const int64_t rows = (int64_t)ns * nseq * p->heads_kv * a.nmb * bm;
       a.o_part = (float*)ws;
-      a.lse_part = (float*)((char*)ws + align_up(rows * p->head_dim * 4));
+      a.lse_part = (float*)((char*)ws + align_up(rows * tile_dim(p->head_dim) * 4));
     }
     const int64_t ctas = GroupGrid{(int)(ns * p->heads_kv * (int64_t)nseq), a.nmb}.grid_size();
     if (ctas >= INT32_MAX || (int64_t)ns * p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
@@ -189,9 +193,9 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   }
   if (a.total_ctas == 0) return ATTN_OK;
   hipStream_t s = (hipStream_t)stream;
-  attn_status st = launched(launch_fwd(a, p->head_dim, p->dtype == ATTN_FP16, s));
+  attn_status st = launched(launch_fwd(a, tile_dim(p->head_dim), p->dtype == ATTN_FP16, s));
   if (st != ATTN_OK || a.n_split <= 1) return st;
-  return launched(launch_fwd_combine(a, p->head_dim, p->dtype == ATTN_FP16, s));
+  return launched(launch_fwd_combine(a, tile_dim(p->head_dim), p->dtype == ATTN_FP16, s));
 }
 
 attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int64_t sq,
@@ -244,7 +248,7 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
     a.total_ctas = (int32_t)ctas;
     a.total_ctas_q = (int32_t)ctas_q;
   }
-  return launched(launch_bwd(a, p->head_dim, p->dtype == ATTN_FP16, (hipStream_t)stream));
+  return launched(launch_bwd(a, tile_dim(p->head_dim), p->dtype == ATTN_FP16, (hipStream_t)stream));
 }
 
 attn_status check_grad_dtype(const attn_params* p, int32_t grad_dtype) {

@@ -52,7 +52,7 @@ __global__ void bwd_zero_kernel(float* p, int n) {
 // tile of 64 keys:  S^T = K Q^T,  dP^T = V dO^T  (K, V natural 16-byte LDS
 // reads), P and dS lane-locally from the row's lse' and D, then
 // dQ^T += K^T dS^T with K^T through transposing LDS reads.
-template <int D, bool F16>
+template <int D, bool F16, bool PAD>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const BwdArgs a) {
   constexpr int BM = BWD_QBM;
@@ -108,27 +108,30 @@ void bwd_dq_kernel(const BwdArgs a) {
     my_kspan = 0;
   }
 
-  const int64_t qrow = (int64_t)a.s.hq * D, krow = (int64_t)a.s.hkv * D;
-  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * D;
-  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 2) : 0u;
-  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * D) * 2);
-  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
-  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2) : 0u;
+  // In memory a head holds dg <= D values (PAD: a run-time dg < D); the tile
+  // columns past dg are zero.
+  const int dg = PAD ? a.s.dg : D;
+  const int64_t qrow = (int64_t)a.s.hq * dg, krow = (int64_t)a.s.hkv * dg;
+  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * dg;
+  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * dg) * 2) : 0u;
+  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * dg) * 2);
+  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * dg;
+  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2) : 0u;
   const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
   const auto rdo = make_rsrc((const uint16_t*)a.dout + qbase_e, qbytes);
 
   u32x4 qf[KS], df[KS];
 #pragma unroll
   for (int s = 0; s < KS; s++) {
-    qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
-    df[s] = buf_load16(rdo, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+    qf[s] = buf_load16(rq, chunk_off(qoff, 2 * s + hh, dg));
+    df[s] = buf_load16(rdo, chunk_off(qoff, 2 * s + hh, dg));
   }
   // The fp16 copy of Q that the dK/dV kernel stages (bf16 inputs): every
   // (query, q head) row is in exactly one of these work tiles.
   if (a.q16) {
     const auto rq16 = make_rsrc(a.q16 + qbase_e, qbytes);
 #pragma unroll
-    for (int s = 0; s < KS; s++) buf_store16(bf16x8_to_f16x8(qf[s]), rq16, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+    for (int s = 0; s < KS; s++) buf_store16(bf16x8_to_f16x8(qf[s]), rq16, chunk_off(qoff, 2 * s + hh, dg));
   }
   // Row statistics, computed here once per (query row, q head) and left in
   // the workspace for the dK/dV kernel that runs after this one:
@@ -142,7 +145,7 @@ void bwd_dq_kernel(const BwdArgs a) {
     float part = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; s++) {
-      const u32x4 ov = buf_load16(ro, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+      const u32x4 ov = buf_load16(ro, chunk_off(qoff, 2 * s + hh, dg));
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), part);
@@ -194,7 +197,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   for (int n = 0; n < SLABS; n++) {
     const int byte = (wave * SLABS + n) * 1024 + lane * 16;
     const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-    dma_off[n] = (uint32_t)((r * krow + (pos ^ swz<D>(r)) * 8) * 2);
+    dma_off[n] = chunk_off((uint32_t)(r * krow * 2), pos ^ swz<D>(r), dg);
   }
   int k_off[KS];
 #pragma unroll
@@ -308,7 +311,7 @@ void bwd_dq_kernel(const BwdArgs a) {
                       __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 1] * a.scale),
                       __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 2] * a.scale),
                       __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 3] * a.scale)};
-        buf_store16(w, rw, qoff * 2 + (uint32_t)(dd * 4));
+        buf_store16(w, rw, dd < dg ? qoff * 2 + (uint32_t)(dd * 4) : DROP_ROW);
       }
   } else {
     static_assert(4 * 32 * ROWB <= 4 * TILE, "dQ staging fits in the tile space");
@@ -317,8 +320,8 @@ void bwd_dq_kernel(const BwdArgs a) {
     store_rows16<D, F16>(acc, a.scale, smem + wave * 32 * ROWB, rw, [&](int r) {
       const int p = p0 + wave * 32 + r;
       const int i = div_group(p, a.s), hl = p - i * G;
-      return p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D) * 2) : DROP_ROW;
-    });
+      return p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2) : DROP_ROW;
+    }, dg);
   }
 }
 
@@ -332,7 +335,7 @@ void bwd_dq_kernel(const BwdArgs a) {
 // therefore fp16 (for bf16 inputs, the copy the dQ kernel wrote; exact for
 // inputs inside fp16's range) and K, used for S, is converted likewise.  Q,
 // dO and the row statistics reach LDS by DMA, double buffered.
-template <int D, bool F16>
+template <int D, bool F16, bool PAD>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
@@ -380,11 +383,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     pb_end = ((q_hi + 1) * G - 1) / BM + 1;
   }
 
-  const int64_t qrow = (int64_t)a.s.hq * D, krow = (int64_t)a.s.hkv * D;
-  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * D;
-  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 2) : 0u;
-  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
-  const uint32_t kbytes = (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2);
+  // In memory a head holds dg <= D values (PAD: a run-time dg < D); the tile
+  // columns past dg are zero.
+  const int dg = PAD ? a.s.dg : D;
+  const int64_t qrow = (int64_t)a.s.hq * dg, krow = (int64_t)a.s.hkv * dg;
+  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * dg;
+  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * dg) * 2) : 0u;
+  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * dg;
+  const uint32_t kbytes = (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2);
   const i32x4 rq16 = make_rsrc_words((F16 ? (const uint16_t*)a.q : (const uint16_t*)a.q16) + qbase_e, qbytes);
   const i32x4 rdo = make_rsrc_words((const uint16_t*)a.dout + qbase_e, qbytes);
   const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
@@ -403,7 +409,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int slab = wave * SLABS + n;
       const int byte = slab * 1024 + lane * 16;
       const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      dma_lds16(rv, v_lds + slab * 1024, (uint32_t)((((int64_t)(j0 + r)) * krow + (pos ^ swz<D>(r)) * 8) * 2));
+      dma_lds16(rv, v_lds + slab * 1024, chunk_off((uint32_t)((int64_t)(j0 + r) * krow * 2), pos ^ swz<D>(r), dg));
     }
   }
   // this wave's 32 keys as the B operand of S (lane: key, 8 dims per k-step), fp16
@@ -413,7 +419,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const uint32_t ko = (uint32_t)((int64_t)my_key * krow * 2);
 #pragma unroll
     for (int s = 0; s < KS; s++) {
-      const u32x4 k = buf_load16(rk, ko + (uint32_t)((16 * s + 8 * hh) * 2));
+      const u32x4 k = buf_load16(rk, chunk_off(ko, 2 * s + hh, dg));
       kf[s] = F16 ? k : bf16x8_to_f16x8(k);
     }
   }
@@ -429,7 +435,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
       const int p = pb * BM + r;
       const int i = div_group(p, a.s), hl = p - i * G;
-      dma_lds16(rs, dst + slab * 1024, (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + (pos ^ swz<D>(r)) * 8) * 2));
+      dma_lds16(rs, dst + slab * 1024, chunk_off((uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2), pos ^ swz<D>(r), dg));
     }
   };
   auto do_fetch = [&](int pb, int buf) __attribute__((always_inline)) {
@@ -565,15 +571,16 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int kk = j0 + wave * 32 + r;
       return kk < si.lk ? (uint32_t)((int64_t)kk * krow * 2) : DROP_ROW;
     };
-    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes), row_off);
-    store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes), row_off);
+    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes), row_off, dg);
+    store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes), row_off, dg);
   } else if (my_key < si.lk) {
-    const int64_t ob = ((int64_t)(si.k0 + my_key) * a.s.hkv + g) * D;
+    const int64_t ob = ((int64_t)(si.k0 + my_key) * a.s.hkv + g) * dg;
 #pragma unroll
     for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int dd = d * 32 + 8 * j4 + 4 * hh;
+        if (dd >= dg) continue;  // zero tile columns past the head dim
         *(f32x4*)((float*)a.dk + ob + dd) = f32x4{dk[d][4 * j4] * a.scale, dk[d][4 * j4 + 1] * a.scale,
                                                   dk[d][4 * j4 + 2] * a.scale, dk[d][4 * j4 + 3] * a.scale};
         *(f32x4*)((float*)a.dv + ob + dd) = f32x4{dv[d][4 * j4], dv[d][4 * j4 + 1], dv[d][4 * j4 + 2], dv[d][4 * j4 + 3]};
@@ -590,19 +597,25 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   if (a.total_ctas_q > 0) {
     timing_begin(K_BWD_DQ, st);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, F16>), dim3(a.total_ctas_q), dim3(THREADS), 0, st, a);
+    if (a.s.dg == D)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, F16, false>), dim3(a.total_ctas_q), dim3(THREADS), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, F16, true>), dim3(a.total_ctas_q), dim3(THREADS), 0, st, a);
     timing_end(K_BWD_DQ, st);
   }
   if (a.total_ctas > 0) {
     timing_begin(K_BWD_DKDV, st);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    if (a.s.dg == D)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
     timing_end(K_BWD_DKDV, st);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool f16, hipStream_t st) {
-  if (head_dim == 128) return f16 ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
+hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st) {
+  if (tile_d == 128) return f16 ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
   return f16 ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
 }
 

@@ -132,12 +132,19 @@ __device__ __forceinline__ constexpr int tile_off(int r, int chunk) {  // byte o
 // rows: the wave's 32 rows go to `stage` (32 rows x 2D bytes, swizzled like
 // the K/V tiles) and come back 16 bytes per lane.  row_off(r) is the byte
 // offset of row r in the descriptor, or DROP_ROW for a row not to store (the
-// chunk offsets added to it stay past any descriptor's end).  Only this wave
-// touches `stage`.
+// chunk offsets added to it stay past any descriptor's end); only the first
+// dg columns of a row are stored.  Only this wave touches `stage`.
 constexpr uint32_t DROP_ROW = 0x80000000u;
+// Byte offset of 16-byte chunk ch of a row that starts at row_byte, for a
+// tensor whose rows hold dg (a multiple of 8) 16-bit values: a chunk past dg
+// gets DROP_ROW instead, so a buffer load of it reads zero and a store of it
+// is dropped (the zero columns of a tile wider than the head dim).
+__device__ __forceinline__ uint32_t chunk_off(uint32_t row_byte, int ch, int dg) {
+  return ch * 8 < dg ? row_byte + (uint32_t)(ch * 16) : DROP_ROW;
+}
 template <int D, bool F16, class RowOff>
 __device__ __forceinline__ void store_rows16(const f32x16 (&v)[D / 32], float scale, char* stage,
-                                             __amdgpu_buffer_rsrc_t rs, RowOff row_off);
+                                             __amdgpu_buffer_rsrc_t rs, RowOff row_off, int dg);
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes every lane supplies the address of 4 consecutive 16-bit values; lane
@@ -154,7 +161,7 @@ __device__ __forceinline__ u32x4 lds_read16(const void* p) { return *LDS_PTR(con
 
 template <int D, bool F16, class RowOff>
 __device__ __forceinline__ void store_rows16(const f32x16 (&v)[D / 32], float scale, char* stage,
-                                             __amdgpu_buffer_rsrc_t rs, RowOff row_off) {
+                                             __amdgpu_buffer_rsrc_t rs, RowOff row_off, int dg) {
   const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int d = 0; d < D / 32; d++)
@@ -167,7 +174,7 @@ __device__ __forceinline__ void store_rows16(const f32x16 (&v)[D / 32], float sc
 #pragma unroll
   for (int it = 0; it < 32 / (64 / CPR); it++) {
     const int r = it * (64 / CPR) + lane / CPR, ch = lane % CPR;
-    buf_store16(*LDS_PTR(const u32x4, stage + tile_off<D>(r, ch)), rs, row_off(r) + (uint32_t)(ch * 16));
+    buf_store16(*LDS_PTR(const u32x4, stage + tile_off<D>(r, ch)), rs, chunk_off(row_off(r), ch, dg));
   }
 }
 

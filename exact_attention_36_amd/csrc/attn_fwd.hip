@@ -35,7 +35,7 @@
 
 namespace attn {
 
-template <int D, bool F16>
+template <int D, bool F16, bool PAD>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const FwdArgs a) {
   // Two workgroups per CU, each with two K and two V buffers (64 KB of LDS
@@ -112,22 +112,25 @@ void fwd_kernel(const FwdArgs a) {
     }
   }
 
-  const int64_t qrow = (int64_t)a.s.hq * D;   // elements per q/o token
-  const int64_t krow = (int64_t)a.s.hkv * D;  // elements per k/v token
-  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * D;
-  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * D) * 2) : 0u;
-  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * D;
-  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + D) * 2) : 0u;
+  // In memory a head holds dg <= D values (PAD: a run-time dg < D); the tile
+  // columns past dg are zero (their loads read zero, their stores are dropped).
+  const int dg = PAD ? a.s.dg : D;
+  const int64_t qrow = (int64_t)a.s.hq * dg;   // elements per q/o token
+  const int64_t krow = (int64_t)a.s.hkv * dg;  // elements per k/v token
+  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * dg;
+  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * dg) * 2) : 0u;
+  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * dg;
+  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2) : 0u;
   const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
 
   // ---- this lane's query row: p0 + 32 wave + l32
   const int my_p = p0 + 32 * wave + l32;
   const int my_i = div_group(my_p, a.s);
   const int my_hl = my_p - my_i * G;
-  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * D) * 2);
+  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * dg) * 2);
   u32x4 qf[KS];  // Q^T as the B operand: 8 consecutive dims of the row per k-step
 #pragma unroll
-  for (int s = 0; s < KS; s++) qf[s] = buf_load16(rq, qoff + (uint32_t)((16 * s + 8 * hh) * 2));
+  for (int s = 0; s < KS; s++) qf[s] = buf_load16(rq, chunk_off(qoff, 2 * s + hh, dg));
   // Visibility of key j0 + o for this lane's row, o = the key's offset in the
   // tile minus 4 hh:  0 <= o - lo_base + j0 <= span  (unsigned compare).
   int lo_base = band.kmin(my_i) - 4 * hh, span = band.kmax(my_i) - band.kmin(my_i);
@@ -144,7 +147,7 @@ void fwd_kernel(const FwdArgs a) {
   for (int n = 0; n < SLABS; n++) {
     const int byte = (wave * SLABS + n) * 1024 + lane * 16;
     const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-    dma_off[n] = (uint32_t)((r * krow + (pos ^ swz<D>(r)) * 8) * 2);
+    dma_off[n] = chunk_off((uint32_t)(r * krow * 2), pos ^ swz<D>(r), dg);
   }
   // K as the A operand: lane reads row (32 kb + l32), chunk (2 s + hh); the
   // swizzle of row 32 kb + l32 equals that of l32, so kb is a constant offset.
@@ -187,8 +190,8 @@ void fwd_kernel(const FwdArgs a) {
       const int key0 = t * FWD_BN, page = key0 / a.s.page_rows;
       const int64_t phys = page_phys(page);
       const int64_t row0 = phys * a.s.page_rows + (key0 - page * a.s.page_rows);
-      r = make_rsrc_words((const uint16_t*)src + (row0 * a.s.hkv + g) * D,
-                          (uint32_t)(((int64_t)(min(FWD_BN, si.lk - key0) - 1) * krow + D) * 2));
+      r = make_rsrc_words((const uint16_t*)src + (row0 * a.s.hkv + g) * dg,
+                          (uint32_t)(((int64_t)(min(FWD_BN, si.lk - key0) - 1) * krow + dg) * 2));
     } else {
       const uint32_t skip = (uint32_t)t * tile_stride;  // bytes before tile t
       r = make_rsrc_words((const char*)((const uint16_t*)src + kbase_e) + skip, kbytes - skip);
@@ -411,7 +414,7 @@ void fwd_kernel(const FwdArgs a) {
     const int p = p0 + 32 * wave + r;
     const int i = div_group(p, a.s), hl = p - i * G;
     // rows past the work tile fall outside the descriptor (dropped)
-    const uint32_t off = p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * D + ch * 8) * 2) : DROP_ROW;
+    const uint32_t off = p < prows ? chunk_off((uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2), ch, dg) : DROP_ROW;
     buf_store16(v, ro, off);
   }
 }
@@ -455,21 +458,25 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
   }
   float gate = mx == -INFINITY ? 0.f : 1.f;
   if (a.sinks && mx != -INFINITY) gate = 1.f / (1.f + exp2_fast((a.sinks[h] - lse) * LOG2E));
-  uint16_t* ob = (uint16_t*)a.o + ((int64_t)(si.q0 + i) * a.s.hq + h) * D + sub * 4;
-  *(u32x2*)ob = u32x2{pack2<F16>(o[0] * gate, o[1] * gate), pack2<F16>(o[2] * gate, o[3] * gate)};
+  uint16_t* ob = (uint16_t*)a.o + ((int64_t)(si.q0 + i) * a.s.hq + h) * a.s.dg + sub * 4;
+  if (sub * 4 < a.s.dg)  // the head's dg values (tile columns past them are zero)
+    *(u32x2*)ob = u32x2{pack2<F16>(o[0] * gate, o[1] * gate), pack2<F16>(o[2] * gate, o[3] * gate)};
   if (sub == 0) a.lse[((int64_t)seq * a.s.hq + h) * a.s.sq + i] = lse;
 }
 
 template <int D, bool F16>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   timing_begin(K_FWD, st);
-  hipLaunchKernelGGL((fwd_kernel<D, F16>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  if (a.s.dg == D)
+    hipLaunchKernelGGL((fwd_kernel<D, F16, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, F16, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
   timing_end(K_FWD, st);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f16, hipStream_t st) {
-  if (head_dim == 128) return f16 ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);
+hipError_t launch_fwd(const FwdArgs& a, int tile_d, bool f16, hipStream_t st) {
+  if (tile_d == 128) return f16 ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);
   return f16 ? launch_fwd_t<64, true>(a, st) : launch_fwd_t<64, false>(a, st);
 }
 
@@ -484,8 +491,8 @@ static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_combine(const FwdArgs& a, int head_dim, bool f16, hipStream_t st) {
-  if (head_dim == 128) return f16 ? launch_combine_t<128, true>(a, st) : launch_combine_t<128, false>(a, st);
+hipError_t launch_fwd_combine(const FwdArgs& a, int tile_d, bool f16, hipStream_t st) {
+  if (tile_d == 128) return f16 ? launch_combine_t<128, true>(a, st) : launch_combine_t<128, false>(a, st);
   return f16 ? launch_combine_t<64, true>(a, st) : launch_combine_t<64, false>(a, st);
 }
 

@@ -24,6 +24,8 @@ struct SeqArgs {
   int32_t sq, sk;        // per-sequence lengths in batched mode
   int32_t total_q;       // tokens of q (lse row stride in packed mode)
   int32_t hq, hkv, group;
+  int32_t dg;            // head dim of the tensors in memory, a multiple of 8 no larger than the
+                         // kernel's tile D; tile columns past it are zero and never stored
   uint32_t group_magic;  // ceil(2^32 / group) for group >= 2 (fast division, see div_group)
   int32_t causal, wl, wr;  // window bounds, -1 = unbounded
   // KV cache (batched forward only): slot seq uses its first seqused_k[seq]
@@ -80,8 +82,8 @@ void timing_begin(int kid, hipStream_t st);
 void timing_end(int kid, hipStream_t st);
 
 // Launchers (defined in the .hip files).  Return hipGetLastError().
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f16, hipStream_t st);
-hipError_t launch_fwd_combine(const FwdArgs& a, int head_dim, bool f16, hipStream_t st);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool f16, hipStream_t st);
+hipError_t launch_fwd(const FwdArgs& a, int tile_d, bool f16, hipStream_t st);
+hipError_t launch_fwd_combine(const FwdArgs& a, int tile_d, bool f16, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st);
 
 }  // namespace attn
