@@ -8,7 +8,8 @@ Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s
 with HIP events on its own stream; `decode` measures the decode-shaped
 forward (B=32, s_q=16, s_kv=32768, Hq=64, Hkv=8) as K/V HBM GB/s;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
-prefill workload.  `--workload decode` runs only the decode shape.
+prefill workload.  `--workload decode` runs only the decode shape;
+`--workload sweep` and `--workload headdims` print one line per shape.
 """
 from __future__ import annotations
 
@@ -211,6 +212,44 @@ def run_sweep(steps, warmup):
     return rows
 
 
+def run_headdims(steps, warmup):
+    """Head-dim sweep on the causal prefill shape (B=4, H=16, S=2048, bf16):
+    D = 32 ... 256.  A head dim runs on the 64-, 128- or 256-wide kernels, the
+    next width up, with zero tile columns, so `tflops` counts the flops of the
+    real head dim and `tile_tflops` those the MFMA pipe executes at the tile
+    width."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    B, S, H = 4, 2048, 16
+    pairs = visible_pairs(B, S, S, H, True, (-1, -1))
+    rows = []
+    for D in (32, 48, 64, 80, 96, 112, 128, 160, 192, 224, 256):
+        q, k, v, do = synth.device_normal(D, [(B, S, H, D)] * 4)
+        o, lse = ea.attn_fwd(q, k, v, causal=True)
+        for _ in range(warmup):
+            ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+            ea.attn_bwd(q, k, v, o, lse, do, causal=True)
+        torch.cuda.synchronize()
+        ea.attn_timing_enable(True)
+        for _ in range(steps):
+            ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+            ea.attn_bwd(q, k, v, o, lse, do, causal=True)
+        torch.cuda.synchronize()
+        t = {n: ea.attn_timing_read(n)[1] / steps for n in ea._lib.KERNELS}
+        ea.attn_timing_enable(False)
+        fwd_ms = t["fwd"] + t["fwd_combine"]
+        bwd_ms = t["bwd_zero"] + t["bwd_dq"] + t["bwd_dkdv"]
+        tile = 64 if D <= 64 else 128 if D <= 128 else 256
+        rows.append({"D": D, "tile_D": tile, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                     "fwd_tflops": round(4.0 * D * pairs / (fwd_ms * 1e-3) / 1e12, 1),
+                     "tflops": round(14.0 * D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1),
+                     "tile_tflops": round(14.0 * tile * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1)})
+        print(json.dumps(rows[-1]), flush=True)
+        del q, k, v, do, o, lse
+    return rows
+
+
 def cpu_baseline(inp, w, seconds_target=15.0):
     """Time the fp64 oracle on whole (batch, head) slices of the workload."""
     import numpy as np
@@ -323,10 +362,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
-    ap.add_argument("--workload", choices=("step", "decode", "sweep", "power"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "power"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
                          "sweep: context sweep over S = 512..16384 (one JSON line per shape); "
+                         "headdims: causal prefill at D = 32..128 (one JSON line per head dim); "
                          "power: socket power and shader clock (amd-smi) under the step's kernels")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,6 +384,9 @@ def main():
 
     if args.workload == "sweep":
         run_sweep(args.steps, args.warmup)
+        return
+    if args.workload == "headdims":
+        run_headdims(args.steps, args.warmup)
         return
     if args.workload == "power":
         run_power(args.seconds)

@@ -31,9 +31,9 @@ constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Head dim of the kernel tiles that serve head_dim: the next of 64, 128 (the
-// tile columns past head_dim are zero).
-int tile_dim(int head_dim) { return head_dim <= 64 ? 64 : 128; }
+// Head dim of the kernel tiles that serve head_dim: the next of 64, 128, 256
+// (the tile columns past head_dim are zero).
+int tile_dim(int head_dim) { return head_dim <= 64 ? 64 : head_dim <= 128 ? 128 : 256; }
 
 float resolve_scale(const attn_params* p) {
   const float s = p->softmax_scale;
@@ -47,8 +47,6 @@ attn_status check_params(const attn_params* p) {
     return fail(ATTN_EINVAL, "dtype must be ATTN_BF16 or ATTN_FP16 (got %d)", p->dtype);
   if (p->head_dim < 8 || p->head_dim > 256 || p->head_dim % 8)
     return fail(ATTN_EINVAL, "head_dim must be a multiple of 8 in [8, 256] (got %d)", p->head_dim);
-  if (p->head_dim > 128)
-    return fail(ATTN_ENOTSUP, "head_dim %d is valid but not built (built: multiples of 8 up to 128)", p->head_dim);
   if (p->heads_q < 1 || p->heads_kv < 1)
     return fail(ATTN_EINVAL, "heads_q and heads_kv must be >= 1 (got %d, %d)", p->heads_q, p->heads_kv);
   if (p->heads_q % p->heads_kv)

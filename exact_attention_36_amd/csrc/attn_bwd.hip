@@ -53,7 +53,7 @@ __global__ void bwd_zero_kernel(float* p, int n) {
 // reads), P and dS lane-locally from the row's lse' and D, then
 // dQ^T += K^T dS^T with K^T through transposing LDS reads.
 template <int D, bool F16, bool PAD>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void bwd_dq_kernel(const BwdArgs a) {
   constexpr int BM = BWD_QBM;
   constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
@@ -336,7 +336,7 @@ void bwd_dq_kernel(const BwdArgs a) {
 // inputs inside fp16's range) and K, used for S, is converted likewise.  Q,
 // dO and the row statistics reach LDS by DMA, double buffered.
 template <int D, bool F16, bool PAD>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
   constexpr int BN = BWD_BN, BM = BWD_BM;
@@ -615,6 +615,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st) {
+  if (tile_d == 256) return f16 ? launch_bwd_t<256, true>(a, st) : launch_bwd_t<256, false>(a, st);
   if (tile_d == 128) return f16 ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
   return f16 ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
 }

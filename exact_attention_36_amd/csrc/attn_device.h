@@ -115,10 +115,12 @@ __device__ __forceinline__ void dma_lds16(i32x4 rsrc, const void* lds_base, uint
 // position c ^ swz(r).  The two access patterns of the kernels -- 16 lanes
 // reading one chunk of 16 consecutive rows, and the transposing read of 4
 // consecutive rows x 4 consecutive chunks by 32 lanes -- then touch every
-// one of the 64 banks exactly once.
+// one of the 64 banks exactly once.  A 256-wide row (512 bytes) spans the
+// banks twice, like a 128-wide row spans them once, so it takes the same
+// swizzle of the low four chunk bits.
 template <int D>
 __device__ __forceinline__ constexpr int swz(int r) {
-  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  if constexpr (D >= 128) return 4 * (r & 3) + ((r >> 2) & 3);
   else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 template <int D>

@@ -36,7 +36,7 @@
 namespace attn {
 
 template <int D, bool F16, bool PAD>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void fwd_kernel(const FwdArgs a) {
   // Two workgroups per CU, each with two K and two V buffers (64 KB of LDS
   // for D = 128).  The waits and loads below are written for NST buffers.
@@ -476,6 +476,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int tile_d, bool f16, hipStream_t st) {
+  if (tile_d == 256) return f16 ? launch_fwd_t<256, true>(a, st) : launch_fwd_t<256, false>(a, st);
   if (tile_d == 128) return f16 ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);
   return f16 ? launch_fwd_t<64, true>(a, st) : launch_fwd_t<64, false>(a, st);
 }
@@ -492,6 +493,7 @@ static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fwd_combine(const FwdArgs& a, int tile_d, bool f16, hipStream_t st) {
+  if (tile_d == 256) return f16 ? launch_combine_t<256, true>(a, st) : launch_combine_t<256, false>(a, st);
   if (tile_d == 128) return f16 ? launch_combine_t<128, true>(a, st) : launch_combine_t<128, false>(a, st);
   return f16 ? launch_combine_t<64, true>(a, st) : launch_combine_t<64, false>(a, st);
 }

@@ -14,6 +14,11 @@ constexpr int FWD_BN = 64;      // keys per K/V tile
 constexpr int BWD_BN = 128;     // keys per backward workgroup
 constexpr int BWD_BM = 32;      // packed query rows per backward step
 constexpr int THREADS = 256;    // 4 wave64s
+// Waves per SIMD the kernels of tile width D are built for: two up to 128
+// (256 registers per lane each), one at 256, whose Q, O and K fragments need
+// up to 512 (the MFMA accumulators then sit in AGPRs) and whose K/V tiles
+// take 128 KB of LDS, one workgroup per CU.
+constexpr int waves_per_simd(int D) { return D > 128 ? 1 : 2; }
 
 // Sequence geometry shared by all kernels.  Batched problems have
 // cu_q == nullptr: sequence b starts at token b*sq (queries) and b*sk (keys).

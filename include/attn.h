@@ -10,9 +10,8 @@
  * Tiling)" and 6 "Flash Attention Backward Pass").
  *
  * Semantics (all four entry points):
- *  - Inputs are bf16 or fp16, head dim a multiple of 8 up to 128 (fa4-jax
- *    page, restrictions paragraph, allows multiples of 8 up to 256; this
- *    build covers those up to 128).
+ *  - Inputs are bf16 or fp16, head dim a multiple of 8 up to 256 (fa4-jax
+ *    page, restrictions paragraph).
  *  - Grouped-query attention: heads_q % heads_kv == 0 and q head h reads kv
  *    head h / (heads_q / heads_kv) (flash_attn_func docstring, 6/2-head
  *    example, vllm-project/flash-attention README on the GitHub search page;
@@ -74,8 +73,8 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_EINVAL = 1,   /* bad argument: null pointer, bad shape, Hq % Hkv != 0,
                           window < -1, workspace too small, bad dtype */
-    ATTN_ENOTSUP = 2,  /* valid request outside this build: head dim above 128,
-                          sizes whose byte offsets exceed 2^31 */
+    ATTN_ENOTSUP = 2,  /* valid request outside this build: sizes whose byte
+                          offsets exceed 2^31, more than 128 q heads per kv head */
     ATTN_EHIP = 3      /* the HIP runtime reported an error at launch */
 } attn_status;
 
@@ -83,10 +82,10 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1, ATTN_FP32 = 2 } attn_dtype;
 
 typedef struct {
     int32_t dtype;          /* ATTN_BF16 or ATTN_FP16: q, k, v, o, dout */
-    int32_t head_dim;       /* D: a multiple of 8 in [8, 128] (the pages allow up to
-                               256: 136..256 return ATTN_ENOTSUP); a head dim below
-                               64 (128) runs on the 64 (128) kernels with zero
-                               columns, so it costs what 64 (128) costs */
+    int32_t head_dim;       /* D: a multiple of 8 in [8, 256].  Kernels are built
+                               64, 128 and 256 wide; a smaller head dim runs on
+                               the next width up with zero columns, so it costs
+                               what that width costs */
     int32_t heads_q;        /* Hq */
     int32_t heads_kv;       /* Hkv, divides Hq */
     float softmax_scale;    /* <= 0 or NaN selects 1/sqrt(D) */

@@ -1,6 +1,6 @@
-"""GPU parity for head dims other than 64 and 128: any multiple of 8 up to 128
-runs on the 64- or 128-wide kernels, whose tile columns past the head dim are
-zero on load and never stored (fa4-jax page, restrictions paragraph: head
+"""GPU parity across head dims: kernels are built 64, 128 and 256 wide, and
+any multiple of 8 up to 256 runs on the next width up, whose tile columns past
+the head dim are zero on load and never stored (fa4-jax page, restrictions paragraph: head
 dims that are multiples of 8).  Each case is checked against the fp64 oracle,
 forward and backward, batched, packed and from a KV cache; and the padded
 kernels must equal, bit for bit, the unpadded kernels run on inputs that carry
@@ -30,6 +30,13 @@ BATCHED = [
     ("d120_fp16_sinks", 1, 129, 129, 2, 2, 120, True, (-1, -1), True, "fp16"),
     # split-KV forward (decode shape): partials and combine with a padded head
     ("d80_decode_split", 2, 3, 5000, 8, 2, 80, True, (-1, -1), True, "bf16"),
+    # the 256-wide kernels (one wave per SIMD), exact and padded
+    ("d256_causal_gqa_sinks", 2, 200, 200, 4, 2, 256, True, (-1, -1), True, "bf16"),
+    ("d256_two_sided_fp16", 1, 257, 190, 2, 2, 256, False, (20, 13), False, "fp16"),
+    ("d192_sq_lt_sk_window", 2, 150, 333, 4, 1, 192, True, (64, 0), False, "bf16"),
+    ("d136_sq_gt_sk", 1, 333, 150, 4, 4, 136, True, (-1, -1), True, "bf16"),
+    ("d160_decode_split", 2, 3, 5000, 8, 2, 160, True, (-1, -1), True, "bf16"),
+    ("d256_decode_split_fp16", 1, 4, 3000, 32, 1, 256, True, (-1, -1), False, "fp16"),
 ]
 
 
@@ -67,6 +74,8 @@ VARLEN = [
     # id, lens_q, lens_k, hq, hkv, d, causal, window, sinks, dtype
     ("varlen_d24_gqa_sinks", [0, 17, 283, 1, 77], None, 4, 2, 24, True, (-1, -1), True, "bf16"),
     ("varlen_d104_mixed", [5, 0, 130, 64, 9], [200, 3, 130, 0, 9], 2, 2, 104, True, (50, 0), False, "fp16"),
+    ("varlen_d256_gqa", [33, 190, 1, 0], [64, 190, 300, 5], 6, 2, 256, True, (-1, -1), True, "bf16"),
+    ("varlen_d200_noncausal", [5, 130, 64], None, 2, 1, 200, False, (-1, -1), False, "bf16"),
 ]
 
 
@@ -100,6 +109,8 @@ KVCACHE = [
     # id, B, sq, hq, hkv, d, lens, capacity, page, causal, window, sinks, dtype
     ("kv_d80_paged64_split", 2, 4, 8, 2, 80, [5000, 700], 5056, 64, True, (-1, -1), True, "bf16"),
     ("kv_d96_contig_q1", 4, 1, 8, 1, 96, [4096, 1, 0, 2000], 4096, 0, True, (-1, -1), False, "fp16"),
+    ("kv_d256_paged256_split", 2, 8, 8, 1, 256, [6000, 257], 6144, 256, True, (-1, -1), True, "bf16"),
+    ("kv_d192_contig", 3, 5, 4, 2, 192, [700, 313, 1], 700, 0, True, (-1, -1), False, "bf16"),
 ]
 
 
@@ -123,14 +134,15 @@ def test_headdim_kvcache_matches_oracle(case):
     assert_lse(name + ".lse", host(lse).transpose(1, 0, 2).reshape(hq, B * sq), ref["lse"])
 
 
-@pytest.mark.parametrize("d,dt", [(8, "bf16"), (48, "fp16"), (72, "bf16"), (120, "bf16")])
+@pytest.mark.parametrize("d,dt", [(8, "bf16"), (48, "fp16"), (72, "bf16"), (120, "bf16"), (136, "bf16"),
+                                  (192, "fp16"), (248, "bf16")])
 def test_padded_equals_explicit_zero_columns(d, dt):
     """A head dim d < D on the D-wide kernels equals, bitwise, the D-wide
     kernels on the same tensors with the zero columns written out (same
     scale): outputs, lse, dQ, dK and dV, with zero gradients in the extra
     columns of the explicit call.  Causal GQA with sinks, batched and split-KV."""
     print("case pad", d, dt, flush=True)
-    D = 64 if d <= 64 else 128
+    D = 64 if d <= 64 else 128 if d <= 128 else 256
     for B, sq, sk in ((2, 190, 190), (1, 3, 4000)):
         inp = synth.batched_inputs(d + sq, B, sq, sk, 8, 2, d, grads=True, sinks=True, dtype=dt)
         q, k, v, do = (dev_tensor(inp[n], dt) for n in ("q", "k", "v", "dout"))
