@@ -11,6 +11,10 @@ marshals arrays and sums the per-row sink terms:
 * ``dsink_h = -sum over rows of (1 - gate_i) * D_i`` -- the sink is a logit
   with no value, so its gradient is minus its softmax share times D_i
   (dew-flash-attn page, sinks paragraph, differentiated by the chain rule).
+  With several sinks per head (ejkernel flash_attention API page,
+  softmax_aux [num_heads, num_sinks] or [num_sinks]) sink k of head h takes
+  the share exp(s_hk) / sum_k' exp(s_hk') of that sum, and sinks shared by
+  all heads sum their per-head gradients.
 """
 from __future__ import annotations
 
@@ -48,6 +52,7 @@ class _Problem(ctypes.Structure):
         ("k_start", ctypes.c_void_p), ("k_len", ctypes.c_void_p),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("dout", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+        ("softcap", ctypes.c_double), ("alibi", ctypes.c_void_p), ("num_sinks", ctypes.c_int64),
     ]
 
 
@@ -84,8 +89,10 @@ class Problem:
     """An attention problem in token-major packed form.
 
     q: [Tq, Hq, D] raw bf16/fp16 bits (uint16) or float64 values (dtype
-    "f64"); k, v: [Tk, Hkv, D]; dout: [Tq, Hq, D] or None; sinks: [Hq] or
-    None (widened to float64).
+    "f64"); k, v: [Tk, Hkv, D]; dout: [Tq, Hq, D] or None; sinks: [Hq],
+    [Hq, n] or, with sinks_shared, [n] (one row for every head), or None
+    (widened to float64); softcap: > 0 caps the logits; alibi: ALiBi slopes
+    [Hq] or [nseq, Hq], or None.
     Sequence s occupies q tokens [q_start[s], q_start[s]+q_len[s]) and
     k/v tokens [k_start[s], k_start[s]+k_len[s]).
     """
@@ -102,6 +109,9 @@ class Problem:
     dout: np.ndarray | None = None
     sinks: np.ndarray | None = None
     dtype: str = "bf16"
+    softcap: float = 0.0
+    alibi: np.ndarray | None = None
+    sinks_shared: bool = False
     _keep: list = field(default_factory=list, repr=False)
 
     @property
@@ -120,6 +130,15 @@ class Problem:
     def nseq(self):
         return len(self.q_len)
 
+    def sink_table(self):
+        """The sinks as [Hq, n] float64 (n sinks per q head), or None."""
+        if self.sinks is None:
+            return None
+        s = np.asarray(self.sinks, np.float64)
+        if self.sinks_shared:
+            return np.broadcast_to(s.reshape(1, -1), (self.hq, s.size))
+        return s.reshape(self.hq, -1)
+
     def _struct(self):
         et = np.float64 if self.dtype == "f64" else np.uint16
         arrs = dict(
@@ -131,7 +150,9 @@ class Problem:
             k_start=np.ascontiguousarray(self.k_start, dtype=np.int64),
             k_len=np.ascontiguousarray(self.k_len, dtype=np.int64),
             dout=None if self.dout is None else np.ascontiguousarray(self.dout, dtype=et),
-            sinks=None if self.sinks is None else np.ascontiguousarray(self.sinks, dtype=np.float64),
+            sinks=None if self.sinks is None else np.ascontiguousarray(self.sink_table()),
+            alibi=None if self.alibi is None else np.ascontiguousarray(
+                np.broadcast_to(np.asarray(self.alibi, np.float64).reshape(-1, self.hq), (self.nseq, self.hq))),
         )
         self._keep = list(arrs.values())
         s = _Problem()
@@ -140,13 +161,16 @@ class Problem:
         s.window_left, s.window_right = int(self.window[0]), int(self.window[1])
         s.nseq, s.hq, s.hkv, s.d = self.nseq, self.hq, self.hkv, self.d
         s.scale = float(self.scale)
-        for name in ("q_start", "q_len", "k_start", "k_len", "q", "k", "v", "dout", "sinks"):
+        for name in ("q_start", "q_len", "k_start", "k_len", "q", "k", "v", "dout", "sinks", "alibi"):
             setattr(s, name, _ptr(arrs[name]))
+        s.softcap = float(self.softcap)
+        s.num_sinks = 0 if self.sinks is None else arrs["sinks"].shape[1]
         return s
 
 
-def batched(q, k, v, scale, causal=False, window=(-1, -1), dout=None, sinks=None, dtype="bf16"):
-    """Wrap [B,S,H,D] uint16 arrays as a Problem (sequence b starts at token b*S)."""
+def batched(q, k, v, scale, causal=False, window=(-1, -1), dout=None, sinks=None, dtype="bf16", **variants):
+    """Wrap [B,S,H,D] uint16 arrays as a Problem (sequence b starts at token b*S).
+    ``variants``: softcap, alibi, sinks_shared (see Problem)."""
     B, sq, hq, d = q.shape
     sk = k.shape[1]
     return Problem(
@@ -155,21 +179,21 @@ def batched(q, k, v, scale, causal=False, window=(-1, -1), dout=None, sinks=None
         q_start=np.arange(B, dtype=np.int64) * sq, q_len=np.full(B, sq, np.int64),
         k_start=np.arange(B, dtype=np.int64) * sk, k_len=np.full(B, sk, np.int64),
         scale=scale, causal=causal, window=window,
-        dout=None if dout is None else dout.reshape(B * sq, hq, d), sinks=sinks, dtype=dtype)
+        dout=None if dout is None else dout.reshape(B * sq, hq, d), sinks=sinks, dtype=dtype, **variants)
 
 
 def varlen(q, k, v, cu_q, cu_k, scale, causal=False, window=(-1, -1), dout=None, sinks=None,
-           dtype="bf16"):
+           dtype="bf16", **variants):
     """Wrap packed [T,H,D] arrays plus int cu_seqlens [N+1] as a Problem."""
     cu_q = np.asarray(cu_q, np.int64)
     cu_k = np.asarray(cu_k, np.int64)
     return Problem(q=q, k=k, v=v, q_start=cu_q[:-1], q_len=np.diff(cu_q),
                    k_start=cu_k[:-1], k_len=np.diff(cu_k), scale=scale, causal=causal,
-                   window=window, dout=dout, sinks=sinks, dtype=dtype)
+                   window=window, dout=dout, sinks=sinks, dtype=dtype, **variants)
 
 
 def kvcache(q, k_cache, v_cache, cache_seqlens, scale, block_table=None, causal=False, window=(-1, -1),
-            sinks=None, dtype="bf16"):
+            sinks=None, dtype="bf16", **variants):
     """A forward over a KV cache as a Problem.  Slot b's queries q[b] attend to
     the first cache_seqlens[b] keys of its slot, the band aligned to that used
     length (fa4-jax page, varlen semantics paragraph: seqused_k).  Without a
@@ -195,7 +219,7 @@ def kvcache(q, k_cache, v_cache, cache_seqlens, scale, block_table=None, causal=
     return Problem(q=q.reshape(B * sq, hq, d), k=kf[idx], v=vf[idx],
                    q_start=np.arange(B, dtype=np.int64) * sq, q_len=np.full(B, sq, np.int64),
                    k_start=np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64), k_len=lens,
-                   scale=scale, causal=causal, window=window, sinks=sinks, dtype=dtype)
+                   scale=scale, causal=causal, window=window, sinks=sinks, dtype=dtype, **variants)
 
 
 def visible(causal, left, right, lq, lk, i, j) -> bool:
@@ -271,7 +295,8 @@ def full(p: Problem, grads: bool = True):
 
     Returns dict: o [Tq,Hq,D], lse [Hq,Tq] (the packed layout; a batched
     caller reshapes), and with grads dq [Tq,Hq,D], dk, dv [Tk,Hkv,D],
-    dsinks [Hq] (zeros when p.sinks is None).
+    dsinks in the layout of p.sinks ([Hq], [Hq, n] or shared [n]; zeros [Hq]
+    when p.sinks is None).
     """
     Tq, Tk = p.q.shape[0], p.k.shape[0]
     seqs, heads, rws, toks = [], [], [], []
@@ -285,7 +310,8 @@ def full(p: Problem, grads: bool = True):
     out = dict(o=np.zeros((Tq, p.hq, p.d)), lse=np.full((p.hq, Tq), np.nan))
     if grads:
         out.update(dq=np.zeros((Tq, p.hq, p.d)), dk=np.zeros((Tk, p.hkv, p.d)),
-                   dv=np.zeros((Tk, p.hkv, p.d)), dsinks=np.zeros(p.hq))
+                   dv=np.zeros((Tk, p.hkv, p.d)),
+                   dsinks=np.zeros(p.hq) if p.sinks is None else np.zeros(np.shape(p.sinks)))
     if not seqs:
         return out
     r = rows(p, seqs, heads, rws, grads=grads)
@@ -297,7 +323,13 @@ def full(p: Problem, grads: bool = True):
         return out
     out["dq"][toks, heads] = r["dq"]
     if p.sinks is not None:
-        np.add.at(out["dsinks"], heads, -(1.0 - r["gate"]) * r["delta"])
+        per_head = np.zeros(p.hq)
+        np.add.at(per_head, heads, -(1.0 - r["gate"]) * r["delta"])
+        tab = p.sink_table()
+        share = np.exp(tab - tab.max(axis=1, keepdims=True))
+        share /= share.sum(axis=1, keepdims=True)
+        per_sink = per_head[:, None] * share  # [Hq, n]
+        out["dsinks"] = (per_sink.sum(axis=0) if p.sinks_shared else per_sink).reshape(np.shape(p.sinks))
     G = p.hq // p.hkv
     for s in range(p.nseq):
         lq, lk = int(p.q_len[s]), int(p.k_len[s])

@@ -35,11 +35,24 @@
  *     denominator with no value, so the output is scaled by
  *     sigmoid(lse - s_h) (dew-flash-attn page, sinks paragraph); the
  *     returned lse is the sink-free one;
+ *   - several sinks per q head (ejkernel flash_attention API page, the
+ *     softmax_aux parameter, one row of sink logits per head): each is one
+ *     more value-less logit in the denominator, so the gate becomes
+ *     1 / (1 + sum_k exp(s_hk - lse));
+ *   - score variants, applied to the scaled logit x = scale <q_i, k_j> in
+ *     this order: the soft cap x -> cap * tanh(x / cap) (the softcapping of
+ *     the vllm-project/flash-attention README, "2.6: Softcapping", and the
+ *     logits_soft_cap parameter of the ejkernel page; the pages name it
+ *     without a formula, and the tanh form is the plain reading), then the
+ *     ALiBi bias -slope_h * |i + Lk - Lq - j| (alibi_slopes in the
+ *     flash_attn_func docstring of the same README), one slope per q head,
+ *     optionally per sequence;
  *   - gradients by the chain rule of the above (tutorial section 6
  *     "Flash Attention Backward Pass": dV = P^T dO, D_i = dO_i . O_i,
- *     dS = P o (dP - D), dQ = dS K, dK = dS^T Q), with the factor `scale`
- *     that the logits carry restored on dQ and dK, and the sink's gradient
- *     -(1 - g_i) D_i summed over rows.
+ *     dS = P o (dP - D), dQ = dS K, dK = dS^T Q), with the derivative of
+ *     the logit with respect to <q_i, k_j> (scale, times 1 - tanh^2 under
+ *     the soft cap; the bias does not depend on q or k) restored on dQ and
+ *     dK, and the sink's gradient -(1 - g_i) D_i summed over rows.
  *
  * Inputs are the raw 16-bit encodings of bf16 or fp16 tensors (or plain
  * doubles, for finite-difference checks), token-major [token][head][dim];
@@ -71,7 +84,10 @@ typedef struct {
     const void *k;          /* [tokens_k][hkv][d] */
     const void *v;          /* [tokens_k][hkv][d] */
     const void *dout;       /* [tokens_q][hq][d], may be NULL */
-    const double *sinks;    /* [hq] or NULL */
+    const double *sinks;    /* [hq][num_sinks] or NULL */
+    double softcap;         /* > 0: soft cap of the logits; 0: none */
+    const double *alibi;    /* [nseq][hq] ALiBi slopes or NULL */
+    int64_t num_sinks;      /* sinks per q head (values < 1 count as 1) */
 } oracle_problem;
 
 /* ---- exact decoding of the 16-bit input formats ---- */
@@ -125,6 +141,35 @@ int oracle_visible(int32_t causal, int64_t left, int64_t right,
     return 1;
 }
 
+/* ---- the logit of one (query, key) pair ---- */
+
+/*
+ * Logit of query i and key j of sequence s (Lq queries, Lk keys), q head h,
+ * from qk = <q_i, k_j>; *dx receives d(logit)/d(qk).
+ */
+static double logit(const oracle_problem *p, int64_t s, int64_t h, int64_t lq, int64_t lk,
+                    int64_t i, int64_t j, double qk, double *dx)
+{
+    double x = p->scale * qk, d = p->scale;
+    if (p->softcap > 0.0) {
+        const double t = tanh(x / p->softcap);
+        x = p->softcap * t;
+        d *= 1.0 - t * t;
+    }
+    if (p->alibi) x -= p->alibi[s * p->hq + h] * fabs((double)(i + lk - lq - j));
+    if (dx) *dx = d;
+    return x;
+}
+
+/* sum_k exp(s_hk - l): the sinks' share of the denominator relative to exp(l) */
+static double sink_terms(const oracle_problem *p, int64_t h, double l)
+{
+    const int64_t n = p->num_sinks < 1 ? 1 : p->num_sinks;
+    double acc = 0.0;
+    for (int64_t k = 0; k < n; k++) acc += exp(p->sinks[h * n + k] - l);
+    return acc;
+}
+
 /* ---- one query row: forward, and optionally dQ ---- */
 
 /*
@@ -161,7 +206,7 @@ static void one_row(const oracle_problem *p, int64_t s, int64_t h, int64_t row,
         const int64_t koff = ((p->k_start[s] + j) * p->hkv + g) * D;
         double acc = 0.0;
         for (int64_t c = 0; c < D; c++) acc += q_loc[c] * elem(p, p->k, koff + c);
-        x[j] = p->scale * acc;
+        x[j] = logit(p, s, h, lq, lk, row, j, acc, NULL);
         if (x[j] > m) m = x[j];
         nvis++;
     }
@@ -174,8 +219,8 @@ static void one_row(const oracle_problem *p, int64_t s, int64_t h, int64_t row,
         for (int64_t j = 0; j < lk; j++)
             if (x[j] != -INFINITY) sum += exp(x[j] - m);
         l = m + log(sum);
-        /* 3. sink gate: the sink is one more logit in the denominator */
-        gt = p->sinks ? 1.0 / (1.0 + exp(p->sinks[h] - l)) : 1.0;
+        /* 3. sink gate: each sink is one more logit in the denominator */
+        gt = p->sinks ? 1.0 / (1.0 + sink_terms(p, h, l)) : 1.0;
         /* 4. O = gate * sum_j P_ij v_j */
         for (int64_t j = 0; j < lk; j++) {
             if (x[j] == -INFINITY) continue;
@@ -197,14 +242,19 @@ static void one_row(const oracle_problem *p, int64_t s, int64_t h, int64_t row,
     if (!dq) return;
     for (int64_t c = 0; c < D; c++) dq[c] = 0.0;
     if (nvis == 0) return;
-    /* dS_ij = gate * P_ij * (dP_ij - D_i),  dQ_i = scale * sum_j dS_ij k_j */
+    /* dS_ij = gate * P_ij * (dP_ij - D_i),  dQ_i = sum_j dS_ij x'_ij k_j
+       with x'_ij = d(logit)/d(qk) */
     for (int64_t j = 0; j < lk; j++) {
         if (x[j] == -INFINITY) continue;
         const int64_t kvoff = ((p->k_start[s] + j) * p->hkv + g) * D;
-        double dp = 0.0;
-        for (int64_t c = 0; c < D; c++) dp += do_loc[c] * elem(p, p->v, kvoff + c);
+        double dp = 0.0, qk = 0.0, dx;
+        for (int64_t c = 0; c < D; c++) {
+            dp += do_loc[c] * elem(p, p->v, kvoff + c);
+            qk += q_loc[c] * elem(p, p->k, kvoff + c);
+        }
+        logit(p, s, h, lq, lk, row, j, qk, &dx);
         const double ds = gt * exp(x[j] - l) * (dp - dl);
-        for (int64_t c = 0; c < D; c++) dq[c] += p->scale * ds * elem(p, p->k, kvoff + c);
+        for (int64_t c = 0; c < D; c++) dq[c] += dx * ds * elem(p, p->k, kvoff + c);
     }
 }
 
@@ -260,7 +310,8 @@ int oracle_rows(const oracle_problem *p, int64_t n, const int64_t *seq,
 /*
  * Columns: dK and dV of keys col[0..ncol) of sequence s, kv head g.
  *   dV_j = sum over the group's q heads h and rows i of  gate_i P_ij dO_i
- *   dK_j = scale * sum over h, i of  gate_i P_ij (dP_ij - D_i) q_i
+ *   dK_j = sum over h, i of  x'_ij gate_i P_ij (dP_ij - D_i) q_i
+ * with x'_ij = d(logit)/d(qk).
  * The per-row statistics lse, gate and delta of every row of the group's q
  * heads are inputs ([G][Lq] each, from oracle_rows), so that a column is the
  * plain sum over rows.
@@ -297,11 +348,12 @@ int oracle_cols(const oracle_problem *p, int64_t s, int64_t g, int64_t ncol,
                     qk += elem(p, p->q, qoff + e) * kj[e];
                     dp += elem(p, p->dout, qoff + e) * vj[e];
                 }
-                const double pg = gate_rows[hh * lq + i] * exp(p->scale * qk - l);
+                double dx;
+                const double pg = gate_rows[hh * lq + i] * exp(logit(p, s, h, lq, lk, i, j, qk, &dx) - l);
                 const double ds = pg * (dp - delta_rows[hh * lq + i]);
                 for (int64_t e = 0; e < D; e++) {
                     dvj[e] += pg * elem(p, p->dout, qoff + e);
-                    dkj[e] += p->scale * ds * elem(p, p->q, qoff + e);
+                    dkj[e] += dx * ds * elem(p, p->q, qoff + e);
                 }
             }
         }

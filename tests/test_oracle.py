@@ -177,11 +177,23 @@ def _loss(p):
     dict(lq=[4, 0, 6], lk=[7, 3, 6], hq=4, hkv=2, causal=True, window=(2, -1), sinks=True),
     dict(lq=[9], lk=[4], hq=2, hkv=2, causal=False, window=(1, 1), sinks=True),
     dict(lq=[6, 3], lk=[2, 8], hq=2, hkv=1, causal=True, window=(-1, -1), sinks=True),
+    # score variants: soft cap, ALiBi (per-sequence slopes), several sinks per head
+    dict(lq=[5, 4], lk=[6, 4], hq=2, hkv=1, causal=True, window=(-1, -1), sinks=False, softcap=0.7),
+    dict(lq=[7], lk=[5], hq=4, hkv=2, causal=False, window=(-1, -1), sinks=False, alibi=True),
+    dict(lq=[4, 6], lk=[6, 6], hq=2, hkv=2, causal=True, window=(3, -1), sinks=3, softcap=1.3, alibi=True),
+    dict(lq=[5], lk=[5], hq=2, hkv=1, causal=False, window=(-1, -1), sinks="shared3"),
 ])
 def test_gradients_match_finite_differences(case):
     rng = np.random.default_rng(5)
     p = _f64_problem(rng, case["lq"], case["lk"], case["hq"], case["hkv"], 4,
-                     causal=case["causal"], window=case["window"], sinks=case["sinks"])
+                     causal=case["causal"], window=case["window"], sinks=case["sinks"] is True)
+    if case["sinks"] == 3:
+        p.sinks = rng.standard_normal((case["hq"], 3))
+    elif case["sinks"] == "shared3":
+        p.sinks, p.sinks_shared = rng.standard_normal(3), True
+    p.softcap = case.get("softcap", 0.0)
+    if case.get("alibi"):
+        p.alibi = rng.uniform(0.05, 0.6, (len(case["lq"]), case["hq"]))
     r = oracle.full(p)
     h = 1e-5
     for name, grad in (("q", r["dq"]), ("k", r["dk"]), ("v", r["dv"])):
@@ -198,15 +210,16 @@ def test_gradients_match_finite_differences(case):
         scale = max(1.0, np.abs(fd).max())
         assert np.abs(fd - grad).max() <= 1e-6 * scale, name
     if case["sinks"]:
-        fd = np.zeros(p.hq)
-        for hh in range(p.hq):
-            old = p.sinks[hh]
-            p.sinks[hh] = old + h
+        fd = np.zeros(p.sinks.shape)
+        for idx in np.ndindex(p.sinks.shape):
+            old = p.sinks[idx]
+            p.sinks[idx] = old + h
             lp = _loss(p)
-            p.sinks[hh] = old - h
+            p.sinks[idx] = old - h
             lm = _loss(p)
-            p.sinks[hh] = old
-            fd[hh] = (lp - lm) / (2 * h)
+            p.sinks[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        assert r["dsinks"].shape == fd.shape
         assert np.abs(fd - r["dsinks"]).max() <= 1e-6 * max(1.0, np.abs(fd).max())
 
 
@@ -421,3 +434,131 @@ def test_synth_bf16_rounding_is_rne():
     assert got[3] == np.float32(1.015625)  # 1 + 3*2^-8 is a tie: resolved to the even mantissa
     t = torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(got, t)
+
+
+# ---------------------------------------------------------------- T14: score variants
+
+def _one_query(keys, values, softcap):
+    """One query (value 1, D = 1, scale 1) over the given keys and values, f64."""
+    lk = len(keys)
+    one = np.ones((1, 1, 1))
+    return oracle.varlen(one, np.asarray(keys, np.float64).reshape(lk, 1, 1),
+                         np.asarray(values, np.float64).reshape(lk, 1, 1), [0, 1], [0, lk], 1.0,
+                         dout=np.ones((1, 1, 1)), dtype="f64", softcap=softcap)
+
+
+def test_softcap_closed_form():
+    """cap 1, logits ln 2 and ln 3: tanh(ln x) = (x^2 - 1) / (x^2 + 1) gives the
+    capped logits 3/5 and 4/5 exactly, hence O, lse and dq in closed form
+    (dq = P1 P2 ((1 - 0.6^2) ln 2 - (1 - 0.8^2) ln 3) for dO = 1, V = (1, 0))."""
+    p = _one_query([math.log(2.0), math.log(3.0)], [1.0, 0.0], softcap=1.0)
+    r = oracle.full(p)
+    e1, e2 = math.exp(0.6), math.exp(0.8)
+    p1, p2 = e1 / (e1 + e2), e2 / (e1 + e2)
+    np.testing.assert_allclose(r["o"][0, 0, 0], p1, rtol=1e-14)
+    np.testing.assert_allclose(r["lse"][0, 0], math.log(e1 + e2), rtol=1e-14)
+    dq = p1 * p2 * (0.64 * math.log(2.0) - 0.36 * math.log(3.0))
+    np.testing.assert_allclose(r["dq"][0, 0, 0], dq, rtol=1e-12)
+    # dK_j = dS_j x'_j q: dS_1 = P1 (1 - O), dS_2 = P2 (0 - O)
+    np.testing.assert_allclose(r["dk"][:, 0, 0], [p1 * (1 - p1) * 0.64, -p2 * p1 * 0.36], rtol=1e-12)
+
+
+def test_softcap_limits():
+    """A cap far above the logits is no cap; a cap far below them flattens
+    every row to the mean of its visible values with lse = log(count)."""
+    rng = np.random.default_rng(21)
+    base = _f64_problem(rng, [5, 9], [7, 9], 4, 2, 8, causal=True, sinks=True)
+    plain = oracle.full(base)
+    base.softcap = 1e9
+    wide = oracle.full(base)
+    for key in ("o", "lse", "dq", "dk", "dv", "dsinks"):
+        np.testing.assert_allclose(wide[key], plain[key], rtol=1e-9, atol=1e-12)
+    base.softcap, base.sinks = 1e-12, None
+    flat = oracle.full(base, grads=False)
+    G = base.hq // base.hkv
+    for s in range(base.nseq):
+        lq, lk = int(base.q_len[s]), int(base.k_len[s])
+        q0, k0 = int(base.q_start[s]), int(base.k_start[s])
+        for i in range(lq):
+            vis = [j for j in range(lk) if oracle.visible(True, -1, -1, lq, lk, i, j)]
+            for h in range(base.hq):
+                mean = base.v[[k0 + j for j in vis], h // G].mean(axis=0)
+                np.testing.assert_allclose(flat["o"][q0 + i, h], mean, rtol=1e-9, atol=1e-12)
+                # every capped logit lies in [-cap, cap]
+                np.testing.assert_allclose(flat["lse"][h, q0 + i], math.log(len(vis)), rtol=1e-9, atol=2e-12)
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (3, -1)])
+def test_alibi_causal_equals_augmented_head(window):
+    """Under a causal mask |i + Lk - Lq - j| = (i + Lk - Lq) - j, so the ALiBi
+    bias is slope_h * j plus a per-row constant: attention with ALiBi equals
+    plain attention on q' = [q, slope_h / scale], k' = [k, j] (j = key position
+    in its sequence), with lse lower by slope_h * (i + Lk - Lq) and the same O,
+    dV and the first D columns of dQ, dK."""
+    rng = np.random.default_rng(8)
+    lq, lk = [5, 8, 3], [9, 8, 3]
+    p = _f64_problem(rng, lq, lk, 4, 2, 6, causal=True, window=window)
+    slopes = rng.uniform(0.1, 0.9, (3, 4))
+    p.alibi = slopes
+    r = oracle.full(p)
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    qa = np.zeros(p.q.shape[:2] + (7,))
+    ka = np.zeros(p.k.shape[:2] + (7,))
+    qa[..., :6], ka[..., :6] = p.q, p.k
+    for s in range(3):
+        qa[cq[s]:cq[s + 1], :, 6] = slopes[s] / p.scale
+        ka[ck[s]:ck[s + 1], :, 6] = np.arange(lk[s])[:, None]
+    doa = np.zeros(qa.shape)
+    doa[..., :6] = p.dout
+    va = np.zeros(p.v.shape[:2] + (7,))
+    va[..., :6] = p.v
+    aug = oracle.full(oracle.varlen(qa, ka, va, cq, ck, p.scale, causal=True, window=window, dout=doa,
+                                    dtype="f64"))
+    np.testing.assert_allclose(r["o"], aug["o"][..., :6], rtol=1e-10, atol=1e-12)
+    shift = np.zeros_like(r["lse"])
+    for s in range(3):
+        for i in range(lq[s]):
+            shift[:, cq[s] + i] = slopes[s] * (i + lk[s] - lq[s])
+    np.testing.assert_allclose(r["lse"], aug["lse"] - shift, rtol=1e-10, atol=1e-10)
+    for key in ("dq", "dk", "dv"):
+        np.testing.assert_allclose(r[key], aug[key][..., :6], rtol=1e-9, atol=1e-11)
+
+
+def test_alibi_steep_slope_selects_nearest_key():
+    """With a slope far above the logits' spread, each row's softmax sits on
+    the visible key nearest to its diagonal i + Lk - Lq (both sides, no mask)."""
+    rng = np.random.default_rng(9)
+    lq, lk = [7, 3], [4, 9]
+    p = _f64_problem(rng, lq, lk, 2, 1, 5)
+    p.alibi = np.full(2, 60.0)
+    r = oracle.full(p, grads=False)
+    for s in range(2):
+        for i in range(lq[s]):
+            j = min(max(i + lk[s] - lq[s], 0), lk[s] - 1)
+            for h in range(2):
+                np.testing.assert_allclose(r["o"][int(p.q_start[s]) + i, h], p.v[int(p.k_start[s]) + j, 0],
+                                           rtol=1e-9, atol=1e-12)
+
+
+def test_several_sinks_equal_their_logsumexp():
+    """n sinks of a head act as one sink at log sum_k exp(s_hk): the same O,
+    lse and gradients, and each sink's gradient is that one's split by
+    softmax(s_h); sinks shared by the heads sum the heads' gradients."""
+    rng = np.random.default_rng(13)
+    p = _f64_problem(rng, [6, 0, 9], [6, 4, 12], 4, 2, 8, causal=True, window=(4, -1))
+    tab = rng.standard_normal((4, 3)) * 2
+    p.sinks = tab
+    many = oracle.full(p)
+    p.sinks = np.log(np.exp(tab).sum(axis=1))
+    one = oracle.full(p)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_allclose(many[key], one[key], rtol=1e-12, atol=1e-14)
+    share = np.exp(tab) / np.exp(tab).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(many["dsinks"], one["dsinks"][:, None] * share, rtol=1e-12, atol=1e-14)
+    p.sinks, p.sinks_shared = tab[1], True
+    shared = oracle.full(p)
+    p.sinks, p.sinks_shared = np.tile(tab[1], (4, 1)), False
+    tiled = oracle.full(p)
+    np.testing.assert_allclose(shared["o"], tiled["o"], rtol=1e-14)
+    np.testing.assert_allclose(shared["dsinks"], tiled["dsinks"].sum(axis=0), rtol=1e-12)
