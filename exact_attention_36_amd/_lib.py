@@ -43,7 +43,8 @@ class attn_params(ctypes.Structure):
         ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32),
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
-        ("sinks", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p), ("num_sinks", ctypes.c_int32), ("sinks_shared", ctypes.c_int32),
+        ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p), ("alibi_per_batch", ctypes.c_int32),
     ]
 
 
@@ -118,7 +119,23 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=None) -> attn_params:
+def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
+                alibi_slopes=None, sinks_shared=False, nseq=None) -> attn_params:
+    """sinks: fp32 [Hq] (one per head), [Hq, n], or [n] with sinks_shared (one row
+    for every head); alibi_slopes: fp32 [Hq] or [B, Hq]; softcap: 0 = off."""
+    hq = q.shape[-2]
+    if sinks is not None:
+        ok = sinks.dim() == 1 if sinks_shared else (tuple(sinks.shape) == (hq,) or
+                                                    (sinks.dim() == 2 and sinks.shape[0] == hq))
+        if not ok or sinks.dtype != torch.float32 or not sinks.is_contiguous():
+            raise ValueError("sinks must be contiguous fp32 [Hq], [Hq, n] or (shared) [n]; got %s %s"
+                             % (tuple(sinks.shape), sinks.dtype))
+    if alibi_slopes is not None:
+        if (alibi_slopes.shape[-1] != hq or alibi_slopes.dim() not in (1, 2) or
+                (alibi_slopes.dim() == 2 and alibi_slopes.shape[0] != nseq) or
+                alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous()):
+            raise ValueError("alibi_slopes must be contiguous fp32 [Hq] or [%s, Hq]; got %s %s"
+                             % (nseq, tuple(alibi_slopes.shape), alibi_slopes.dtype))
     p = attn_params()
     p.dtype = _dtype_code(q.dtype)
     p.head_dim = q.shape[-1]
@@ -128,6 +145,12 @@ def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(window[0]), int(window[1])
     p.sinks = _ptr(sinks)
+    if sinks is not None:
+        p.sinks_shared = 1 if sinks_shared else 0
+        p.num_sinks = sinks.numel() if sinks_shared else (1 if sinks.dim() == 1 else int(sinks.shape[-1]))
+    p.softcap = float(softcap)
+    p.alibi_slopes = _ptr(alibi_slopes)
+    p.alibi_per_batch = 1 if alibi_slopes is not None and alibi_slopes.dim() == 2 else 0
     return p
 
 
@@ -144,12 +167,14 @@ def _workspace(nbytes, dev):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
 
 
-def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, out=None, lse=None):
+def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
+             alibi_slopes=None, sinks_shared=False, out=None, lse=None):
     """Batched forward: q [B,Sq,Hq,D], k, v [B,Sk,Hkv,D] -> (o, lse [B,Hq,Sq] fp32)."""
     lib = load_library()
     B, sq, hq, d = q.shape
     sk = k.shape[1]
-    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
+                    nseq=B)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, hq, sq), dtype=torch.float32, device=q.device) if lse is None else lse
     n = lib.attn_fwd_workspace_size(ctypes.byref(p), B, sq, sk)
@@ -159,18 +184,20 @@ def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
     return o, lse
 
 
-def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, softmax_scale=None,
+def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
+             alibi_slopes=None, sinks_shared=False,
              grad_dtype=None):
     """Batched backward -> (dq, dk, dv, dsinks or None)."""
     lib = load_library()
     B, sq, hq, d = q.shape
     sk = k.shape[1]
-    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
+                    nseq=B)
     gd = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gd, device=q.device)
     dk = torch.empty(k.shape, dtype=gd, device=q.device)
     dv = torch.empty(v.shape, dtype=gd, device=q.device)
-    dsinks = torch.empty(hq, dtype=torch.float32, device=q.device) if sinks is not None else None
+    dsinks = torch.empty(sinks.shape, dtype=torch.float32, device=q.device) if sinks is not None else None
     n = lib.attn_bwd_workspace_size(ctypes.byref(p), B, sq, sk, _dtype_code(gd))
     ws = _workspace(n, q.device)
     _check(lib.attn_bwd(ctypes.byref(p), B, sq, sk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -180,13 +207,15 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, s
 
 
 def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causal=False, window=(-1, -1),
-                     sinks=None, softmax_scale=None, out=None, lse=None):
+                     sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None, sinks_shared=False, out=None,
+                     lse=None):
     """Forward over a KV cache: q [B,Sq,Hq,D]; cache_seqlens int32 [B] (used keys per slot);
     k_cache, v_cache [B,capacity,Hkv,D], or pages [num_blocks,page,Hkv,D] with
     block_table int32 [B,max_blocks] -> (o, lse [B,Hq,Sq])."""
     lib = load_library()
     B, sq, hq, d = q.shape
-    p = make_params(q, k_cache, causal, window, sinks, softmax_scale)
+    p = make_params(q, k_cache, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
+                    nseq=B)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, hq, sq), dtype=torch.float32, device=q.device) if lse is None else lse
     if block_table is not None:
@@ -202,13 +231,15 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causa
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
-                    window=(-1, -1), sinks=None, softmax_scale=None, out=None, lse=None):
+                    window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None,
+                    sinks_shared=False, out=None, lse=None):
     """Packed forward: q [Tq,Hq,D], k, v [Tk,Hkv,D], int32 cu_seqlens [N+1] -> (o, lse [Hq,Tq])."""
     lib = load_library()
     tq, hq, d = q.shape
     tk = k.shape[0]
     n = cu_seqlens_q.shape[0] - 1
-    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
+                    nseq=n)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device) if lse is None else lse
     nb = lib.attn_fwd_varlen_workspace_size(ctypes.byref(p), n, tq, tk, max_seqlen_q, max_seqlen_k)
@@ -220,18 +251,20 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 
 def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                    causal=False, window=(-1, -1), sinks=None, softmax_scale=None, grad_dtype=None):
+                    causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None,
+                    sinks_shared=False, grad_dtype=None):
     """Packed backward -> (dq, dk, dv, dsinks or None)."""
     lib = load_library()
     tq, hq, d = q.shape
     tk = k.shape[0]
     n = cu_seqlens_q.shape[0] - 1
-    p = make_params(q, k, causal, window, sinks, softmax_scale)
+    p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
+                    nseq=n)
     gd = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gd, device=q.device)
     dk = torch.empty(k.shape, dtype=gd, device=q.device)
     dv = torch.empty(v.shape, dtype=gd, device=q.device)
-    dsinks = torch.empty(hq, dtype=torch.float32, device=q.device) if sinks is not None else None
+    dsinks = torch.empty(sinks.shape, dtype=torch.float32, device=q.device) if sinks is not None else None
     nb = lib.attn_bwd_varlen_workspace_size(ctypes.byref(p), n, tq, tk, max_seqlen_q, max_seqlen_k,
                                             _dtype_code(gd))
     ws = _workspace(nb, q.device)

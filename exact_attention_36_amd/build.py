@@ -11,7 +11,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libattn36.so")
-SOURCES = ["attn_api.cpp", "attn_timing.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.cpp", "attn_timing.cpp", "attn_fwd.hip", "attn_bwd.hip",
+           # one translation unit per score variant, compiled in parallel
+           "attn_fwd_cap.hip", "attn_fwd_alibi.hip", "attn_fwd_cap_alibi.hip",
+           "attn_bwd_cap.hip", "attn_bwd_alibi.hip", "attn_bwd_cap_alibi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -36,7 +39,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, src + ".o")
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+    with ThreadPoolExecutor(max_workers=min(os.cpu_count() or 4, 16, len(cmds))) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     _run([HIPCC, *FLAGS, "-shared", *objs, "-o", tmp])

@@ -27,6 +27,7 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 
 constexpr int64_t OFF_LIMIT = (int64_t)1 << 31;  // byte offsets inside one sequence are 32-bit
 constexpr size_t ALIGN = 256;
+constexpr int MAX_SINKS = 64;  // sinks per q head
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -56,7 +57,32 @@ attn_status check_params(const attn_params* p) {
   if (p->window_left < -1 || p->window_right < -1)
     return fail(ATTN_EINVAL, "window bounds must be >= -1 (got %d, %d)", p->window_left, p->window_right);
   if (p->causal != 0 && p->causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1");
+  if (p->num_sinks < 0 || p->num_sinks > MAX_SINKS)
+    return fail(ATTN_EINVAL, "num_sinks must be in [0, %d] (got %d)", MAX_SINKS, p->num_sinks);
+  if (p->sinks_shared != 0 && p->sinks_shared != 1) return fail(ATTN_EINVAL, "sinks_shared must be 0 or 1");
+  if (!(p->softcap >= 0.f) || std::isinf(p->softcap))
+    return fail(ATTN_EINVAL, "softcap must be finite and >= 0 (got %g)", (double)p->softcap);
+  if (p->alibi_per_batch != 0 && p->alibi_per_batch != 1) return fail(ATTN_EINVAL, "alibi_per_batch must be 0 or 1");
   return ATTN_OK;
+}
+
+// Score variants and the sinks' layout, from the params.
+ScoreArgs score_args(const attn_params* p, float scale) {
+  ScoreArgs x{};
+  x.inv_scale = 1.f / scale;
+  if (p->softcap > 0.f) {
+    x.ext |= EXT_CAP;
+    x.cap_k2 = 2.f * scale * 1.4426950408889634f / p->softcap;
+    x.cap_k3 = p->softcap / scale;
+  }
+  if (p->alibi_slopes) {
+    x.ext |= EXT_ALIBI;
+    x.alibi = p->alibi_slopes;
+    x.alibi_bstride = p->alibi_per_batch ? p->heads_q : 0;
+  }
+  x.nsinks = p->num_sinks < 1 ? 1 : p->num_sinks;
+  x.sink_hstride = p->sinks_shared ? 0 : x.nsinks;
+  return x;
 }
 
 attn_status check_extent(int64_t max_q, int64_t max_k, const attn_params* p) {
@@ -163,6 +189,7 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   a.lse = lse;
   a.sinks = p->sinks;
   a.scale_log2 = resolve_scale(p) * 1.4426950408889634f;
+  a.x = score_args(p, resolve_scale(p));
   const int G = a.s.group;
   a.n_split = 1;
   if (packed) {
@@ -228,6 +255,8 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   const float scale = resolve_scale(p);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.x = score_args(p, scale);
+  a.dsink_count = p->sinks ? (p->sinks_shared ? 1 : p->heads_q) * a.x.nsinks : 0;
   const int64_t G = p->heads_q / p->heads_kv;
   if (packed) {
     a.nblk = (int32_t)(total_k / BWD_BN + nseq);

@@ -1,43 +1,7 @@
-// attn_bwd.hip -- exact-attention backward for gfx950.
-//
-// The probabilities are recomputed tile by tile from the saved log-sum-exp
-// instead of being stored (GitHub search page, gitctrlx/flash-attention-
-// tutorial README, section 6 "Flash Attention Backward Pass"):
-//     P   = exp(scale * Q K^T - lse')        lse' = logaddexp(lse, sink)
-//     dV  = P^T dO
-//     dP  = dO V^T
-//     D_i = <dO_i, O_i>
-//     dS  = P o (dP - D)
-//     dQ  = scale * dS K,    dK = scale * dS^T Q
-// (the scale factor on dQ and dK is the chain rule through the scaled
-// logits).  With sinks, P already carries the sink's share of the
-// denominator (lse' includes the sink), and d(loss)/d(sink_h) is
-// -sum_i (1 - g_i) D_i with g_i = sigmoid(lse_i - sink_h)
-// (dew-flash-attn page, sinks paragraph: the sinks get their gradient from
-// the backward).
-//
-// Kernels, in stream order:
-//   bwd_zero_kernel   clears dsinks
-//   bwd_dq_kernel     query-major: one workgroup per 128 packed query rows
-//                     computes the rows' D_i, lse' (log2 units, with the
-//                     sink) and dsink partials, then
-//                     streams the visible K/V tiles (like the forward),
-//                     recomputes S, P, dP, dS and accumulates dQ in
-//                     registers; dQ is written once, no atomics
-//   bwd_dkdv_kernel   key-major: one workgroup per 128-key block of one kv
-//                     head streams the visible query blocks of all the
-//                     group's q heads, recomputes S, P, dP, dS and
-//                     accumulates dK and dV in registers (fp32 across the
-//                     GQA group: fa4-jax page, restrictions paragraph)
-// The two main kernels recompute S and dP each (7 products per visible
-// block instead of 5) in exchange for no fp32 atomics, no dS exchange
-// through LDS and two waves per SIMD in both.  The packed (varlen) grids
-// cover only the real blocks: sequence i's blocks start at
-// floor(cu[i] * rows / block) + i and a workgroup finds its sequence by
-// binary search (dew-flash-attn page, packed-backward paragraph).
-#include <type_traits>
-
-#include "attn_common.h"
+// attn_bwd.hip -- backward launchers: clearing dsinks, then the dQ and dK/dV
+// kernels of the call's score variant (soft cap / ALiBi instances compile in
+// their own translation units).
+#include "attn_bwd_kernels.h"
 
 namespace attn {
 
@@ -46,578 +10,25 @@ __global__ void bwd_zero_kernel(float* p, int n) {
   if (i < n) p[i] = 0.f;
 }
 
-// ------------------------------------------------------------------ dQ
-// Work tile as in the forward: 128 packed query rows of one kv group, 4 waves
-// of 32 rows; a lane owns one query row (S^T = K Q^T orientation).  Per K/V
-// tile of 64 keys:  S^T = K Q^T,  dP^T = V dO^T  (K, V natural 16-byte LDS
-// reads), P and dS lane-locally from the row's lse' and D, then
-// dQ^T += K^T dS^T with K^T through transposing LDS reads.
-template <int D, bool F16, bool PAD>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
-void bwd_dq_kernel(const BwdArgs a) {
-  constexpr int BM = BWD_QBM;
-  constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
-  constexpr int TILE = FWD_BN * ROWB;
-  constexpr int SLABS = TILE / 1024 / 4;
-  constexpr int KB = FWD_BN / 32, PT = FWD_BN / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int G = a.s.group;
-  int seq, g, mb;
-  if (a.s.cu_q) {
-    const int id = xcd_remap(blockIdx.x, a.total_ctas_q);
-    g = id / a.nblk_q;
-    const int t = id - g * a.nblk_q;
-    seq = find_sequence(a.s.cu_q, a.s.nseq, t, G, BM);
-    mb = t - packed_block_start(a.s.cu_q, seq, G, BM);
-  } else {
-    int grp, rank;
-    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nmb}.decode(blockIdx.x, grp, rank)) return;
-    g = grp % a.s.hkv;
-    seq = grp / a.s.hkv;
-    mb = a.nmb - 1 - rank;  // causal: the longest tiles start first
-  }
-  const SeqInfo si = seq_info(a.s, seq);
-  const int prows = si.lq * G;
-  const int p0 = mb * BM;
-  if (p0 >= prows) return;
-
-  const Band band(a.s, si);
-  const int i_lo = div_group(p0, a.s), i_hi = div_group(min(p0 + BM, prows) - 1, a.s);
-  const int kv_lo = band.kmin(i_lo), kv_hi = band.kmax(i_hi);
-  int t_begin = 0, t_end = 0;
-  if (kv_hi >= kv_lo) {
-    t_begin = kv_lo / FWD_BN;
-    t_end = kv_hi / FWD_BN + 1;
-  }
-  const int full_lo = band.kmin(i_hi), full_hi = band.kmax(i_lo);
-
-  const int my_p = p0 + wave * 32 + l32;
-  const int my_i = div_group(my_p, a.s);
-  const int my_hl = my_p - my_i * G;
-  const int my_h = g * G + my_hl;
-  // this row's keys [kmin, kmin + span] as one unsigned compare (none for a
-  // row that sees no key)
-  int my_kmin = band.kmin(my_i);
-  uint32_t my_kspan = (uint32_t)(band.kmax(my_i) - my_kmin);
-  if (band.kmax(my_i) < my_kmin) {
-    my_kmin = 1 << 30;
-    my_kspan = 0;
-  }
-
-  // In memory a head holds dg <= D values (PAD: a run-time dg < D); the tile
-  // columns past dg are zero.
-  const int dg = PAD ? a.s.dg : D;
-  const int64_t qrow = (int64_t)a.s.hq * dg, krow = (int64_t)a.s.hkv * dg;
-  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * dg;
-  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * dg) * 2) : 0u;
-  const uint32_t qoff = (uint32_t)(((int64_t)my_i * qrow + (int64_t)my_hl * dg) * 2);
-  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * dg;
-  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2) : 0u;
-  const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
-  const auto rdo = make_rsrc((const uint16_t*)a.dout + qbase_e, qbytes);
-
-  u32x4 qf[KS], df[KS];
-#pragma unroll
-  for (int s = 0; s < KS; s++) {
-    qf[s] = buf_load16(rq, chunk_off(qoff, 2 * s + hh, dg));
-    df[s] = buf_load16(rdo, chunk_off(qoff, 2 * s + hh, dg));
-  }
-  // The fp16 copy of Q that the dK/dV kernel stages (bf16 inputs): every
-  // (query, q head) row is in exactly one of these work tiles.
-  if (a.q16) {
-    const auto rq16 = make_rsrc(a.q16 + qbase_e, qbytes);
-#pragma unroll
-    for (int s = 0; s < KS; s++) buf_store16(bf16x8_to_f16x8(qf[s]), rq16, chunk_off(qoff, 2 * s + hh, dg));
-  }
-  // Row statistics, computed here once per (query row, q head) and left in
-  // the workspace for the dK/dV kernel that runs after this one:
-  //   D = rowsum(dO * O), O being the stored (sink-gated) output;
-  //   lse' = log2(2^lse + 2^sink) in log2 units (+inf for an empty row, so
-  //   that P = 0 there);  dsink = -sum_rows (1 - gate) D, gate = sigmoid(lse - sink)
-  //   (dew-flash-attn page, sinks paragraph).
-  float row_d;
-  {
-    const auto ro = make_rsrc((const uint16_t*)a.o + qbase_e, qbytes);
-    float part = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; s++) {
-      const u32x4 ov = buf_load16(ro, chunk_off(qoff, 2 * s + hh, dg));
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), part);
-        part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), to_f32<F16>((uint16_t)(df[s][e] >> 16)), part);
-      }
-    }
-    row_d = half_sum(part);  // the two lanes holding one row's halves
-  }
-  float row_lse2 = INFINITY, dsink_part = 0.f;
-  if (my_p < prows) {
-    const int64_t li = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
-                                : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
-    const float lse = a.lse[li];
-    if (lse != -INFINITY) {
-      row_lse2 = lse * LOG2E;
-      if (a.sinks) {
-        const float s2 = a.sinks[my_h] * LOG2E;
-        const float mx = fmaxf(row_lse2, s2), mn = fminf(row_lse2, s2);
-        dsink_part = -row_d / (1.f + exp2_fast(row_lse2 - s2));
-        row_lse2 = mx + log2_fast(1.f + exp2_fast(mn - mx));
-      }
-    } else {
-      dsink_part = -row_d;  // no visible key: the sink takes the whole denominator
-    }
-    if (hh == 0) {
-      a.delta[li] = row_d;
-      a.lse2[li] = row_lse2;
-    }
-  }
-  if (a.sinks && a.dsinks) {
-    // sum the block's rows per q head in LDS, then one global add per head;
-    // 128 consecutive packed rows hold at most 128 distinct heads, slot
-    // (p - p0) mod G names them without collisions
-    __shared__ float dsink_red[BM];
-    if (threadIdx.x < BM) dsink_red[threadIdx.x] = 0.f;
-    __syncthreads();
-    if (hh == 0 && dsink_part != 0.f) atomicAdd(&dsink_red[(my_p - p0) % G], dsink_part);
-    __syncthreads();
-    if ((int)threadIdx.x < min(G, BM)) {
-      const float v = dsink_red[threadIdx.x];
-      if (v != 0.f) atomicAdd(a.dsinks + g * G + (p0 + (int)threadIdx.x) % G, v);
-    }
-  }
-  const float c = a.scale_log2;
-  const float mlse = row_lse2 == INFINITY ? 0.f : row_lse2;  // empty rows are fully masked
-
-  uint32_t dma_off[SLABS];
-#pragma unroll
-  for (int n = 0; n < SLABS; n++) {
-    const int byte = (wave * SLABS + n) * 1024 + lane * 16;
-    const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-    dma_off[n] = chunk_off((uint32_t)(r * krow * 2), pos ^ swz<D>(r), dg);
-  }
-  int k_off[KS];
-#pragma unroll
-  for (int s = 0; s < KS; s++) k_off[s] = tile_off<D>(l32, 2 * s + hh);
-  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
-  int t_off[DB][2];
-#pragma unroll
-  for (int d = 0; d < DB; d++) {
-    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
-#pragma unroll
-    for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
-  }
-  // (byte offsets inside one sequence's K/V fit in 31 bits)
-  const uint32_t tile_stride = (uint32_t)(FWD_BN * krow * 2);
-  auto load_tile = [&](int t) {
-    const int buf = (t - t_begin) & 1;
-    const uint32_t skip = (uint32_t)t * tile_stride;  // bytes before tile t
-    const uint32_t left = kbytes - skip;
-    const i32x4 rk = make_rsrc_words((const char*)((const uint16_t*)a.k + kbase_e) + skip, left);
-    const i32x4 rv = make_rsrc_words((const char*)((const uint16_t*)a.v + kbase_e) + skip, left);
-#pragma unroll
-    for (int n = 0; n < SLABS; n++) {
-      dma_lds16(rk, smem + buf * TILE + (wave * SLABS + n) * 1024, dma_off[n]);
-      dma_lds16(rv, smem + (2 + buf) * TILE + (wave * SLABS + n) * 1024, dma_off[n]);
-    }
-  };
-
-  f32x16 acc[DB];
-#pragma unroll
-  for (int d = 0; d < DB; d++) acc[d] = f32x16{};
-
-  auto tile = [&](int t, auto MASK) {
-    constexpr bool masked = decltype(MASK)::value;
-    const int buf = (t - t_begin) & 1;
-    const char* kt = smem + buf * TILE;
-    const char* vt = smem + (2 + buf) * TILE;
-    f32x16 st[KB], dp[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; kb++)
-#pragma unroll
-      for (int s = 0; s < KS; s++) {
-        st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], s == 0 ? f32x16{} : st[kb]);
-        dp[kb] = mfma32<F16>(lds_read16(vt + kb * 32 * ROWB + k_off[s]), df[s], s == 0 ? f32x16{} : dp[kb]);
-      }
-    if constexpr (masked) {  // scores of invisible keys -> -inf, so that P = 0 there
-      const int lo = my_kmin - t * FWD_BN - 4 * hh;
-#pragma unroll
-      for (int kb = 0; kb < KB; kb++)
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int o = kb * 32 + 8 * (i >> 2) + (i & 3);
-          if ((uint32_t)(o - lo) > my_kspan) st[kb][i] = -INFINITY;
-        }
-    }
-#pragma unroll
-    for (int kb = 0; kb < KB; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const float p = exp2_fast(fmaf(st[kb][i], c, -mlse));
-        st[kb][i] = p * (dp[kb][i] - row_d);  // dS
-      }
-    u32x4 sf[PT];
-#pragma unroll
-    for (int t2 = 0; t2 < PT; t2++) {
-      const int kb = t2 >> 1, u = t2 & 1;
-      sf[t2] = u32x4{pack2<F16>(st[kb][8 * u + 0], st[kb][8 * u + 1]), pack2<F16>(st[kb][8 * u + 2], st[kb][8 * u + 3]),
-                     pack2<F16>(st[kb][8 * u + 4], st[kb][8 * u + 5]), pack2<F16>(st[kb][8 * u + 6], st[kb][8 * u + 7])};
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int d = 0; d < DB; d++)
-#pragma unroll
-      for (int t2 = 0; t2 < PT; t2++) {
-        const u32x2 a1 = lds_read_tr(kt + t2 * 16 * ROWB + t_off[d][0]);
-        const u32x2 a2 = lds_read_tr(kt + t2 * 16 * ROWB + t_off[d][1]);
-        acc[d] = mfma32<F16>(u32x4{a1[0], a1[1], a2[0], a2[1]}, sf[t2], acc[d]);
-      }
-    // S/dP: 2 reads feed 2 MFMAs per step, reads 3 steps ahead; dQ: 2
-    // transposing reads per MFMA, 4 MFMAs ahead
-    sched_reads_ahead<KB * KS, 2, 2, 3>();
-    sched_reads_ahead<DB * PT, 1, 2, 4>();
-  };
-  auto run = [&](int t0, int t1, auto MASK) {
-    for (int t = t0; t < t1; t++) {
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      if (t + 1 < t_end) load_tile(t + 1);
-      tile(t, MASK);
-    }
-  };
-  int ti0 = t_begin, ti1 = t_begin;
-  if (full_hi >= full_lo) {
-    ti0 = max(t_begin, (full_lo + FWD_BN - 1) / FWD_BN);
-    ti1 = min(t_end, (full_hi + 1) / FWD_BN);
-    if (ti1 <= ti0) ti0 = ti1 = t_begin;
-  }
-  if (t_begin < t_end) load_tile(t_begin);
-  run(t_begin, ti0, std::true_type{});
-  run(ti0, ti1, std::false_type{});
-  run(ti1, t_end, std::true_type{});
-
-  // dQ = scale * acc; lane = query row, registers = dims 8(i/4) + 4hh + i%4 of each 32-block
-  if (a.grad_f32) {
-    const auto rw = make_rsrc((float*)a.dq + qbase_e, qbytes * 2);
-#pragma unroll
-    for (int d = 0; d < DB; d++)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; j4++) {
-        const int dd = d * 32 + 8 * j4 + 4 * hh;
-        const u32x4 w{__builtin_bit_cast(uint32_t, acc[d][4 * j4] * a.scale),
-                      __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 1] * a.scale),
-                      __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 2] * a.scale),
-                      __builtin_bit_cast(uint32_t, acc[d][4 * j4 + 3] * a.scale)};
-        buf_store16(w, rw, dd < dg ? qoff * 2 + (uint32_t)(dd * 4) : DROP_ROW);
-      }
-  } else {
-    static_assert(4 * 32 * ROWB <= 4 * TILE, "dQ staging fits in the tile space");
-    __syncthreads();  // all waves are done reading the K/V tiles
-    const auto rw = make_rsrc((uint16_t*)a.dq + qbase_e, qbytes);
-    store_rows16<D, F16>(acc, a.scale, smem + wave * 32 * ROWB, rw, [&](int r) {
-      const int p = p0 + wave * 32 + r;
-      const int i = div_group(p, a.s), hl = p - i * G;
-      return p < prows ? (uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2) : DROP_ROW;
-    }, dg);
-  }
-}
-
-// ------------------------------------------------------------------ dK, dV
-// One workgroup per 128-key block of one kv head; wave w owns keys
-// 32w .. 32w+31 and keeps dK^T, dV^T (dims x its keys) in registers.  Per
-// block of 32 packed query rows: S = Q K^T and dP = dO V^T (lane = key
-// column, registers = query rows), P and dS with the rows' lse' and D from
-// LDS, dV^T += dO^T P and dK^T += Q^T dS (dO, Q through transposing LDS
-// reads).  dS is kept in fp16 (10 fraction bits) for dK; the Q tiles are
-// therefore fp16 (for bf16 inputs, the copy the dQ kernel wrote; exact for
-// inputs inside fp16's range) and K, used for S, is converted likewise.  Q,
-// dO and the row statistics reach LDS by DMA, double buffered.
-template <int D, bool F16, bool PAD>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
-void bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
-  constexpr int BN = BWD_BN, BM = BWD_BM;
-  constexpr int VBLK = BN * ROWB;           // V block in LDS (B operand of dP)
-  constexpr int QTILE = BM * ROWB;          // one Q (or dO) tile
-  __shared__ __attribute__((aligned(1024))) char smem[VBLK + 4 * QTILE + 2 * 256];
-  char* const v_lds = smem;
-  char* const q_lds = smem + VBLK;              // [buf] fp16 Q tile
-  char* const do_lds = q_lds + 2 * QTILE;       // [buf] dO tile, input dtype
-  float* const st_lds = (float*)(do_lds + 2 * QTILE);  // [buf][lse2 32 | delta 32]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
-  const int G = a.s.group;
-
-  int seq, g, nb;
-  if (a.s.cu_q) {
-    const int id = xcd_remap(blockIdx.x, a.total_ctas);
-    g = id / a.nblk;
-    const int t = id - g * a.nblk;
-    seq = find_sequence(a.s.cu_k, a.s.nseq, t, 1, BN);
-    nb = t - packed_block_start(a.s.cu_k, seq, 1, BN);
-  } else {
-    // groups are (sequence, kv head); rank 0 is key block 0, the one most
-    // query rows see under a causal mask
-    int grp;
-    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nkb}.decode(blockIdx.x, grp, nb)) return;
-    g = grp % a.s.hkv;
-    seq = grp / a.s.hkv;
-  }
-  const SeqInfo si = seq_info(a.s, seq);
-  const int j0 = nb * BN;
-  if (j0 >= si.lk) return;  // idle slot of the packed grid
-  const int prows = si.lq * G;
-  const Band band(a.s, si);
-  const QBand qband(a.s, si);
-  const int j_last = min(j0 + BN, si.lk) - 1;
-  const int q_lo = qband.qmin(j0), q_hi = qband.qmax(j_last);
-  int pb_begin = 0, pb_end = 0;  // packed q-blocks of BM rows
-  if (q_hi >= q_lo && prows > 0) {
-    pb_begin = (q_lo * G) / BM;
-    pb_end = ((q_hi + 1) * G - 1) / BM + 1;
-  }
-
-  // In memory a head holds dg <= D values (PAD: a run-time dg < D); the tile
-  // columns past dg are zero.
-  const int dg = PAD ? a.s.dg : D;
-  const int64_t qrow = (int64_t)a.s.hq * dg, krow = (int64_t)a.s.hkv * dg;
-  const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * dg;
-  const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * dg) * 2) : 0u;
-  const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * dg;
-  const uint32_t kbytes = (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2);
-  const i32x4 rq16 = make_rsrc_words((F16 ? (const uint16_t*)a.q : (const uint16_t*)a.q16) + qbase_e, qbytes);
-  const i32x4 rdo = make_rsrc_words((const uint16_t*)a.dout + qbase_e, qbytes);
-  const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
-  const int64_t st_base = a.s.cu_q ? si.q0 : (int64_t)seq * a.s.hq * a.s.sq;
-  const int64_t st_hs = a.s.cu_q ? a.s.total_q : a.s.sq;
-  const int64_t st_total = a.s.cu_q ? (int64_t)a.s.hq * a.s.total_q : (int64_t)a.s.nseq * a.s.hq * a.s.sq;
-  const i32x4 rl = make_rsrc_words(a.lse2, (uint32_t)(st_total * 4));
-  const i32x4 rd = make_rsrc_words(a.delta, (uint32_t)(st_total * 4));
-
-  // V block -> LDS (swizzled) once
-  {
-    const i32x4 rv = make_rsrc_words((const uint16_t*)a.v + kbase_e, kbytes);
-    constexpr int SLABS = VBLK / 1024 / 4;
-#pragma unroll
-    for (int n = 0; n < SLABS; n++) {
-      const int slab = wave * SLABS + n;
-      const int byte = slab * 1024 + lane * 16;
-      const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      dma_lds16(rv, v_lds + slab * 1024, chunk_off((uint32_t)((int64_t)(j0 + r) * krow * 2), pos ^ swz<D>(r), dg));
-    }
-  }
-  // this wave's 32 keys as the B operand of S (lane: key, 8 dims per k-step), fp16
-  const int my_key = j0 + wave * 32 + l32;
-  u32x4 kf[KS];
-  {
-    const uint32_t ko = (uint32_t)((int64_t)my_key * krow * 2);
-#pragma unroll
-    for (int s = 0; s < KS; s++) {
-      const u32x4 k = buf_load16(rk, chunk_off(ko, 2 * s + hh, dg));
-      kf[s] = F16 ? k : bf16x8_to_f16x8(k);
-    }
-  }
-
-  // Q (fp16) and dO tiles of one block of BM packed rows -> LDS by DMA, and
-  // the rows' lse' and D; rows past the sequence read as 0 (and are masked).
-  auto tile_dma = [&](const i32x4& rs, char* dst, int pb) __attribute__((always_inline)) {
-    constexpr int SL = QTILE / 1024 / 4;  // 1 KB slabs per wave
-#pragma unroll
-    for (int n = 0; n < SL; n++) {
-      const int slab = wave * SL + n;
-      const int byte = slab * 1024 + lane * 16;
-      const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      const int p = pb * BM + r;
-      const int i = div_group(p, a.s), hl = p - i * G;
-      dma_lds16(rs, dst + slab * 1024, chunk_off((uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2), pos ^ swz<D>(r), dg));
-    }
-  };
-  auto do_fetch = [&](int pb, int buf) __attribute__((always_inline)) {
-    tile_dma(rq16, q_lds + buf * QTILE, pb);
-    tile_dma(rdo, do_lds + buf * QTILE, pb);
-    if (wave == 0) {
-      const int p = pb * BM + l32;
-      const int i = div_group(p, a.s), hl = p - i * G;
-      const int64_t idx = st_base + (int64_t)(g * G + hl) * st_hs + i;
-      // rows past the sequence read index 0 (valid memory); they are masked
-      const uint32_t off = p < prows ? (uint32_t)(idx * 4) : 0u;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(st_lds + buf * 64));
-      // lanes 0-31 fetch lse', lanes 32-63 fetch D: lane l's dword lands at m0 + 4 l
-      if (hh == 0)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rl)
-                     : "memory", "m0");
-      else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(rd)
-                     : "memory", "m0");
-    }
-  };
-
-  // loop-invariant LDS offsets
-  int q_off[KS];  // Q / dO as the A operand: row l32, chunk 2 s + hh
-#pragma unroll
-  for (int s = 0; s < KS; s++) q_off[s] = tile_off<D>(l32, 2 * s + hh);
-  int t_off[DB][2];  // transposing reads of Q / dO: rows 16 u + 4 hh + esrc (+8)
-#pragma unroll
-  for (int d = 0; d < DB; d++) {
-    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
-#pragma unroll
-    for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
-  }
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int d = 0; d < DB; d++) {
-    dk[d] = f32x16{};
-    dv[d] = f32x16{};
-  }
-  const float c = a.scale_log2;
-  const char* vrow = v_lds + wave * 32 * ROWB;  // this wave's 32 V rows
-  // The packed rows that see this lane's key form one range,
-  // [pr_lo, pr_lo + pr_span] (the queries [qmin, qmax] of the key times the
-  // group); the mask of a row is then one unsigned compare.  A key past the
-  // sequence is seen by no row.
-  int pr_lo = 1 << 30;
-  uint32_t pr_span = 0;
-  {
-    const int qlo = qband.qmin(my_key), qhi = qband.qmax(my_key);
-    if (my_key < si.lk && qhi >= qlo) {
-      pr_lo = qlo * G;
-      pr_span = (uint32_t)((qhi + 1) * G - 1 - pr_lo);
-    }
-  }
-
-  if (pb_begin < pb_end) do_fetch(pb_begin, 0);
-  for (int pb = pb_begin; pb < pb_end; pb++) {
-    const int buf = (pb - pb_begin) & 1;
-    wait_vmcnt<0>();               // Q, dO tiles, row statistics (and V block) are in LDS
-    __builtin_amdgcn_s_barrier();  // everyone's writes visible; everyone is done with step pb-1
-    if (pb + 1 < pb_end) do_fetch(pb + 1, buf ^ 1);  // buffers of step pb-1, which everyone has left
-    const char* qt = q_lds + buf * QTILE;
-    const char* dot = do_lds + buf * QTILE;
-    const float* stt = st_lds + buf * 64;
-
-    // S and dP, [32 queries x 32 keys]: lane = key column, registers = query rows
-    f32x16 s_acc, dp;
-#pragma unroll
-    for (int s = 0; s < KS; s++) {
-      s_acc = mfma32<true>(lds_read16(qt + q_off[s]), kf[s], s == 0 ? f32x16{} : s_acc);
-      dp = mfma32<F16>(lds_read16(dot + q_off[s]), lds_read16(vrow + q_off[s]), s == 0 ? f32x16{} : dp);
-    }
-    const int p0 = pb * BM;
-    const int qi_lo = div_group(p0, a.s), qi_hi = div_group(min(p0 + BM, prows) - 1, a.s);
-    const bool interior = (p0 + BM <= prows) && j0 + wave * 32 >= band.kmin(qi_hi) &&
-                          j0 + wave * 32 + 31 <= band.kmax(qi_lo);
-    // P and dS from the row statistics of this lane's 16 rows (rows
-    // 8a + 4hh + 0..3); only steps that straddle the band, the last query
-    // rows or the last keys mask
-    if (!interior) {
-      // scores of invisible (row, key) pairs -> -inf, so that P = 0 there
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if ((uint32_t)(pr - pr_lo) > pr_span) s_acc[i] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int a4 = 0; a4 < 4; a4++) {
-      const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
-      const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int i = 4 * a4 + e;
-        const float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
-        s_acc[i] = p;
-        dp[i] = p * (dp[i] - dl[e]);  // dS
-      }
-    }
-    // P^T / dS^T as B operands: k-step u covers queries 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}
-    u32x4 pf[2], sf[2];
-#pragma unroll
-    for (int u = 0; u < 2; u++) {
-      pf[u] = u32x4{pack2<F16>(s_acc[8 * u + 0], s_acc[8 * u + 1]), pack2<F16>(s_acc[8 * u + 2], s_acc[8 * u + 3]),
-                    pack2<F16>(s_acc[8 * u + 4], s_acc[8 * u + 5]), pack2<F16>(s_acc[8 * u + 6], s_acc[8 * u + 7])};
-      sf[u] = u32x4{pack2<true>(dp[8 * u + 0], dp[8 * u + 1]), pack2<true>(dp[8 * u + 2], dp[8 * u + 3]),
-                    pack2<true>(dp[8 * u + 4], dp[8 * u + 5]), pack2<true>(dp[8 * u + 6], dp[8 * u + 7])};
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS   (M = dims, N = this wave's keys, K = queries)
-#pragma unroll
-    for (int d = 0; d < DB; d++)
-#pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int rb = u * 16 * ROWB;
-        const u32x2 o1 = lds_read_tr(dot + rb + t_off[d][0]), o2 = lds_read_tr(dot + rb + t_off[d][1]);
-        dv[d] = mfma32<F16>(u32x4{o1[0], o1[1], o2[0], o2[1]}, pf[u], dv[d]);
-        const u32x2 q1 = lds_read_tr(qt + rb + t_off[d][0]), q2 = lds_read_tr(qt + rb + t_off[d][1]);
-        dk[d] = mfma32<true>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
-      }
-    // S/dP: 3 reads (Q, dO, V) feed 2 MFMAs per step, 2 steps ahead;
-    // dV/dK: 4 transposing reads feed 2 MFMAs per step, 2 steps ahead
-    sched_reads_ahead<KS, 2, 3, 2>();
-    sched_reads_ahead<2 * DB, 2, 4, 2>();
-  }
-
-  // ---- epilogue: dK = scale * dK_acc, dV; lane = key, registers = dims
-  if (!a.grad_f32) {
-    __syncthreads();  // all waves are done reading the V block and the Q/dO tiles
-    static_assert(4 * 2 * 32 * ROWB <= VBLK + 4 * QTILE, "dK/dV staging fits in the tile space");
-    char* const stg = smem + wave * 2 * 32 * ROWB;  // this wave's dK and dV rows
-    auto row_off = [&](int r) {
-      const int kk = j0 + wave * 32 + r;
-      return kk < si.lk ? (uint32_t)((int64_t)kk * krow * 2) : DROP_ROW;
-    };
-    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes), row_off, dg);
-    store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes), row_off, dg);
-  } else if (my_key < si.lk) {
-    const int64_t ob = ((int64_t)(si.k0 + my_key) * a.s.hkv + g) * dg;
-#pragma unroll
-    for (int d = 0; d < DB; d++)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; j4++) {
-        const int dd = d * 32 + 8 * j4 + 4 * hh;
-        if (dd >= dg) continue;  // zero tile columns past the head dim
-        *(f32x4*)((float*)a.dk + ob + dd) = f32x4{dk[d][4 * j4] * a.scale, dk[d][4 * j4 + 1] * a.scale,
-                                                  dk[d][4 * j4 + 2] * a.scale, dk[d][4 * j4 + 3] * a.scale};
-        *(f32x4*)((float*)a.dv + ob + dd) = f32x4{dv[d][4 * j4], dv[d][4 * j4 + 1], dv[d][4 * j4 + 2], dv[d][4 * j4 + 3]};
-      }
-  }
-}
-
-template <int D, bool F16>
-static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  if (a.sinks && a.dsinks) {
-    timing_begin(K_BWD_ZERO, st);
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.s.hq + 255) / 256), dim3(256), 0, st, a.dsinks, a.s.hq);
-    timing_end(K_BWD_ZERO, st);
-  }
-  if (a.total_ctas_q > 0) {
-    timing_begin(K_BWD_DQ, st);
-    if (a.s.dg == D)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, F16, false>), dim3(a.total_ctas_q), dim3(THREADS), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, F16, true>), dim3(a.total_ctas_q), dim3(THREADS), 0, st, a);
-    timing_end(K_BWD_DQ, st);
-  }
-  if (a.total_ctas > 0) {
-    timing_begin(K_BWD_DKDV, st);
-    if (a.s.dg == D)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-    timing_end(K_BWD_DKDV, st);
-  }
-  return hipGetLastError();
-}
+extern template hipError_t launch_bwd_variant<EXT_CAP>(const BwdArgs&, int, bool, hipStream_t);
+extern template hipError_t launch_bwd_variant<EXT_ALIBI>(const BwdArgs&, int, bool, hipStream_t);
+extern template hipError_t launch_bwd_variant<EXT_CAP | EXT_ALIBI>(const BwdArgs&, int, bool, hipStream_t);
 
 hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st) {
-  if (tile_d == 256) return f16 ? launch_bwd_t<256, true>(a, st) : launch_bwd_t<256, false>(a, st);
-  if (tile_d == 128) return f16 ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
-  return f16 ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
+  if (a.sinks && a.dsinks) {
+    timing_begin(K_BWD_ZERO, st);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.dsink_count + 255) / 256), dim3(256), 0, st, a.dsinks,
+                       a.dsink_count);
+    timing_end(K_BWD_ZERO, st);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (a.x.ext) {
+    case EXT_CAP: return launch_bwd_variant<EXT_CAP>(a, tile_d, f16, st);
+    case EXT_ALIBI: return launch_bwd_variant<EXT_ALIBI>(a, tile_d, f16, st);
+    case EXT_CAP | EXT_ALIBI: return launch_bwd_variant<EXT_CAP | EXT_ALIBI>(a, tile_d, f16, st);
+    default: return launch_bwd_variant<0>(a, tile_d, f16, st);
+  }
 }
 
 }  // namespace attn

@@ -91,4 +91,44 @@ __device__ __forceinline__ int find_sequence(const int32_t* cu, int n, int t, in
   return lo;
 }
 
+// ---------------------------------------------------------------- sinks
+// The sinks of q head h act as one logit, log sum_k exp(s_hk) (each is a
+// value-less logit of the row's softmax: dew-flash-attn page, sinks
+// paragraph; several per head: ejkernel flash_attention API page,
+// softmax_aux).  Returned in log2 units; -inf when every sink is -inf.
+__device__ __forceinline__ float sink_log2(const float* sinks, const ScoreArgs& x, int h) {
+  const float* s = sinks + h * x.sink_hstride;
+  if (x.nsinks == 1) return s[0] * LOG2E;
+  float mx = -INFINITY;
+  for (int k = 0; k < x.nsinks; k++) mx = fmaxf(mx, s[k]);
+  if (mx == -INFINITY) return -INFINITY;
+  float sum = 0.f;
+  for (int k = 0; k < x.nsinks; k++) sum += exp2_fast((s[k] - mx) * LOG2E);
+  return mx * LOG2E + log2_fast(sum);
+}
+
+// ---------------------------------------------------------------- score variants
+// Raw score x of a (row, key) pair -> x' (see ScoreArgs): soft cap
+// (vllm-project/flash-attention README on the GitHub search page, "2.6:
+// Softcapping"; ejkernel page, logits_soft_cap), then the ALiBi bias
+// -slope |i + Lk - Lq - j| (alibi_slopes, flash_attn_func docstring of the
+// same README).  kb = slope / scale of the row's q head, dist = i + Lk - Lq - j.
+// t receives tanh(x scale / cap) (dx'/dx = 1 - t^2) under the cap.
+template <int EXT>
+__device__ __forceinline__ float ext_score(float x, const ScoreArgs& a, float kb, float dist, float& t) {
+  if constexpr ((EXT & EXT_CAP) != 0) {
+    // tanh(u) = 1 - 2 / (1 + e^(2u)); e^(2u) = 2^(x k2) overflows to inf for
+    // large u (t = 1) and underflows to 0 for very negative u (t = -1)
+    t = fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + exp2_fast(x * a.cap_k2)), 1.f);
+    x = a.cap_k3 * t;
+  }
+  if constexpr ((EXT & EXT_ALIBI) != 0) x = fmaf(-kb, fabsf(dist), x);
+  return x;
+}
+
+// slope / scale of q head h in sequence seq (0 without ALiBi)
+__device__ __forceinline__ float alibi_kb(const ScoreArgs& x, int seq, int h) {
+  return x.alibi ? x.alibi[(int64_t)seq * x.alibi_bstride + h] * x.inv_scale : 0.f;
+}
+
 }  // namespace attn

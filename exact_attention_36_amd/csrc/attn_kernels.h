@@ -41,11 +41,30 @@ struct SeqArgs {
   int32_t page_rows, pages_per_seq;
 };
 
+// Score variants and sinks.  The kernels work on raw scores x = <q, k> and
+// P = 2^(x c - m), c = scale log2(e); a variant replaces x by x' such that
+// x' c is the variant's logit in log2 units:
+//   soft cap: x' = (cap / scale) tanh(x scale / cap), tanh(u) = 1 - 2 / (1 + 2^(2 u log2 e));
+//   ALiBi:    x' -= (slope_h / scale) |i + Lk - Lq - j|.
+// Variants are compile-time (EXT_CAP, EXT_ALIBI bits); sinks are not.
+constexpr int EXT_CAP = 1, EXT_ALIBI = 2;
+struct ScoreArgs {
+  float cap_k2;           // 2 scale log2(e) / cap
+  float cap_k3;           // cap / scale
+  const float* alibi;     // slopes [nseq or 1][hq], or nullptr
+  int32_t alibi_bstride;  // hq (per sequence) or 0 (one row for all)
+  float inv_scale;        // 1 / scale
+  int32_t nsinks;         // sinks per q head (>= 1 when sinks are given)
+  int32_t sink_hstride;   // nsinks ([hq][nsinks]) or 0 (one row shared by the heads)
+  int32_t ext;            // the EXT_* bits this call needs
+};
+
 struct FwdArgs {
   SeqArgs s;
+  ScoreArgs x;
   const void* q; const void* k; const void* v;
   void* o; float* lse;
-  const float* sinks;     // [hq] or nullptr
+  const float* sinks;     // sink logits (layout in x), or nullptr
   float* o_part;          // split-KV partial outputs (fp32) or nullptr
   float* lse_part;        // split-KV partial log-sum-exps
   float scale_log2;       // softmax scale * log2(e)
@@ -58,10 +77,12 @@ struct FwdArgs {
 
 struct BwdArgs {
   SeqArgs s;
+  ScoreArgs x;
   const void* q; const void* k; const void* v; const void* o; const void* dout;
   const float* lse;       // sink-free log-sum-exp from the forward
-  const float* sinks;     // [hq] or nullptr
-  float* dsinks;          // [hq] or nullptr
+  const float* sinks;     // sink logits (layout in x), or nullptr
+  float* dsinks;          // gradient, laid out like sinks, or nullptr
+  int32_t dsink_count;    // floats in dsinks
   float* delta;           // fp32, laid out like lse: D_i = <dO_i, O_i>
   float* lse2;            // fp32, laid out like lse: log-sum-exp with the sink, in log2 units
   uint16_t* q16;          // fp16 copy of Q (layout of Q) for bf16 inputs, written by the dQ kernel; nullptr for fp16

@@ -151,6 +151,24 @@ def packed_workload(seed: int = 4, n: int = 64, total: int = 65536, hq: int = 16
     return dict(q=q, k=k, v=v, dout=dout, sinks=None, cu_q=cu, cu_k=cu, lengths=L)
 
 
+def sink_table(seed: int, rows: int, n: int) -> np.ndarray:
+    """Sink logits, float32 [rows, n] (rows = q heads, or 1 for a shared row):
+    N(0, 1.5^2), seeded on their own."""
+    rng = np.random.default_rng(int(seed) + 7919)
+    return (1.5 * rng.standard_normal((rows, n))).astype(np.float32)
+
+
+def alibi_slopes(hq: int, batch: int = 0, seed: int = 0) -> np.ndarray:
+    """ALiBi slopes, float32: the geometric sequence 2^(-8 (h+1) / hq) of the
+    ALiBi paper (Press et al., 2021) for [hq]; with batch > 0, [batch, hq]
+    rows of it scaled by seeded factors in [0.5, 2)."""
+    base = np.exp2(-8.0 * (np.arange(hq) + 1) / hq)
+    if batch <= 0:
+        return base.astype(np.float32)
+    rng = np.random.default_rng(int(seed) + 104729)
+    return (base[None, :] * rng.uniform(0.5, 2.0, (batch, 1))).astype(np.float32)
+
+
 def device_normal(seed: int, shapes, device="cuda", dtype: str = "bf16"):
     """Large inputs drawn on the GPU: i.i.d. N(0,1) float32 from torch's seeded
     device generator (Philox), rounded to bf16/fp16 (RNE), in the order of

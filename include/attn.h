@@ -29,6 +29,16 @@
  *    denominator with no value, which multiplies the row's output by
  *    sigmoid(lse - sink); the returned lse is the sink-free one, and the
  *    backward returns d(loss)/d(sink) (dew-flash-attn page, sinks paragraph).
+ *    Several sinks per q head (ejkernel flash_attention API page,
+ *    softmax_aux [num_heads, num_sinks] or [num_sinks]) each join the
+ *    denominator; together they act as one sink at log sum_k exp(sink_k).
+ *  - Score variants: a soft cap, softcap * tanh(x / softcap) of each logit
+ *    x = scale * q.k (vllm-project/flash-attention README on the GitHub
+ *    search page, "2.6: Softcapping"; ejkernel page, logits_soft_cap; the
+ *    pages give no formula and the tanh form is the plain reading), then the
+ *    ALiBi bias -slope_h * |i + Lk - Lq - j| (alibi_slopes in the
+ *    flash_attn_func docstring of the same README).  Gradients follow the
+ *    chain rule through both.
  *  - Packed variable-length batches: [T, H, D] tensors with int32 offsets
  *    cu_seqlens [N+1] from 0 to T; attention never crosses sequences; the
  *    mask applies per sequence with that sequence's own Lq, Lk; zero-length
@@ -45,7 +55,8 @@
  *             lse              fp32 [B, Hq, Sq]
  *   packed:   q, o, dout, dq   [Tq, Hq, D];     k, v, dk, dv  [Tk, Hkv, D]
  *             lse              fp32 [Hq, Tq]
- *   sinks, dsinks              fp32 [Hq]
+ *   sinks, dsinks              fp32 [Hq][num_sinks], or [num_sinks] shared
+ *   alibi_slopes               fp32 [Hq], or [B or num_seqs][Hq]
  *
  * Ownership: every pointer except `params` is device memory owned by the
  * caller; the library allocates nothing and keeps no device state.  Scratch
@@ -92,7 +103,19 @@ typedef struct {
     int32_t causal;         /* 0 or 1 */
     int32_t window_left;    /* >= -1; -1 = unbounded */
     int32_t window_right;   /* >= -1; -1 = unbounded */
-    const float *sinks;     /* device fp32 [Hq] or NULL */
+    const float *sinks;     /* device fp32 sink logits or NULL: num_sinks per q
+                               head, [Hq][num_sinks], or one row [num_sinks]
+                               for all heads when sinks_shared = 1 */
+    int32_t num_sinks;      /* sinks per q head, 0..64 (0 counts as 1) */
+    int32_t sinks_shared;   /* 0 or 1, see sinks */
+    float softcap;          /* >= 0; > 0 replaces each logit x (scale * q.k)
+                               by softcap * tanh(x / softcap) */
+    const float *alibi_slopes; /* device fp32 ALiBi slopes or NULL: [Hq], or
+                               [batch][Hq] (packed: [num_seqs][Hq]) when
+                               alibi_per_batch = 1; adds
+                               -slope * |i + Lk - Lq - j| to the logit of
+                               query i and key j, after the soft cap */
+    int32_t alibi_per_batch; /* 0 or 1, see alibi_slopes */
 } attn_params;
 
 /*
@@ -111,7 +134,8 @@ size_t attn_fwd_workspace_size(const attn_params *params, int64_t batch, int64_t
  * Backward, batched.  Inputs are the forward's q, k, v, o and lse plus the
  * output gradient dout.  Writes dq [B,Sq,Hq,D], dk, dv [B,Sk,Hkv,D] as
  * grad_dtype (the input dtype, or ATTN_FP32 for fp32 gradients) and, when
- * params->sinks is set, dsinks (fp32 [Hq], must then be non-NULL).
+ * params->sinks is set, dsinks (fp32, laid out like the sinks; must then be
+ * non-NULL; heads that share a row of sinks add into it).
  * dK/dV of a kv head sum over the q heads that share it (fa4-jax page,
  * restrictions paragraph: fp32 accumulation across the q heads).
  */

@@ -55,6 +55,13 @@ def _fwd(p, B=1, sq=16, sk=16, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=None
     (dict(window_left=-2), _lib.ATTN_EINVAL, "window"),
     (dict(window_right=-5), _lib.ATTN_EINVAL, "window"),
     (dict(causal=2), _lib.ATTN_EINVAL, "causal"),
+    (dict(num_sinks=-1), _lib.ATTN_EINVAL, "num_sinks"),
+    (dict(num_sinks=65), _lib.ATTN_EINVAL, "num_sinks"),
+    (dict(sinks_shared=2), _lib.ATTN_EINVAL, "sinks_shared"),
+    (dict(softcap=-1.0), _lib.ATTN_EINVAL, "softcap"),
+    (dict(softcap=float("inf")), _lib.ATTN_EINVAL, "softcap"),
+    (dict(softcap=float("nan")), _lib.ATTN_EINVAL, "softcap"),
+    (dict(alibi_per_batch=3), _lib.ATTN_EINVAL, "alibi_per_batch"),
 ])
 def test_fwd_rejects_bad_params(kw, status, needle):
     assert _fwd(_params(**kw)) == status
