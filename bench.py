@@ -9,7 +9,7 @@ with HIP events on its own stream; `decode` measures the decode-shaped
 forward (B=32, s_q=16, s_kv=32768, Hq=64, Hkv=8) as K/V HBM GB/s;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
 prefill workload.  `--workload decode` runs only the decode shape;
-`--workload sweep` and `--workload headdims` print one line per shape.
+`--workload sweep`, `headdims` and `variants` print one line per shape.
 """
 from __future__ import annotations
 
@@ -250,6 +250,43 @@ def run_headdims(steps, warmup):
     return rows
 
 
+def run_variants(steps, warmup):
+    """Score variants on the causal prefill shape (B=4, H=16, S=2048, D=128,
+    bf16): plain, soft cap 50, ALiBi (geometric slopes), both, and 4 sinks per
+    head; forward and backward ms and TFLOP/s (14*D flops per visible pair)."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    B, S, H, D = 4, 2048, 16, 128
+    pairs = visible_pairs(B, S, S, H, True, (-1, -1))
+    q, k, v, do = synth.device_normal(11, [(B, S, H, D)] * 4)
+    slopes = torch.from_numpy(synth.alibi_slopes(H)).cuda()
+    sinks4 = torch.from_numpy(synth.sink_table(11, H, 4)).cuda()
+    rows = []
+    for name, kw in (("plain", {}), ("softcap50", dict(softcap=50.0)), ("alibi", dict(alibi_slopes=slopes)),
+                     ("softcap50_alibi", dict(softcap=50.0, alibi_slopes=slopes)), ("sinks4", dict(sinks=sinks4))):
+        o, lse = ea.attn_fwd(q, k, v, causal=True, **kw)
+        for _ in range(warmup):
+            ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse, **kw)
+            ea.attn_bwd(q, k, v, o, lse, do, causal=True, **kw)
+        torch.cuda.synchronize()
+        ea.attn_timing_enable(True)
+        for _ in range(steps):
+            ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse, **kw)
+            ea.attn_bwd(q, k, v, o, lse, do, causal=True, **kw)
+        torch.cuda.synchronize()
+        t = {n: ea.attn_timing_read(n)[1] / steps for n in ea._lib.KERNELS}
+        ea.attn_timing_enable(False)
+        fwd_ms = t["fwd"] + t["fwd_combine"]
+        bwd_ms = t["bwd_zero"] + t["bwd_dq"] + t["bwd_dkdv"]
+        rows.append({"variant": name, "fwd_ms": round(fwd_ms, 4), "bwd_dq_ms": round(t["bwd_dq"], 4),
+                     "bwd_dkdv_ms": round(t["bwd_dkdv"], 4), "bwd_ms": round(bwd_ms, 4),
+                     "fwd_tflops": round(4.0 * D * pairs / (fwd_ms * 1e-3) / 1e12, 1),
+                     "tflops": round(14.0 * D * pairs / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 1)})
+        print(json.dumps(rows[-1]), flush=True)
+    return rows
+
+
 def cpu_baseline(inp, w, seconds_target=15.0):
     """Time the fp64 oracle on whole (batch, head) slices of the workload."""
     import numpy as np
@@ -362,11 +399,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
-    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "power"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "power"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
                          "sweep: context sweep over S = 512..16384 (one JSON line per shape); "
-                         "headdims: causal prefill at D = 32..128 (one JSON line per head dim); "
+                         "headdims: causal prefill at D = 32..256 (one JSON line per head dim); "
+                         "variants: causal prefill with soft cap / ALiBi / 4 sinks (one line each); "
                          "power: socket power and shader clock (amd-smi) under the step's kernels")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -387,6 +425,9 @@ def main():
         return
     if args.workload == "headdims":
         run_headdims(args.steps, args.warmup)
+        return
+    if args.workload == "variants":
+        run_variants(args.steps, args.warmup)
         return
     if args.workload == "power":
         run_power(args.seconds)

@@ -253,7 +253,19 @@ void bwd_dq_kernel(const BwdArgs a) {
         st[kb] = mfma32<F16>(lds_read16(kt + kb * 32 * ROWB + k_off[s]), qf[s], s == 0 ? f32x16{} : st[kb]);
         dp[kb] = mfma32<F16>(lds_read16(vt + kb * 32 * ROWB + k_off[s]), df[s], s == 0 ? f32x16{} : dp[kb]);
       }
-    if constexpr (EXT == 0) {
+    if constexpr ((EXT & EXT_CAP) == 0) {
+      if constexpr (EXT != 0) {
+        // ALiBi alone: the variant logit in place of the raw score, before the
+        // mask, which then treats it as a plain score
+        const float base = ext_diag - (float)(t * FWD_BN);
+#pragma unroll
+        for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            float th;
+            st[kb][i] = ext_score<EXT>(st[kb][i], a.x, ext_kb, base - (float)(kb * 32 + 8 * (i >> 2) + (i & 3)), th);
+          }
+      }
       if constexpr (masked) {  // scores of invisible keys -> -inf, so that P = 0 there
         const int lo = my_kmin - t * FWD_BN - 4 * hh;
 #pragma unroll
@@ -272,8 +284,9 @@ void bwd_dq_kernel(const BwdArgs a) {
           st[kb][i] = p * (dp[kb][i] - row_d);  // dS
         }
     } else {
-      // variant logit, P, and dS with the soft cap's 1 - tanh^2; invisible
-      // keys are zeroed after (their logits may be anything)
+      // soft cap (and ALiBi): variant logit, P, and dS with 1 - tanh^2 in one
+      // pass (the tanh stays a temporary); invisible keys are zeroed after
+      // (their logits may be anything)
       const float base = ext_diag - (float)(t * FWD_BN);
 #pragma unroll
       for (int kb = 0; kb < KB; kb++)
@@ -571,7 +584,22 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     // P and dS from the row statistics of this lane's 16 rows (rows
     // 8a + 4hh + 0..3); only steps that straddle the band, the last query
     // rows or the last keys mask
-    if constexpr (EXT == 0) {
+    if constexpr ((EXT & EXT_CAP) == 0) {
+      if constexpr (EXT != 0) {
+        // ALiBi alone: the variant logit in place of the raw score, with the
+        // rows' terms from LDS, before the mask
+        const float* ext = ext_lds + buf * 64;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; a4++) {
+          const f32x4 dg4 = *(const f32x4*)(ext + 8 * a4 + 4 * hh);
+          const f32x4 kb4 = *(const f32x4*)(ext + 32 + 8 * a4 + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            float th;
+            s_acc[4 * a4 + e] = ext_score<EXT>(s_acc[4 * a4 + e], a.x, kb4[e], dg4[e] - keyf, th);
+          }
+        }
+      }
       if (!interior) {
         // scores of invisible (row, key) pairs -> -inf, so that P = 0 there
 #pragma unroll
@@ -593,8 +621,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
     } else {
-      // variant logits (rows' ALiBi terms from LDS), P, and dS with the soft
-      // cap's 1 - tanh^2; invisible pairs are zeroed after
+      // soft cap (and ALiBi, rows' terms from LDS): variant logits, P, and dS
+      // with 1 - tanh^2 in one pass; invisible pairs are zeroed after
       const float* ext = ext_lds + buf * 64;
 #pragma unroll
       for (int a4 = 0; a4 < 4; a4++) {
