@@ -202,7 +202,7 @@ def run_sweep(steps, warmup):
             t = {n: ea.attn_timing_read(n)[1] / steps for n in ea._lib.KERNELS}
             ea.attn_timing_enable(False)
             fwd_ms = t["fwd"] + t["fwd_combine"]
-            bwd_ms = t["bwd_zero"] + t["bwd_dq"] + t["bwd_dkdv"]
+            bwd_ms = t["bwd_dsink"] + t["bwd_dq"] + t["bwd_dkdv"]
             pairs = visible_pairs(B, S, S, H, causal, (-1, -1))
             rows.append({"S": S, "B": B, "causal": causal, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
                          "fwd_tflops": round(4.0 * D * pairs / (fwd_ms * 1e-3) / 1e12, 1),
@@ -239,7 +239,7 @@ def run_headdims(steps, warmup):
         t = {n: ea.attn_timing_read(n)[1] / steps for n in ea._lib.KERNELS}
         ea.attn_timing_enable(False)
         fwd_ms = t["fwd"] + t["fwd_combine"]
-        bwd_ms = t["bwd_zero"] + t["bwd_dq"] + t["bwd_dkdv"]
+        bwd_ms = t["bwd_dsink"] + t["bwd_dq"] + t["bwd_dkdv"]
         tile = 64 if D <= 64 else 128 if D <= 128 else 256
         rows.append({"D": D, "tile_D": tile, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
                      "fwd_tflops": round(4.0 * D * pairs / (fwd_ms * 1e-3) / 1e12, 1),
@@ -278,7 +278,7 @@ def run_variants(steps, warmup):
         t = {n: ea.attn_timing_read(n)[1] / steps for n in ea._lib.KERNELS}
         ea.attn_timing_enable(False)
         fwd_ms = t["fwd"] + t["fwd_combine"]
-        bwd_ms = t["bwd_zero"] + t["bwd_dq"] + t["bwd_dkdv"]
+        bwd_ms = t["bwd_dsink"] + t["bwd_dq"] + t["bwd_dkdv"]
         rows.append({"variant": name, "fwd_ms": round(fwd_ms, 4), "bwd_dq_ms": round(t["bwd_dq"], 4),
                      "bwd_dkdv_ms": round(t["bwd_dkdv"], 4), "bwd_ms": round(bwd_ms, 4),
                      "fwd_tflops": round(4.0 * D * pairs / (fwd_ms * 1e-3) / 1e12, 1),

@@ -136,20 +136,30 @@ size_t fwd_ws(const attn_params* p, int64_t B, int64_t sq, int64_t sk, int* n_sp
   return align_up(rows * tile_dim(p->head_dim) * 4) + align_up(rows * 4);
 }
 
+// dQ workgroups per kv head: batched, nseq * ceil(sq G / 128); packed, the
+// linear grid's floor(total_q G / 128) + nseq.
+int64_t dq_blocks(const attn_params* p, bool packed, int64_t nseq, int64_t sq, int64_t total_q) {
+  const int64_t G = p->heads_q / p->heads_kv;
+  return packed ? (total_q * G) / BWD_QBM + nseq : nseq * cdiv(sq * G, BWD_QBM);
+}
+
 // Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like
-// lse, and for bf16 inputs an fp16 copy of Q (layout of Q) that the dQ kernel
-// writes and the dK/dV kernel reads.
+// lse; for bf16 inputs an fp16 copy of Q (layout of Q) that the dQ kernel
+// writes and the dK/dV kernel reads; with sinks, each dQ workgroup's sums of
+// the sink gradient per q head of its group ([Hkv][blocks][G]), which a last
+// kernel adds up in a fixed order.
 struct BwdWs {
-  size_t delta, lse2, q16, total;
+  size_t delta, lse2, q16, dsink_part, total;
 };
-BwdWs bwd_ws(const attn_params* p, int64_t tq, int32_t grad_dtype) {
+BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) {
   (void)grad_dtype;
   BwdWs w{};
   const int64_t rows = tq * p->heads_q;
   w.delta = align_up(rows * 4);
   w.lse2 = align_up(rows * 4);
   w.q16 = p->dtype == ATTN_BF16 ? align_up(rows * p->head_dim * 2) : 0;
-  w.total = w.delta + w.lse2 + w.q16;
+  w.dsink_part = p->sinks ? align_up(nbq * p->heads_q * 4) : 0;  // Hkv * nbq * G = nbq * Hq
+  w.total = w.delta + w.lse2 + w.q16 + w.dsink_part;
   return w;
 }
 
@@ -229,7 +239,8 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
                     int32_t grad_dtype, void* ws, size_t ws_bytes, void* stream) {
   const bool packed = cu_q != nullptr;
   const int64_t tq = packed ? total_q : nseq * sq;
-  const BwdWs w = bwd_ws(p, tq, grad_dtype);
+  const int64_t nbq = dq_blocks(p, packed, nseq, sq, total_q);
+  const BwdWs w = bwd_ws(p, tq, nbq, grad_dtype);
   attn_status st = check_ws(ws, ws_bytes, w.total);
   if (st != ATTN_OK) return st;
   BwdArgs a{};
@@ -252,6 +263,9 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   a.lse2 = (float*)wp;
   wp += w.lse2;
   a.q16 = w.q16 ? (uint16_t*)wp : nullptr;
+  wp += w.q16;
+  a.dsink_part = w.dsink_part ? (float*)wp : nullptr;
+  a.nbq = (int32_t)nbq;
   const float scale = resolve_scale(p);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -301,7 +315,7 @@ size_t attn_bwd_workspace_size(const attn_params* p, int64_t batch, int64_t seql
                                int32_t grad_dtype) {
   (void)seqlen_k;
   if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1) return 0;
-  return bwd_ws(p, batch * seqlen_q, grad_dtype).total;
+  return bwd_ws(p, batch * seqlen_q, dq_blocks(p, false, batch, seqlen_q, 0), grad_dtype).total;
 }
 
 // Bound on a KV-cache call's keys per slot: the slot capacity, or the pages
@@ -365,12 +379,11 @@ size_t attn_fwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, in
 
 size_t attn_bwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
                                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t grad_dtype) {
-  (void)num_seqs;
   (void)total_k;
   (void)max_seqlen_q;
   (void)max_seqlen_k;
-  if (check_params(p) != ATTN_OK || total_q < 0) return 0;
-  return bwd_ws(p, total_q, grad_dtype).total;
+  if (check_params(p) != ATTN_OK || total_q < 0 || num_seqs < 0) return 0;
+  return bwd_ws(p, total_q, dq_blocks(p, true, num_seqs, 0, total_q), grad_dtype).total;
 }
 
 attn_status attn_fwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,

@@ -17,10 +17,9 @@
 // the backward).
 //
 // Kernels, in stream order:
-//   bwd_zero_kernel   clears dsinks
 //   bwd_dq_kernel     query-major: one workgroup per 128 packed query rows
 //                     computes the rows' D_i, lse' (log2 units, with the
-//                     sink) and dsink partials, then
+//                     sink) and its per-head dsink sums, then
 //                     streams the visible K/V tiles (like the forward),
 //                     recomputes S, P, dP, dS and accumulates dQ in
 //                     registers; dQ is written once, no atomics
@@ -29,6 +28,12 @@
 //                     group's q heads, recomputes S, P, dP, dS and
 //                     accumulates dK and dV in registers (fp32 across the
 //                     GQA group: fa4-jax page, restrictions paragraph)
+//   bwd_dsink_kernel  (with sinks) adds the dQ workgroups' dsink sums in a
+//                     fixed order
+// No output is accumulated with atomics, so every result of the backward is
+// the same bit for bit on every run (the deterministic backward of the
+// vllm-project/flash-attention README's flash_attn_func docstring, here the
+// only backward).
 // The two main kernels recompute S and dP each (7 products per visible
 // block instead of 5) in exchange for no fp32 atomics, no dS exchange
 // through LDS and two waves per SIMD in both.  The packed (varlen) grids
@@ -62,24 +67,30 @@ void bwd_dq_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.s.group;
-  int seq, g, mb;
+  int seq, g, mb, blk;  // blk: this workgroup's index among its kv head's dQ workgroups
   if (a.s.cu_q) {
     const int id = xcd_remap(blockIdx.x, a.total_ctas_q);
     g = id / a.nblk_q;
-    const int t = id - g * a.nblk_q;
-    seq = find_sequence(a.s.cu_q, a.s.nseq, t, G, BM);
-    mb = t - packed_block_start(a.s.cu_q, seq, G, BM);
+    blk = id - g * a.nblk_q;
+    seq = find_sequence(a.s.cu_q, a.s.nseq, blk, G, BM);
+    mb = blk - packed_block_start(a.s.cu_q, seq, G, BM);
   } else {
     int grp, rank;
     if (!GroupGrid{a.s.nseq * a.s.hkv, a.nmb}.decode(blockIdx.x, grp, rank)) return;
     g = grp % a.s.hkv;
     seq = grp / a.s.hkv;
     mb = a.nmb - 1 - rank;  // causal: the longest tiles start first
+    blk = seq * a.nmb + mb;
   }
+  // this workgroup's per-head sums of the sink gradient (every slot written)
+  float* const dsink_out = a.dsink_part ? a.dsink_part + ((int64_t)g * a.nbq + blk) * G : nullptr;
   const SeqInfo si = seq_info(a.s, seq);
   const int prows = si.lq * G;
   const int p0 = mb * BM;
-  if (p0 >= prows) return;
+  if (p0 >= prows) {  // idle slot of the packed grid (whole workgroup)
+    if (dsink_out && (int)threadIdx.x < G) dsink_out[threadIdx.x] = 0.f;
+    return;
+  }
 
   const Band band(a.s, si);
   const int i_lo = div_group(p0, a.s), i_hi = div_group(min(p0 + BM, prows) - 1, a.s);
@@ -171,30 +182,18 @@ void bwd_dq_kernel(const BwdArgs a) {
       a.lse2[li] = row_lse2;
     }
   }
-  if (a.sinks && a.dsinks) {
-    // sum the block's rows per q head in LDS, then one global add per head;
-    // 128 consecutive packed rows hold at most 128 distinct heads, slot
-    // (p - p0) mod G names them without collisions
-    __shared__ float dsink_red[BM];
-    if (threadIdx.x < BM) dsink_red[threadIdx.x] = 0.f;
+  if (dsink_out) {
+    // the block's rows summed per q head in a fixed order (no atomics): row r
+    // of the block (packed row p0 + r) belongs to head slot r mod G, and
+    // thread t < G adds rows t, t + G, t + 2G, ...; slot t is q head
+    // (p0 + t) mod G of the group
+    __shared__ float dsink_rows[BM];
+    if (hh == 0) dsink_rows[my_p - p0] = dsink_part;
     __syncthreads();
-    if (hh == 0 && dsink_part != 0.f) atomicAdd(&dsink_red[(my_p - p0) % G], dsink_part);
-    __syncthreads();
-    if ((int)threadIdx.x < min(G, BM)) {
-      const float v = dsink_red[threadIdx.x];
-      if (v != 0.f) {
-        // several sinks: sink k takes the share 2^(s_hk log2 e - s2) of the
-        // head's gradient (heads sharing one row of sinks add into it)
-        const int h = g * G + (p0 + (int)threadIdx.x) % G;
-        float* dst = a.dsinks + h * a.x.sink_hstride;
-        if (a.x.nsinks == 1) {
-          atomicAdd(dst, v);
-        } else {
-          const float s2 = sink_log2(a.sinks, a.x, h);
-          const float* src = a.sinks + h * a.x.sink_hstride;
-          for (int k = 0; k < a.x.nsinks; k++) atomicAdd(dst + k, v * exp2_fast(fmaf(src[k], LOG2E, -s2)));
-        }
-      }
+    if ((int)threadIdx.x < G) {
+      float v = 0.f;
+      for (int r = threadIdx.x; r < BM; r += G) v += dsink_rows[r];
+      dsink_out[(p0 + (int)threadIdx.x) % G] = v;
     }
   }
   const float c = a.scale_log2;

@@ -83,6 +83,8 @@ struct BwdArgs {
   const float* sinks;     // sink logits (layout in x), or nullptr
   float* dsinks;          // gradient, laid out like sinks, or nullptr
   int32_t dsink_count;    // floats in dsinks
+  float* dsink_part;      // [hkv][nbq][G]: each dQ workgroup's per-head sums (workspace)
+  int32_t nbq;            // dQ workgroups per kv head (batched: nseq * nmb; packed: nblk_q)
   float* delta;           // fp32, laid out like lse: D_i = <dO_i, O_i>
   float* lse2;            // fp32, laid out like lse: log-sum-exp with the sink, in log2 units
   uint16_t* q16;          // fp16 copy of Q (layout of Q) for bf16 inputs, written by the dQ kernel; nullptr for fp16
@@ -103,7 +105,7 @@ constexpr int BWD_QBM = 128;    // packed query rows per dQ workgroup
 
 // Optional per-launch timing (attn_timing_enable): the launchers call these
 // around every kernel launch; they record HIP events only while enabled.
-enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_ZERO, K_BWD_DQ, K_BWD_DKDV, K_COUNT };
+enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_DSINK, K_BWD_DQ, K_BWD_DKDV, K_COUNT };
 void timing_begin(int kid, hipStream_t st);
 void timing_end(int kid, hipStream_t st);
 

@@ -217,7 +217,7 @@ size_t attn_bwd_varlen_workspace_size(const attn_params *params, int32_t num_seq
 typedef enum {
     ATTN_KERNEL_FWD = 0,          /* fused forward */
     ATTN_KERNEL_FWD_COMBINE = 1,  /* split-KV merge */
-    ATTN_KERNEL_BWD_ZERO = 2,     /* clears dsinks */
+    ATTN_KERNEL_BWD_DSINK = 2,    /* sums the dQ workgroups' sink-gradient partials into dsinks */
     ATTN_KERNEL_BWD_DQ = 3,       /* query-major backward: row statistics, dsinks, dQ */
     ATTN_KERNEL_BWD_DKDV = 4,     /* key-major backward: dK, dV */
     ATTN_KERNEL_COUNT = 5

@@ -66,11 +66,12 @@ def test_batched_matches_oracle(case):
                                      grad_dtype=gd)
         torch.cuda.synchronize()
         od = "f32" if gd == torch.float32 else dt
-        if gd != torch.float32:  # dQ, dK, dV accumulate without atomics: bitwise repeatable
-            dq2, dk2, dv2, _ = ea.attn_bwd(q, k, v, o, lse, do, causal=causal, window=window, sinks=s_dev,
-                                           grad_dtype=gd)
+        if gd != torch.float32:  # no output accumulates with atomics: bitwise repeatable
+            dq2, dk2, dv2, ds2 = ea.attn_bwd(q, k, v, o, lse, do, causal=causal, window=window, sinks=s_dev,
+                                             grad_dtype=gd)
             torch.cuda.synchronize()
             assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), "backward not repeatable"
+            assert ds is None or torch.equal(ds, ds2), "dsinks not repeatable"
         assert_close(name + ".dq", host(dq).reshape(B * sq, hq, d), ref["dq"], od)
         assert_close(name + ".dk", host(dk).reshape(B * sk, hkv, d), ref["dk"], od)
         assert_close(name + ".dv", host(dv).reshape(B * sk, hkv, d), ref["dv"], od)
