@@ -19,9 +19,12 @@ from _helpers import assert_close, assert_lse, dev_tensor, host
 pytestmark = pytest.mark.gpu
 
 
-def _sum_rules(name, q, do, dk, dv, lse, o, sinks, scale, q_rows, k_rows, hkv):
+def _sum_rules(name, q, do, dk, dv, lse, o, sinks, scale, q_rows, k_rows, hkv, dk_rule=True):
     """q, do [Tq,Hq,D], dk, dv [Tk,Hkv,D] float64; lse [Hq,Tq]; o [Tq,Hq,D];
-    q_rows / k_rows: lists of token slices per sequence."""
+    sinks: one logit per head ([Hq], several sinks as their log-sum-exp) or
+    None; q_rows / k_rows: lists of token slices per sequence.  The dV rule
+    holds for any logits; the dK rule needs d(logit)/d<q,k> = scale (not under
+    a soft cap)."""
     hq = q.shape[1]
     G = hq // hkv
     for qs, ks in zip(q_rows, k_rows):
@@ -50,6 +53,8 @@ def _sum_rules(name, q, do, dk, dv, lse, o, sinks, scale, q_rows, k_rows, hkv):
             wv = int(np.argmax(np.abs(got_dv - exp_dv) - tol_v))
             assert np.all(np.abs(got_dv - exp_dv) <= tol_v), "%s: sum rule dV (rows %s, g %d, dim %d: %g vs %g, tol %g)" % (
                 name, qs, g, wv, got_dv[wv], exp_dv[wv], tol_v[wv])
+            if not dk_rule:
+                continue
             wk = int(np.argmax(np.abs(got_dk - exp_dk) - tol_k))
             assert np.all(np.abs(got_dk - exp_dk) <= tol_k), "%s: sum rule dK (rows %s, g %d, dim %d: %g vs %g, tol %g)" % (
                 name, qs, g, wk, got_dk[wk], exp_dk[wk], tol_k[wk])
@@ -78,22 +83,29 @@ def _check_cols(name, p, dk, dv, s, g, cols, k0):
 
 
 def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bwd, n_rows, col_slices,
-                  n_cols):
+                  n_cols, softcap=0.0, alibi=None, sink_table=None, dsink_rows=True):
+    """sinks: one per head; sink_table: [hq, n] sinks instead; softcap, alibi
+    ([hq] slopes): the score variants; dsink_rows: check d(sink) against the
+    oracle over every row (slow for long causal rows with no window)."""
     print("case", name, flush=True)
     shapes = [(B, S_q, hq, d), (B, S_k, hkv, d), (B, S_k, hkv, d)] + ([(B, S_q, hq, d)] if bwd else [])
     tens = synth.device_normal(seed, shapes)
     q, k, v = tens[:3]
+    if sink_table is not None:
+        sinks = True
     inp = dict(q=synth.host_bits(q), k=synth.host_bits(k), v=synth.host_bits(v),
                dout=synth.host_bits(tens[3]) if bwd else None,
-               sinks=np.random.default_rng(seed).standard_normal(hq, dtype=np.float32) if sinks else None)
+               sinks=(sink_table if sink_table is not None else
+                      np.random.default_rng(seed).standard_normal(hq, dtype=np.float32)) if sinks else None)
     scale = synth.default_scale(d)
     s_dev = torch.from_numpy(inp["sinks"]).cuda() if sinks else None
-    o, lse = ea.attn_fwd(q, k, v, causal=causal, window=window, sinks=s_dev)
+    kw = dict(causal=causal, window=window, sinks=s_dev, softcap=softcap,
+              alibi_slopes=None if alibi is None else torch.from_numpy(alibi).cuda())
+    o, lse = ea.attn_fwd(q, k, v, **kw)
     grads = None
     if bwd:
-        grads = ea.attn_bwd(q, k, v, o, lse, tens[3], causal=causal, window=window, sinks=s_dev,
-                            grad_dtype=torch.float32)
-        g16 = ea.attn_bwd(q, k, v, o, lse, tens[3], causal=causal, window=window, sinks=s_dev)
+        grads = ea.attn_bwd(q, k, v, o, lse, tens[3], grad_dtype=torch.float32, **kw)
+        g16 = ea.attn_bwd(q, k, v, o, lse, tens[3], **kw)
         torch.cuda.synchronize()
         _input_dtype_grads_match(name, grads[:3], g16[:3])
         del g16
@@ -104,7 +116,7 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
     oh = host(o).reshape(Tq, hq, d)
     lh = host(lse).transpose(1, 0, 2).reshape(hq, Tq)
     p = oracle.batched(inp["q"], inp["k"], inp["v"], scale, causal=causal, window=window,
-                       dout=inp["dout"], sinks=inp["sinks"])
+                       dout=inp["dout"], sinks=inp["sinks"], softcap=softcap, alibi=alibi)
     rng = np.random.default_rng(seed + 1000)
     seqs = rng.integers(0, B, n_rows)
     heads = rng.integers(0, hq, n_rows)
@@ -129,7 +141,7 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
     g_ = int(rng.integers(0, hkv))
     cols = np.unique(np.r_[rng.integers(0, S_k, n_cols), 0, S_k - 1])
     _check_cols(name + "[cols]", p, dkh, dvh, s_, g_, cols, s_ * S_k)
-    if sinks:
+    if sinks and dsink_rows:
         # d(loss)/d(sink_h) = -sum over every row of head h of (1 - g_i) D_i
         sa, ha, ra = (a.ravel() for a in np.meshgrid(np.arange(B), np.arange(hq), np.arange(S_q),
                                                       indexing="ij"))
@@ -137,12 +149,21 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
         terms = -(1.0 - r["gate"]) * r["delta"]
         ref_ds = np.bincount(ha, weights=terms, minlength=hq)
         mag = np.bincount(ha, weights=np.abs(terms), minlength=hq)
+        tab = p.sink_table()  # several sinks per head: each takes its softmax share
+        share = np.exp(tab - tab.max(axis=1, keepdims=True))
+        share /= share.sum(axis=1, keepdims=True)
+        ref_ds = (ref_ds[:, None] * share).reshape(np.shape(inp["sinks"]))
+        mag = (mag[:, None] * share).reshape(np.shape(inp["sinks"]))
         err = np.abs(host(grads[3]) - ref_ds)
         assert np.all(err <= 2e-2 + 1e-3 * mag), (err.max(), mag.max())
+    one_sink = None
+    if sinks:
+        tab = p.sink_table()
+        one_sink = tab.max(axis=1) + np.log(np.exp(tab - tab.max(axis=1, keepdims=True)).sum(axis=1))
     _sum_rules(name, synth.bits_to_f32(inp["q"]).reshape(Tq, hq, d).astype(np.float64),
                synth.bits_to_f32(inp["dout"]).reshape(Tq, hq, d).astype(np.float64), dkh, dvh, lh, oh,
-               inp["sinks"], scale, [slice(b * S_q, (b + 1) * S_q) for b in range(B)],
-               [slice(b * S_k, (b + 1) * S_k) for b in range(B)], hkv)
+               one_sink, scale, [slice(b * S_q, (b + 1) * S_q) for b in range(B)],
+               [slice(b * S_k, (b + 1) * S_k) for b in range(B)], hkv, dk_rule=softcap == 0.0)
 
 
 def test_config2_causal_prefill():
@@ -152,6 +173,23 @@ def test_config2_causal_prefill():
 
 def test_config3_gqa_window_sinks():
     _batched_case("cfg3", 3, 2, 8192, 8192, 32, 8, 128, True, (127, 0), True, True, 1024, [(1, 7)], 256)
+
+
+def test_headdim256_causal_prefill():
+    """The head-dim sweep's largest width (256-wide kernels), at the sweep's shape."""
+    _batched_case("d256", 6, 4, 2048, 2048, 16, 16, 256, True, (-1, -1), False, True, 512, [(2, 9)], 128)
+
+
+def test_headdim96_padded_causal_prefill():
+    """A padded head dim (96 on the 128-wide kernels) at the sweep's shape."""
+    _batched_case("d96", 7, 4, 2048, 2048, 16, 16, 96, True, (-1, -1), False, True, 512, [(1, 4)], 128)
+
+
+def test_variants_causal_prefill():
+    """Soft cap 50 with ALiBi and 4 sinks per head at the variant benchmark's shape."""
+    _batched_case("cap_alibi_sinks4", 8, 4, 2048, 2048, 16, 16, 128, True, (-1, -1), True, True, 512, [(3, 2)],
+                  128, softcap=50.0, alibi=synth.alibi_slopes(16), sink_table=synth.sink_table(8, 16, 4),
+                  dsink_rows=False)
 
 
 def test_config5_decode_split_kv():
