@@ -23,7 +23,7 @@ EXPORTED = (
     "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
     "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
     "attn_fwd_varlen", "attn_fwd_varlen_workspace_size", "attn_bwd_varlen",
-    "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable",
+    "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable", "attn_timing_select",
     "attn_timing_read",
 )
 KERNELS = ("fwd", "fwd_combine", "bwd_dsink", "bwd_dq", "bwd_dkdv")
@@ -73,6 +73,7 @@ def load_library():
                                     vp, vp, i32, vp, sz, vp]
     lib.attn_bwd_varlen_workspace_size.argtypes = [P, i32, i64, i64, i32, i32, i32]
     lib.attn_timing_enable.argtypes = [i32]
+    lib.attn_timing_select.argtypes = [ctypes.c_uint32]
     lib.attn_timing_read.argtypes = [i32, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]
     for name in EXPORTED:
         if name.endswith("workspace_size"):
@@ -93,9 +94,13 @@ def version() -> int:
     return int(load_library().attn_version())
 
 
-def attn_timing_enable(on: bool = True) -> None:
-    """Start (or stop) bracketing every library kernel launch with HIP events."""
-    _check(load_library().attn_timing_enable(1 if on else 0))
+def attn_timing_enable(on: bool = True, kernels=None) -> None:
+    """Start (or stop) bracketing library kernel launches with HIP events:
+    every kernel, or only those named in ``kernels`` (names from KERNELS)."""
+    lib = load_library()
+    mask = (1 << len(KERNELS)) - 1 if kernels is None else sum(1 << KERNELS.index(k) for k in kernels)
+    _check(lib.attn_timing_select(mask))
+    _check(lib.attn_timing_enable(1 if on else 0))
 
 
 def attn_timing_read(kernel: str):

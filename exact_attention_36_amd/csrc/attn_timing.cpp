@@ -18,6 +18,7 @@ struct Rec {
 };
 
 bool g_on = false;
+uint32_t g_mask = (1u << K_COUNT) - 1;  // kernels to time while on
 bool g_overflow = false;
 std::vector<Rec> g_pool;  // events, created on first enable
 int g_used = 0;
@@ -26,7 +27,7 @@ int g_open = -1;          // record whose start is recorded but not its stop
 }  // namespace
 
 void timing_begin(int kid, hipStream_t st) {
-  if (!g_on) return;
+  if (!g_on || !((g_mask >> kid) & 1u)) return;
   if (g_used >= (int)g_pool.size()) {
     g_overflow = true;
     g_open = -1;
@@ -62,6 +63,12 @@ extern "C" attn_status attn_timing_enable(int32_t on) {
   g_used = 0;
   g_open = -1;
   g_overflow = false;
+  return ATTN_OK;
+}
+
+extern "C" attn_status attn_timing_select(uint32_t kernel_mask) {
+  if (kernel_mask >> K_COUNT) return ATTN_EINVAL;
+  g_mask = kernel_mask;
   return ATTN_OK;
 }
 

@@ -210,9 +210,13 @@ size_t attn_bwd_varlen_workspace_size(const attn_params *params, int32_t num_seq
  * stream.  attn_timing_read synchronises on the recorded events and returns,
  * for one kernel, the number of launches and their total duration in
  * milliseconds since the last attn_timing_enable call; it returns
- * ATTN_EINVAL for an unknown kernel id.  Not thread safe: enable, run, read
- * from one thread.  At most 16384 launches are recorded per enable (later
- * ones are not timed; attn_timing_read then reports ATTN_ENOTSUP).
+ * ATTN_EINVAL for an unknown kernel id.  attn_timing_select limits the
+ * timing to the kernels whose bit (1 << attn_kernel_id) is set in
+ * kernel_mask (the others launch with no events around them; the default
+ * mask times every kernel); it returns ATTN_EINVAL for bits past
+ * ATTN_KERNEL_COUNT.  Not thread safe: enable, run, read from one thread.
+ * At most 16384 launches are recorded per enable (later ones are not timed;
+ * attn_timing_read then reports ATTN_ENOTSUP).
  */
 typedef enum {
     ATTN_KERNEL_FWD = 0,          /* fused forward */
@@ -223,6 +227,7 @@ typedef enum {
     ATTN_KERNEL_COUNT = 5
 } attn_kernel_id;
 attn_status attn_timing_enable(int32_t on);
+attn_status attn_timing_select(uint32_t kernel_mask);
 attn_status attn_timing_read(int32_t kernel, int64_t *launches, double *total_ms);
 
 /* Message describing the last non-OK status returned on this thread. */
