@@ -48,12 +48,9 @@ def visible_pairs(B, sq, sk, hq, causal, window):
     return int(keep.sum()) * B * hq
 
 
-KERNEL_SOURCES = {
-    "fwd": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
-    "fwd_decode": ["exact_attention_36_amd/csrc/attn_fwd.hip"],
-    "bwd_dkdv": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
-    "bwd_dq": ["exact_attention_36_amd/csrc/attn_bwd.hip"],
-}
+_FWD = ["exact_attention_36_amd/csrc/attn_fwd_kernels.h", "exact_attention_36_amd/csrc/attn_fwd.hip"]
+_BWD = ["exact_attention_36_amd/csrc/attn_bwd_kernels.h", "exact_attention_36_amd/csrc/attn_bwd.hip"]
+KERNEL_SOURCES = {"fwd": _FWD, "fwd_decode": _FWD, "bwd_dkdv": _BWD, "bwd_dq": _BWD}
 COMMON_SOURCES = ["exact_attention_36_amd/csrc/attn_device.h", "exact_attention_36_amd/csrc/attn_common.h",
                   "exact_attention_36_amd/csrc/attn_kernels.h", "exact_attention_36_amd/csrc/attn_api.cpp"]
 
