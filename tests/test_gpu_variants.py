@@ -219,3 +219,23 @@ def test_backward_is_deterministic_with_sinks():
         torch.cuda.synchronize()
         for a, b in zip(first, again):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_zero_alibi_slopes_equal_plain_kernels(d):
+    """ALiBi slopes of 0 add -0 * |dist| to every score: the ALiBi instances
+    then give the plain instances' results bit for bit (forward, every
+    gradient, split-KV decode included)."""
+    for B, sq, sk in ((2, 150, 230), (1, 3, 4000)):
+        inp = synth.batched_inputs(d + sk, B, sq, sk, 4, 2, d, grads=True, sinks=True)
+        q, k, v, do = (dev_tensor(inp[n]) for n in ("q", "k", "v", "dout"))
+        kw = dict(causal=True, sinks=_dev(inp["sinks"]))
+        zero = torch.zeros(4, dtype=torch.float32, device="cuda")
+        o, lse = ea.attn_fwd(q, k, v, **kw)
+        oz, lsez = ea.attn_fwd(q, k, v, alibi_slopes=zero, **kw)
+        g = ea.attn_bwd(q, k, v, o, lse, do, **kw)
+        gz = ea.attn_bwd(q, k, v, o, lse, do, alibi_slopes=zero, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o, oz) and torch.equal(lse, lsez), (d, sq, sk)
+        for a, b in zip(g, gz):
+            assert torch.equal(a, b), (d, sq, sk)
