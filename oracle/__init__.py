@@ -168,27 +168,40 @@ class Problem:
         return s
 
 
-def batched(q, k, v, scale, causal=False, window=(-1, -1), dout=None, sinks=None, dtype="bf16", **variants):
-    """Wrap [B,S,H,D] uint16 arrays as a Problem (sequence b starts at token b*S).
+def _used(slot_len, seqused):
+    """Lengths a slot uses: its first seqused[b] tokens (fa4-jax page, varlen
+    semantics paragraph: seqused_q / seqused_k), or all of them."""
+    slot_len = np.asarray(slot_len, np.int64)
+    if seqused is None:
+        return slot_len
+    return np.minimum(np.maximum(np.asarray(seqused, np.int64), 0), slot_len)
+
+
+def batched(q, k, v, scale, causal=False, window=(-1, -1), dout=None, sinks=None, dtype="bf16", seqused_q=None,
+            seqused_k=None, **variants):
+    """Wrap [B,S,H,D] uint16 arrays as a Problem (sequence b starts at token b*S
+    and uses its first seqused_q[b] / seqused_k[b] tokens when given).
     ``variants``: softcap, alibi, sinks_shared (see Problem)."""
     B, sq, hq, d = q.shape
     sk = k.shape[1]
     return Problem(
         q=q.reshape(B * sq, hq, d), k=k.reshape(B * sk, k.shape[2], d),
         v=v.reshape(B * sk, v.shape[2], d),
-        q_start=np.arange(B, dtype=np.int64) * sq, q_len=np.full(B, sq, np.int64),
-        k_start=np.arange(B, dtype=np.int64) * sk, k_len=np.full(B, sk, np.int64),
+        q_start=np.arange(B, dtype=np.int64) * sq, q_len=_used(np.full(B, sq), seqused_q),
+        k_start=np.arange(B, dtype=np.int64) * sk, k_len=_used(np.full(B, sk), seqused_k),
         scale=scale, causal=causal, window=window,
         dout=None if dout is None else dout.reshape(B * sq, hq, d), sinks=sinks, dtype=dtype, **variants)
 
 
 def varlen(q, k, v, cu_q, cu_k, scale, causal=False, window=(-1, -1), dout=None, sinks=None,
-           dtype="bf16", **variants):
-    """Wrap packed [T,H,D] arrays plus int cu_seqlens [N+1] as a Problem."""
+           dtype="bf16", seqused_q=None, seqused_k=None, **variants):
+    """Wrap packed [T,H,D] arrays plus int cu_seqlens [N+1] as a Problem
+    (sequence i uses the first seqused_q[i] / seqused_k[i] tokens of its slot
+    when given)."""
     cu_q = np.asarray(cu_q, np.int64)
     cu_k = np.asarray(cu_k, np.int64)
-    return Problem(q=q, k=k, v=v, q_start=cu_q[:-1], q_len=np.diff(cu_q),
-                   k_start=cu_k[:-1], k_len=np.diff(cu_k), scale=scale, causal=causal,
+    return Problem(q=q, k=k, v=v, q_start=cu_q[:-1], q_len=_used(np.diff(cu_q), seqused_q),
+                   k_start=cu_k[:-1], k_len=_used(np.diff(cu_k), seqused_k), scale=scale, causal=causal,
                    window=window, dout=dout, sinks=sinks, dtype=dtype, **variants)
 
 

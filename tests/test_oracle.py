@@ -562,3 +562,40 @@ def test_several_sinks_equal_their_logsumexp():
     tiled = oracle.full(p)
     np.testing.assert_allclose(shared["o"], tiled["o"], rtol=1e-14)
     np.testing.assert_allclose(shared["dsinks"], tiled["dsinks"].sum(axis=0), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- T15: used lengths (seqused)
+
+def test_seqused_equals_compacted_problem():
+    """Slots that use only their first seqused_q / seqused_k tokens equal, value
+    for value, the packed problem built from those tokens alone (copied out by
+    plain slicing); rows of unused queries and keys get nothing (zeros here),
+    and the band aligns to the used lengths."""
+    rng = np.random.default_rng(17)
+    slot_q, slot_k = [9, 4, 0, 12], [11, 6, 5, 12]
+    used_q, used_k = [5, 4, 0, 1], [11, 0, 3, 7]
+    cq = np.concatenate([[0], np.cumsum(slot_q)])
+    ck = np.concatenate([[0], np.cumsum(slot_k)])
+    q = rng.standard_normal((cq[-1], 4, 8))
+    k = rng.standard_normal((ck[-1], 2, 8))
+    v = rng.standard_normal((ck[-1], 2, 8))
+    do = rng.standard_normal((cq[-1], 4, 8))
+    s = rng.standard_normal(4)
+    p = oracle.varlen(q, k, v, cq, ck, 0.3, causal=True, window=(4, -1), dout=do, sinks=s, dtype="f64",
+                      seqused_q=used_q, seqused_k=[99, 0, 3, 7])  # above the slot: the whole slot
+    r = oracle.full(p)
+    assert list(p.k_len) == used_k
+    qi = np.concatenate([np.arange(cq[b], cq[b] + used_q[b]) for b in range(4)])
+    ki = np.concatenate([np.arange(ck[b], ck[b] + used_k[b]) for b in range(4)])
+    cq2 = np.concatenate([[0], np.cumsum(used_q)])
+    ck2 = np.concatenate([[0], np.cumsum(used_k)])
+    c = oracle.full(oracle.varlen(q[qi], k[ki], v[ki], cq2, ck2, 0.3, causal=True, window=(4, -1), dout=do[qi],
+                                  sinks=s, dtype="f64"))
+    np.testing.assert_array_equal(r["o"][qi], c["o"])
+    np.testing.assert_array_equal(r["lse"][:, qi], c["lse"])
+    np.testing.assert_array_equal(r["dq"][qi], c["dq"])
+    np.testing.assert_array_equal(r["dk"][ki], c["dk"])
+    np.testing.assert_array_equal(r["dv"][ki], c["dv"])
+    np.testing.assert_array_equal(r["dsinks"], c["dsinks"])
+    unused_k = np.setdiff1d(np.arange(ck[-1]), ki)
+    assert not r["dk"][unused_k].any() and not r["dv"][unused_k].any()
