@@ -45,6 +45,7 @@ class attn_params(ctypes.Structure):
         ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
         ("sinks", ctypes.c_void_p), ("num_sinks", ctypes.c_int32), ("sinks_shared", ctypes.c_int32),
         ("softcap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p), ("alibi_per_batch", ctypes.c_int32),
+        ("seqused_q", ctypes.c_void_p), ("seqused_k", ctypes.c_void_p),
     ]
 
 
@@ -125,9 +126,11 @@ def _ptr(t):
 
 
 def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
-                alibi_slopes=None, sinks_shared=False, nseq=None) -> attn_params:
+                alibi_slopes=None, sinks_shared=False, nseq=None, seqused_q=None,
+                seqused_k=None) -> attn_params:
     """sinks: fp32 [Hq] (one per head), [Hq, n], or [n] with sinks_shared (one row
-    for every head); alibi_slopes: fp32 [Hq] or [B, Hq]; softcap: 0 = off."""
+    for every head); alibi_slopes: fp32 [Hq] or [B, Hq]; softcap: 0 = off;
+    seqused_q, seqused_k: int32 [B] (or [num_seqs]) used lengths per slot."""
     hq = q.shape[-2]
     if sinks is not None:
         ok = sinks.dim() == 1 if sinks_shared else (tuple(sinks.shape) == (hq,) or
@@ -156,6 +159,10 @@ def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
     p.softcap = float(softcap)
     p.alibi_slopes = _ptr(alibi_slopes)
     p.alibi_per_batch = 1 if alibi_slopes is not None and alibi_slopes.dim() == 2 else 0
+    for name, t in (("seqused_q", seqused_q), ("seqused_k", seqused_k)):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (nseq,) or not t.is_contiguous()):
+            raise ValueError("%s must be contiguous int32 [%s]; got %s %s" % (name, nseq, tuple(t.shape), t.dtype))
+        setattr(p, name, _ptr(t))
     return p
 
 
@@ -173,13 +180,13 @@ def _workspace(nbytes, dev):
 
 
 def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
-             alibi_slopes=None, sinks_shared=False, out=None, lse=None):
+             alibi_slopes=None, sinks_shared=False, seqused_q=None, seqused_k=None, out=None, lse=None):
     """Batched forward: q [B,Sq,Hq,D], k, v [B,Sk,Hkv,D] -> (o, lse [B,Hq,Sq] fp32)."""
     lib = load_library()
     B, sq, hq, d = q.shape
     sk = k.shape[1]
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
-                    nseq=B)
+                    nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, hq, sq), dtype=torch.float32, device=q.device) if lse is None else lse
     n = lib.attn_fwd_workspace_size(ctypes.byref(p), B, sq, sk)
@@ -190,14 +197,14 @@ def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
-             alibi_slopes=None, sinks_shared=False,
+             alibi_slopes=None, sinks_shared=False, seqused_q=None, seqused_k=None,
              grad_dtype=None):
     """Batched backward -> (dq, dk, dv, dsinks or None)."""
     lib = load_library()
     B, sq, hq, d = q.shape
     sk = k.shape[1]
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
-                    nseq=B)
+                    nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
     gd = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gd, device=q.device)
     dk = torch.empty(k.shape, dtype=gd, device=q.device)
@@ -212,15 +219,15 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, s
 
 
 def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causal=False, window=(-1, -1),
-                     sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None, sinks_shared=False, out=None,
-                     lse=None):
+                     sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None, sinks_shared=False, seqused_q=None,
+                     seqused_k=None, out=None, lse=None):
     """Forward over a KV cache: q [B,Sq,Hq,D]; cache_seqlens int32 [B] (used keys per slot);
     k_cache, v_cache [B,capacity,Hkv,D], or pages [num_blocks,page,Hkv,D] with
     block_table int32 [B,max_blocks] -> (o, lse [B,Hq,Sq])."""
     lib = load_library()
     B, sq, hq, d = q.shape
     p = make_params(q, k_cache, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
-                    nseq=B)
+                    nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, hq, sq), dtype=torch.float32, device=q.device) if lse is None else lse
     if block_table is not None:
@@ -237,14 +244,14 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causa
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=False,
                     window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None,
-                    sinks_shared=False, out=None, lse=None):
+                    sinks_shared=False, seqused_q=None, seqused_k=None, out=None, lse=None):
     """Packed forward: q [Tq,Hq,D], k, v [Tk,Hkv,D], int32 cu_seqlens [N+1] -> (o, lse [Hq,Tq])."""
     lib = load_library()
     tq, hq, d = q.shape
     tk = k.shape[0]
     n = cu_seqlens_q.shape[0] - 1
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
-                    nseq=n)
+                    nseq=n, seqused_q=seqused_q, seqused_k=seqused_k)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device) if lse is None else lse
     nb = lib.attn_fwd_varlen_workspace_size(ctypes.byref(p), n, tq, tk, max_seqlen_q, max_seqlen_k)
@@ -257,14 +264,14 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                     causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None,
-                    sinks_shared=False, grad_dtype=None):
+                    sinks_shared=False, seqused_q=None, seqused_k=None, grad_dtype=None):
     """Packed backward -> (dq, dk, dv, dsinks or None)."""
     lib = load_library()
     tq, hq, d = q.shape
     tk = k.shape[0]
     n = cu_seqlens_q.shape[0] - 1
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
-                    nseq=n)
+                    nseq=n, seqused_q=seqused_q, seqused_k=seqused_k)
     gd = q.dtype if grad_dtype is None else grad_dtype
     dq = torch.empty(q.shape, dtype=gd, device=q.device)
     dk = torch.empty(k.shape, dtype=gd, device=q.device)

@@ -107,6 +107,8 @@ SeqArgs seq_args(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k,
   s.hkv = p->heads_kv;
   s.group = p->heads_q / p->heads_kv;
   s.dg = p->head_dim;
+  s.seqused_q = p->seqused_q;
+  s.seqused_k = p->seqused_k;
   s.group_magic = s.group >= 2 ? (uint32_t)((((uint64_t)1 << 32) + s.group - 1) / s.group) : 0u;
   s.causal = p->causal;
   s.wl = p->window_left;
@@ -188,7 +190,7 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   const bool packed = cu_q != nullptr;
   FwdArgs a{};
   a.s = seq_args(p, cu_q, cu_k, nseq, sq, sk, total_q);
-  a.s.seqused_k = kvc.seqused_k;
+  if (kvc.seqused_k) a.s.seqused_k = kvc.seqused_k;  // the cache's used lengths
   a.s.block_table = kvc.block_table;
   a.s.page_rows = kvc.page_rows;
   a.s.pages_per_seq = kvc.pages_per_seq;

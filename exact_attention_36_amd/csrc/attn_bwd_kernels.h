@@ -424,14 +424,16 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
   const SeqInfo si = seq_info(a.s, seq);
   const int j0 = nb * BN;
-  if (j0 >= si.lk) return;  // idle slot of the packed grid
+  if (j0 >= si.lk_slot) return;  // idle slot of the packed grid
+  // (a block past the used keys but inside the slot visits no query block and
+  // writes the zero gradients of its keys)
   const int prows = si.lq * G;
   const Band band(a.s, si);
   const QBand qband(a.s, si);
   const int j_last = min(j0 + BN, si.lk) - 1;
   const int q_lo = qband.qmin(j0), q_hi = qband.qmax(j_last);
   int pb_begin = 0, pb_end = 0;  // packed q-blocks of BM rows
-  if (q_hi >= q_lo && prows > 0) {
+  if (j0 < si.lk && q_hi >= q_lo && prows > 0) {
     pb_begin = (q_lo * G) / BM;
     pb_end = ((q_hi + 1) * G - 1) / BM + 1;
   }
@@ -443,7 +445,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int64_t qbase_e = ((int64_t)si.q0 * a.s.hq + (int64_t)g * G) * dg;
   const uint32_t qbytes = si.lq > 0 ? (uint32_t)(((int64_t)(si.lq - 1) * qrow + (int64_t)G * dg) * 2) : 0u;
   const int64_t kbase_e = ((int64_t)si.k0 * a.s.hkv + g) * dg;
-  const uint32_t kbytes = (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2);
+  const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2) : 0u;
+  // dK, dV are stored for every key row of the slot (zero past the used keys)
+  const uint32_t kbytes_slot = (uint32_t)(((int64_t)(si.lk_slot - 1) * krow + dg) * 2);
   const i32x4 rq16 = make_rsrc_words((F16 ? (const uint16_t*)a.q : (const uint16_t*)a.q16) + qbase_e, qbytes);
   const i32x4 rdo = make_rsrc_words((const uint16_t*)a.dout + qbase_e, qbytes);
   const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
@@ -688,11 +692,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     char* const stg = smem + wave * 2 * 32 * ROWB;  // this wave's dK and dV rows
     auto row_off = [&](int r) {
       const int kk = j0 + wave * 32 + r;
-      return kk < si.lk ? (uint32_t)((int64_t)kk * krow * 2) : DROP_ROW;
+      return kk < si.lk_slot ? (uint32_t)((int64_t)kk * krow * 2) : DROP_ROW;
     };
-    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes), row_off, dg);
-    store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes), row_off, dg);
-  } else if (my_key < si.lk) {
+    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes_slot), row_off, dg);
+    store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes_slot), row_off, dg);
+  } else if (my_key < si.lk_slot) {
     const int64_t ob = ((int64_t)(si.k0 + my_key) * a.s.hkv + g) * dg;
 #pragma unroll
     for (int d = 0; d < DB; d++)

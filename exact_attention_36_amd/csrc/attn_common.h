@@ -17,22 +17,27 @@ __device__ __forceinline__ int div_group(int n, const SeqArgs& s) {
 }
 
 struct SeqInfo {
-  int q0, lq, k0, lk;  // first token and length of the sequence in q and in k/v
+  int q0, lq, k0, lk;  // first token and used length of the sequence in q and in k/v
+  int lk_slot;         // key rows the slot holds (>= lk; dK/dV rows past lk are zero)
 };
 
 __device__ __forceinline__ SeqInfo seq_info(const SeqArgs& s, int seq) {
   SeqInfo r;
+  int lq_slot;
   if (s.cu_q) {
     r.q0 = s.cu_q[seq];
-    r.lq = s.cu_q[seq + 1] - r.q0;
+    lq_slot = s.cu_q[seq + 1] - r.q0;
     r.k0 = s.cu_k[seq];
-    r.lk = s.cu_k[seq + 1] - r.k0;
+    r.lk_slot = s.cu_k[seq + 1] - r.k0;
   } else {
     r.q0 = seq * s.sq;
-    r.lq = s.sq;
+    lq_slot = s.sq;
     r.k0 = seq * s.sk;
-    r.lk = s.seqused_k ? s.seqused_k[seq] : s.sk;  // a KV-cache slot: its used keys
+    r.lk_slot = s.sk;
   }
+  // used lengths, read as given but kept inside the slot
+  r.lq = s.seqused_q ? min(max(s.seqused_q[seq], 0), lq_slot) : lq_slot;
+  r.lk = s.seqused_k ? min(max(s.seqused_k[seq], 0), r.lk_slot) : r.lk_slot;
   return r;
 }
 

@@ -33,9 +33,13 @@ struct SeqArgs {
                          // kernel's tile D; tile columns past it are zero and never stored
   uint32_t group_magic;  // ceil(2^32 / group) for group >= 2 (fast division, see div_group)
   int32_t causal, wl, wr;  // window bounds, -1 = unbounded
-  // KV cache (batched forward only): slot seq uses its first seqused_k[seq]
-  // keys of sk; with a block table, key j of slot seq is row j % page_rows of
-  // page block_table[seq * pages_per_seq + j / page_rows] ([page][row][hkv][D])
+  // Used lengths: slot seq (a batch entry, or a packed sequence whose tokens
+  // cu_seqlens allot) uses its first seqused_q[seq] queries and
+  // seqused_k[seq] keys (fa4-jax page, varlen semantics paragraph; the KV
+  // cache's cache_seqlens).  With a block table (KV-cache forward), key j of
+  // slot seq is row j % page_rows of page
+  // block_table[seq * pages_per_seq + j / page_rows] ([page][row][hkv][D]).
+  const int32_t* seqused_q;    // [nseq] or nullptr
   const int32_t* seqused_k;    // [nseq] or nullptr
   const int32_t* block_table;  // [nseq][pages_per_seq] or nullptr
   int32_t page_rows, pages_per_seq;

@@ -39,6 +39,9 @@
  *    ALiBi bias -slope_h * |i + Lk - Lq - j| (alibi_slopes in the
  *    flash_attn_func docstring of the same README).  Gradients follow the
  *    chain rule through both.
+ *  - Used lengths (fa4-jax page, varlen semantics paragraph: seqused_q,
+ *    seqused_k): a batch entry or packed sequence may use only the first
+ *    tokens of its slot; see attn_params.
  *  - Packed variable-length batches: [T, H, D] tensors with int32 offsets
  *    cu_seqlens [N+1] from 0 to T; attention never crosses sequences; the
  *    mask applies per sequence with that sequence's own Lq, Lk; zero-length
@@ -116,6 +119,16 @@ typedef struct {
                                -slope * |i + Lk - Lq - j| to the logit of
                                query i and key j, after the soft cap */
     int32_t alibi_per_batch; /* 0 or 1, see alibi_slopes */
+    const int32_t *seqused_q; /* device int32 [B or num_seqs] or NULL: slot b uses its
+                               first seqused_q[b] queries; the other rows' outputs,
+                               lse and dq are unspecified (not written) */
+    const int32_t *seqused_k; /* device int32 [B or num_seqs] or NULL: slot b uses its
+                               first seqused_k[b] keys; the others are invisible and
+                               their dk, dv are written as 0.  The causal/window band
+                               aligns to the used lengths.  Contents are not checked
+                               (like cu_seqlens); values outside [0, slot length] act
+                               as the nearest bound.  attn_fwd_kvcache's
+                               cache_seqlens replaces seqused_k */
 } attn_params;
 
 /*

@@ -84,3 +84,65 @@ def test_kvcache_paged_unsplit_rows_sampled():
     tok = seqs * sq + rows
     assert_close("paged_unsplit.o[rows]", host(o).reshape(B * sq, hq, d)[tok, heads], r["o"], "bf16")
     assert_lse("paged_unsplit.lse[rows]", host(lse).transpose(1, 0, 2).reshape(hq, B * sq)[heads, tok], r["lse"])
+
+
+SEQUSED = [
+    # id, packed, slot_q, slot_k, used_q, used_k, hq, hkv, d, causal, window, sinks, dtype
+    ("seqused_packed_gqa_sinks", True, [100, 7, 0, 300, 64], [150, 64, 20, 300, 64], [60, 7, 0, 1, 64],
+     [90, 0, 20, 129, 64], 4, 2, 128, True, (-1, -1), True, "bf16"),
+    ("seqused_packed_window_fp16", True, [33, 190], [64, 190], [33, 100], [50, 190], 2, 1, 64, True, (20, 0),
+     False, "fp16"),
+    ("seqused_batched_noncausal", False, [80] * 3, [200] * 3, [80, 33, 1], [200, 64, 5], 8, 2, 128, False,
+     (-1, -1), True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SEQUSED, ids=[c[0] for c in SEQUSED])
+def test_seqused_forward_backward(case):
+    """Slots that use only their first seqused_q / seqused_k tokens: the used
+    rows' O, lse, dQ, every key's dK, dV (zero for unused keys) and dsinks
+    against the oracle on the same slot layout; unused query rows are not
+    compared (unspecified)."""
+    name, packed, slot_q, slot_k, used_q, used_k, hq, hkv, d, causal, window, sinks, dt = case
+    print("case", name, flush=True)
+    seed = zlib.crc32(name.encode()) % 1000
+    if packed:
+        inp = synth.varlen_inputs(seed, slot_q, slot_k, hq, hkv, d, grads=True, sinks=sinks, dtype=dt)
+        p = oracle.varlen(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], scale_of(d), causal=causal,
+                          window=window, dout=inp["dout"], sinks=inp["sinks"], dtype=dt, seqused_q=used_q,
+                          seqused_k=used_k)
+        cq = np.asarray(inp["cu_q"])
+    else:
+        B, sq, sk = len(slot_q), slot_q[0], slot_k[0]
+        inp = synth.batched_inputs(seed, B, sq, sk, hq, hkv, d, grads=True, sinks=sinks, dtype=dt)
+        p = oracle.batched(inp["q"], inp["k"], inp["v"], scale_of(d), causal=causal, window=window,
+                           dout=inp["dout"], sinks=inp["sinks"], dtype=dt, seqused_q=used_q, seqused_k=used_k)
+        cq = np.arange(B + 1) * sq
+    ref = oracle.full(p)
+    q, k, v, do = (dev_tensor(inp[n], dt) for n in ("q", "k", "v", "dout"))
+    kw = dict(causal=causal, window=window, sinks=torch.from_numpy(inp["sinks"]).cuda() if sinks else None,
+              seqused_q=torch.tensor(used_q, dtype=torch.int32, device="cuda"),
+              seqused_k=torch.tensor(used_k, dtype=torch.int32, device="cuda"))
+    if packed:
+        cqd, ckd = torch.from_numpy(inp["cu_q"]).cuda(), torch.from_numpy(inp["cu_k"]).cuda()
+        o, lse = ea.attn_fwd_varlen(q, k, v, cqd, ckd, max(slot_q), max(slot_k), **kw)
+        dq, dk, dv, ds = ea.attn_bwd_varlen(q, k, v, o, lse, do, cqd, ckd, max(slot_q), max(slot_k),
+                                            grad_dtype=torch.float32, **kw)
+        oh, lh, dqh = host(o), host(lse), host(dq)
+        dkh, dvh = host(dk), host(dv)
+    else:
+        o, lse = ea.attn_fwd(q, k, v, **kw)
+        dq, dk, dv, ds = ea.attn_bwd(q, k, v, o, lse, do, grad_dtype=torch.float32, **kw)
+        oh = host(o).reshape(-1, hq, d)
+        lh = host(lse).transpose(1, 0, 2).reshape(hq, -1)
+        dqh = host(dq).reshape(-1, hq, d)
+        dkh, dvh = host(dk).reshape(-1, hkv, d), host(dv).reshape(-1, hkv, d)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(cq[b], cq[b] + used_q[b]) for b in range(len(used_q))]).astype(np.int64)
+    assert_close(name + ".o", oh[rows], ref["o"][rows], dt)
+    assert_lse(name + ".lse", lh[:, rows], ref["lse"][:, rows])
+    assert_close(name + ".dq", dqh[rows], ref["dq"][rows], "f32")
+    assert_close(name + ".dk", dkh, ref["dk"], "f32")  # unused keys: exactly 0 on both sides
+    assert_close(name + ".dv", dvh, ref["dv"], "f32")
+    if sinks:
+        assert np.abs(host(ds) - ref["dsinks"]).max() <= 2e-2 + 1e-3 * np.abs(ref["dsinks"]).max()
