@@ -11,7 +11,8 @@ HIP events on the library's stream (the other kernels run untimed there);
 Hq=64, Hkv=8) as K/V HBM GB/s;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
 prefill workload.  `--workload decode` runs only the decode shape;
-`--workload sweep`, `headdims` and `variants` print one line per shape.
+`--workload sweep`, `headdims` and `variants` print one line per shape;
+`--workload latency` times the launch-bound shape eagerly and as graph replays.
 """
 from __future__ import annotations
 
@@ -286,6 +287,56 @@ def run_variants(steps, warmup):
     return rows
 
 
+def run_latency(steps, warmup):
+    """Launch-bound shape (B=1, H=2, S=128, D=64, bf16, non-causal forward):
+    µs per call issued eagerly through the binding, per call of a HIP graph
+    that holds 20 calls (torch.cuda.graph; the library allocates nothing and
+    never synchronises, so it captures as is), and per replay of a graph that
+    holds one call (the graph launch's own cost)."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    q, k, v = synth.device_normal(1, [(1, 128, 2, 64)] * 3)
+    o, lse = ea.attn_fwd(q, k, v)
+    n = max(steps, 100) * 10
+    for _ in range(warmup * 10):
+        ea.attn_fwd(q, k, v, out=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        ea.attn_fwd(q, k, v, out=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / n
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ea.attn_fwd(q, k, v, out=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    def graph_of(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                ea.attn_fwd(q, k, v, out=o, lse=lse)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = n // calls
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * calls)
+    graph20_us = graph_of(20)
+    graph1_us = graph_of(1)
+    row = {"workload": "fwd B1 H2 S128 D64 bf16 non-causal", "calls": n, "eager_us_per_call": round(eager_us, 2),
+           "graph20_us_per_call": round(graph20_us, 2), "graph1_us_per_replay": round(graph1_us, 2)}
+    print(json.dumps(row), flush=True)
+    return row
+
+
 def cpu_baseline(inp, w, seconds_target=15.0):
     """Time the fp64 oracle on whole (batch, head) slices of the workload."""
     import numpy as np
@@ -398,12 +449,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
-    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "power"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
                          "sweep: context sweep over S = 512..16384 (one JSON line per shape); "
                          "headdims: causal prefill at D = 32..256 (one JSON line per head dim); "
                          "variants: causal prefill with soft cap / ALiBi / 4 sinks (one line each); "
+                         "latency: launch-bound forward, eager calls vs HIP graph replays; "
                          "power: socket power and shader clock (amd-smi) under the step's kernels")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -427,6 +479,9 @@ def main():
         return
     if args.workload == "variants":
         run_variants(args.steps, args.warmup)
+        return
+    if args.workload == "latency":
+        run_latency(args.steps, args.warmup)
         return
     if args.workload == "power":
         run_power(args.seconds)
