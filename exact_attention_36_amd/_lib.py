@@ -176,7 +176,9 @@ def _stream(dev):
 
 
 def _workspace(nbytes, dev):
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+    """Device workspace of nbytes, or None when the call needs none (the
+    library accepts a NULL workspace of size 0)."""
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=dev) if nbytes else None
 
 
 def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
