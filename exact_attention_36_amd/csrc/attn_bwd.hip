@@ -6,32 +6,35 @@
 namespace attn {
 
 // d(sink): each q head's gradient is the sum of the dQ workgroups' partial
-// sums, taken in workgroup order so that it is the same on every run; sink k
-// of a head gets the share 2^(s_hk log2 e - s2) of it (s2 = the head's sinks
-// as one logit), and a row of sinks shared by the heads sums the heads' in
-// head order.  One thread per output.
-__global__ void bwd_dsink_kernel(const BwdArgs a) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.dsink_count) return;
+// sums, and sink k of a head gets the share 2^(s_hk log2 e - s2) of it (s2 =
+// the head's sinks as one logit); a row of sinks shared by the heads gets the
+// sum over the heads.  One workgroup per output: thread t adds the partials
+// t, t + 256, ... of the head (heads in order for a shared row), then a tree
+// of fixed shape in LDS adds the threads' sums -- the same order on every run.
+constexpr int DSINK_THREADS = 256;
+__global__ __launch_bounds__(DSINK_THREADS) void bwd_dsink_kernel(const BwdArgs a) {
+  const int e = blockIdx.x, t = threadIdx.x;
   const int G = a.s.group, n = a.x.nsinks;
-  auto head_sum = [&](int h) {
+  const bool shared = a.x.sink_hstride == 0;
+  const int h0 = shared ? 0 : e / n, h1 = shared ? a.s.hq : h0 + 1, k = shared ? e : e - h0 * n;
+  float acc = 0.f;
+  for (int h = h0; h < h1; h++) {
     const int g = h / G;
     const float* src = a.dsink_part + (int64_t)g * a.nbq * G + (h - g * G);
-    float v = 0.f;
-    for (int b = 0; b < a.nbq; b++) v += src[(int64_t)b * G];
-    return v;
-  };
-  auto share = [&](int h, int k) {
-    if (n == 1) return 1.f;
-    return exp2_fast(fmaf(a.sinks[h * a.x.sink_hstride + k], LOG2E, -sink_log2(a.sinks, a.x, h)));
-  };
-  if (a.x.sink_hstride == 0) {
-    float v = 0.f;
-    for (int h = 0; h < a.s.hq; h++) v += head_sum(h) * share(h, e);
-    a.dsinks[e] = v;
-  } else {
-    const int h = e / n;
-    a.dsinks[e] = head_sum(h) * share(h, e - h * n);
+    for (int b = t; b < a.nbq; b += DSINK_THREADS) acc += src[(int64_t)b * G];
+  }
+  __shared__ float red[DSINK_THREADS];
+  red[t] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int w = DSINK_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) {
+    float share = 1.f;  // the same for every head of a shared row
+    if (n > 1) share = exp2_fast(fmaf(a.sinks[h0 * a.x.sink_hstride + k], LOG2E, -sink_log2(a.sinks, a.x, h0)));
+    a.dsinks[e] = red[0] * share;
   }
 }
 
@@ -51,7 +54,7 @@ hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st) {
   BwdArgs r = a;
   if (a.total_ctas_q == 0) r.nbq = 0;  // no dQ workgroup ran: every sum is 0
   timing_begin(K_BWD_DSINK, st);
-  hipLaunchKernelGGL(bwd_dsink_kernel, dim3((a.dsink_count + 255) / 256), dim3(256), 0, st, r);
+  hipLaunchKernelGGL(bwd_dsink_kernel, dim3(a.dsink_count), dim3(DSINK_THREADS), 0, st, r);
   timing_end(K_BWD_DSINK, st);
   return hipGetLastError();
 }
