@@ -235,6 +235,85 @@ def kvcache(q, k_cache, v_cache, cache_seqlens, scale, block_table=None, causal=
                    scale=scale, causal=causal, window=window, sinks=sinks, dtype=dtype, **variants)
 
 
+def rotary(x, cos, sin, positions, rotary_dim, interleaved):
+    """Rotary embedding of x [B, S, H, D] (float64) at integer positions [B, S]:
+    the first rotary_dim dims form rotary_dim/2 pairs, pair j of a token at
+    position p turns by the angle whose cosine and sine are cos[p, j],
+    sin[p, j]: (a, b) -> (a cos - b sin, a sin + b cos); the other dims are
+    unchanged.  Pairs are dims (2j, 2j+1) when interleaved, else (j, j +
+    rotary_dim/2) (vllm-project/flash-attention README on the GitHub search
+    page, flash_attn_with_kvcache: rotary_cos, rotary_sin, rotary_interleaved)."""
+    x = np.array(x, np.float64, copy=True)
+    half = rotary_dim // 2
+    c = np.asarray(cos, np.float64)[positions][:, :, None, :]  # [B, S, 1, half]
+    s = np.asarray(sin, np.float64)[positions][:, :, None, :]
+    if interleaved:
+        a, b = x[..., 0:rotary_dim:2].copy(), x[..., 1:rotary_dim:2].copy()
+        x[..., 0:rotary_dim:2] = a * c - b * s
+        x[..., 1:rotary_dim:2] = a * s + b * c
+    else:
+        a, b = x[..., :half].copy(), x[..., half:rotary_dim].copy()
+        x[..., :half] = a * c - b * s
+        x[..., half:rotary_dim] = a * s + b * c
+    return x
+
+
+def decode_array(dtype: str, bits) -> np.ndarray:
+    """bf16 / fp16 bit patterns -> float64, exactly (a bf16 value is the top
+    half of a binary32; fp16 is numpy's binary16)."""
+    bits = np.asarray(bits, np.uint16)
+    if dtype == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def encode(dtype: str, x) -> np.ndarray:
+    """float64 -> bf16 / fp16 bit patterns, rounded to nearest, ties to even,
+    in one rounding from the float64 value."""
+    x = np.asarray(x, np.float64)
+    if dtype == "fp16":
+        return x.astype(np.float16).view(np.uint16)
+    # bf16: the nearest of the two bf16 values around x (float32 keeps x
+    # between them: it has more precision than bf16)
+    lo = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint32)
+    hi = lo + 1
+    vlo = (lo << 16).view(np.float32).astype(np.float64)
+    vhi = (hi << 16).view(np.float32).astype(np.float64)
+    dlo, dhi = np.abs(x - vlo), np.abs(vhi - x)
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(np.isfinite(x), pick, lo)
+    return pick.astype(np.uint16)
+
+
+def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new, block_table=None, rotary_cos=None,
+                   rotary_sin=None, rotary_dim=0, rotary_interleaved=True, dtype="bf16"):
+    """The cache after writing new keys and values in place: token i of slot b
+    goes to key position cache_seqlens[b] + i of the slot (a row of k_cache[b],
+    or of the page the block table names), the keys rotated at that position
+    when rotary tables are given and rounded to the cache's dtype
+    (flash_attn_with_kvcache docstring: k, v, cache_seqlens, rotary_cos).
+    Arrays are bit patterns; returns new (k_cache, v_cache, seqlens)."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    B, sn = k_new.shape[0], k_new.shape[1]
+    lens = np.asarray(cache_seqlens, np.int64)
+    pos = lens[:, None] + np.arange(sn)[None, :]
+    kn = k_new
+    if rotary_cos is not None:
+        kn = encode(dtype, rotary(decode_array(dtype, k_new), rotary_cos, rotary_sin, pos, rotary_dim,
+                                  rotary_interleaved))
+    rows = kc.shape[1]
+    for b in range(B):
+        for i in range(sn):
+            p = int(pos[b, i])
+            if block_table is None:
+                slot, r = b, p
+            else:
+                slot, r = int(block_table[b][p // rows]), p % rows
+            kc[slot, r] = kn[b, i]
+            vc[slot, r] = v_new[b, i]
+    return kc, vc, (lens + sn).astype(np.int32)
+
+
 def visible(causal, left, right, lq, lk, i, j) -> bool:
     """The bottom-right aligned causal/window predicate, as the oracle applies it."""
     return bool(_load().oracle_visible(int(causal), int(left), int(right), int(lq), int(lk),

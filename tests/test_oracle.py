@@ -599,3 +599,121 @@ def test_seqused_equals_compacted_problem():
     np.testing.assert_array_equal(r["dsinks"], c["dsinks"])
     unused_k = np.setdiff1d(np.arange(ck[-1]), ki)
     assert not r["dk"][unused_k].any() and not r["dv"][unused_k].any()
+
+
+# ---------------------------------------------------------------- T16: rotary embedding, cache append
+
+def _rope_tables(n_pos, rotary_dim, base=10000.0):
+    theta = base ** (-np.arange(0, rotary_dim, 2) / rotary_dim)
+    ang = np.arange(n_pos)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+@pytest.mark.parametrize("interleaved", [True, False])
+def test_rotary_closed_forms(interleaved):
+    """cos 1, sin 0 is the identity; cos 0, sin 1 turns each pair (a, b) into
+    (-b, a); every pair keeps its length; dims past rotary_dim are unchanged."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((2, 5, 3, 64))
+    pos = np.tile(np.arange(5), (2, 1))
+    one, zero = np.ones((5, 16)), np.zeros((5, 16))
+    np.testing.assert_array_equal(oracle.rotary(x, one, zero, pos, 32, interleaved), x)
+    y = oracle.rotary(x, zero, one, pos, 32, interleaved)
+    if interleaved:
+        a, b, ya, yb = x[..., 0:32:2], x[..., 1:32:2], y[..., 0:32:2], y[..., 1:32:2]
+    else:
+        a, b, ya, yb = x[..., :16], x[..., 16:32], y[..., :16], y[..., 16:32]
+    np.testing.assert_array_equal(ya, -b)
+    np.testing.assert_array_equal(yb, a)
+    np.testing.assert_array_equal(y[..., 32:], x[..., 32:])
+    c, s_ = _rope_tables(5, 32)
+    z = oracle.rotary(x, c, s_, pos, 32, interleaved)
+    za, zb = (z[..., 0:32:2], z[..., 1:32:2]) if interleaved else (z[..., :16], z[..., 16:32])
+    np.testing.assert_allclose(za ** 2 + zb ** 2, a ** 2 + b ** 2, rtol=1e-12)
+
+
+@pytest.mark.parametrize("interleaved", [True, False])
+def test_rotary_scores_depend_on_relative_position(interleaved):
+    """With the rotary tables cos(p theta_j), sin(p theta_j), the score of a
+    query at p1 and a key at p2 depends only on p2 - p1 (a wrong sign or
+    pairing breaks this)."""
+    rng = np.random.default_rng(32)
+    q = rng.standard_normal((1, 1, 1, 64))
+    k = rng.standard_normal((1, 1, 1, 64))
+    c, s_ = _rope_tables(64, 48)
+    def score(p1, p2):
+        return float(np.sum(oracle.rotary(q, c, s_, np.array([[p1]]), 48, interleaved) *
+                            oracle.rotary(k, c, s_, np.array([[p2]]), 48, interleaved)))
+    for p1, p2, sh in ((3, 10, 17), (0, 0, 40), (20, 5, 11)):
+        np.testing.assert_allclose(score(p1, p2), score(p1 + sh, p2 + sh), rtol=1e-10, atol=1e-12)
+    assert abs(score(3, 10) - score(3, 11)) > 1e-6
+
+
+def test_rotary_halves_are_interleaved_pairs_permuted():
+    """The GPT-NeoX form (pairs j, j + R/2) is the interleaved form (pairs 2j,
+    2j + 1) applied to the dims permuted so that j -> 2j, j + R/2 -> 2j + 1."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((2, 4, 2, 64))
+    c, s_ = _rope_tables(4, 32)
+    pos = np.tile(np.arange(4), (2, 1))
+    perm = np.arange(64)
+    perm[0:32:2], perm[1:32:2] = np.arange(16), np.arange(16, 32)  # new dim 2j <- old j, 2j+1 <- old j+16
+    neox = oracle.rotary(x, c, s_, pos, 32, False)
+    inter = oracle.rotary(x[..., perm], c, s_, pos, 32, True)
+    np.testing.assert_allclose(inter, neox[..., perm], rtol=1e-14, atol=1e-15)
+
+
+def test_encode_rounds_to_nearest_even():
+    """float64 -> bf16 / fp16: the nearest representable value, ties to the
+    even encoding (halfway points built exactly), checked against the two
+    neighbours found by brute force."""
+    rng = np.random.default_rng(34)
+    for dt in ("bf16", "fp16"):
+        bits = rng.integers(0, 0x7B00, 400).astype(np.uint16)  # finite positive encodings
+        a = oracle.decode_array(dt, bits)
+        b = oracle.decode_array(dt, bits + 1)
+        mids = (a + b) / 2                                    # exact ties
+        np.testing.assert_array_equal(oracle.encode(dt, mids), np.where(bits % 2 == 0, bits, bits + 1))
+        np.testing.assert_array_equal(oracle.encode(dt, -mids), oracle.encode(dt, mids) | 0x8000)
+        near = a + (b - a) * rng.uniform(0.01, 0.49, 400)     # strictly nearer the lower one
+        np.testing.assert_array_equal(oracle.encode(dt, near), bits)
+        np.testing.assert_array_equal(oracle.encode(dt, a), bits)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_kvcache_append_then_attend_equals_concatenation(paged):
+    """Writing new keys/values at each slot's used length and attending over
+    the grown cache equals attention over the old used keys concatenated with
+    the new ones (np.concatenate), with the new keys rotated at their cache
+    positions; the new lengths are the old plus the new token count."""
+    rng = np.random.default_rng(35)
+    B, sn, hq, hkv, d, cap, page = 3, 4, 4, 2, 64, 192, 64
+    lens = np.array([100, 0, 187], np.int32)
+    bf = lambda shape: oracle.encode("bf16", rng.standard_normal(shape))  # noqa: E731
+    q, kn, vn = bf((B, sn, hq, d)), bf((B, sn, hkv, d)), bf((B, sn, hkv, d))
+    c, s_ = _rope_tables(cap, 32)
+    if paged:
+        npg = cap // page
+        table = rng.permutation(B * npg).reshape(B, npg).astype(np.int32)
+        kc, vc = bf((B * npg, page, hkv, d)), bf((B * npg, page, hkv, d))
+        def slot_rows(cache, b, n):
+            return np.concatenate([cache[table[b][j // page], j % page][None] for j in range(n)]) if n else \
+                np.zeros((0, hkv, d), np.uint16)
+    else:
+        table = None
+        kc, vc = bf((B, cap, hkv, d)), bf((B, cap, hkv, d))
+        def slot_rows(cache, b, n):
+            return cache[b, :n]
+    kc2, vc2, lens2 = oracle.kvcache_append(kc, vc, lens, kn, vn, block_table=table, rotary_cos=c, rotary_sin=s_,
+                                            rotary_dim=32, rotary_interleaved=False)
+    np.testing.assert_array_equal(lens2, lens + sn)
+    got = oracle.full(oracle.kvcache(q, kc2, vc2, lens2, 0.125, block_table=table, causal=True), grads=False)
+    pos = lens[:, None] + np.arange(sn)[None, :]
+    kn_rot = oracle.encode("bf16", oracle.rotary(oracle.decode_array("bf16", kn), c, s_, pos, 32, False))
+    ks = [np.concatenate([slot_rows(kc, b, lens[b]), kn_rot[b]]) for b in range(B)]
+    vs = [np.concatenate([slot_rows(vc, b, lens[b]), vn[b]]) for b in range(B)]
+    cu_k = np.concatenate([[0], np.cumsum([len(x) for x in ks])])
+    ref = oracle.full(oracle.varlen(q.reshape(B * sn, hq, d), np.concatenate(ks), np.concatenate(vs),
+                                    np.arange(B + 1) * sn, cu_k, 0.125, causal=True), grads=False)
+    np.testing.assert_array_equal(got["o"], ref["o"])
+    np.testing.assert_array_equal(got["lse"], ref["lse"])
