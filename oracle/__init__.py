@@ -245,6 +245,7 @@ def rotary(x, cos, sin, positions, rotary_dim, interleaved):
     page, flash_attn_with_kvcache: rotary_cos, rotary_sin, rotary_interleaved)."""
     x = np.array(x, np.float64, copy=True)
     half = rotary_dim // 2
+    positions = np.minimum(positions, len(cos) - 1)  # positions past the table: its last row
     c = np.asarray(cos, np.float64)[positions][:, :, None, :]  # [B, S, 1, half]
     s = np.asarray(sin, np.float64)[positions][:, :, None, :]
     if interleaved:
@@ -292,7 +293,9 @@ def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new, block_table=No
     or of the page the block table names), the keys rotated at that position
     when rotary tables are given and rounded to the cache's dtype
     (flash_attn_with_kvcache docstring: k, v, cache_seqlens, rotary_cos).
-    Arrays are bit patterns; returns new (k_cache, v_cache, seqlens)."""
+    Positions past the slot (its capacity, or its pages) are not written: the
+    pages leave them to the caller, and the library drops them.  Arrays are
+    bit patterns; returns new (k_cache, v_cache, seqlens)."""
     kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
     B, sn = k_new.shape[0], k_new.shape[1]
     lens = np.asarray(cache_seqlens, np.int64)
@@ -306,8 +309,12 @@ def kvcache_append(k_cache, v_cache, cache_seqlens, k_new, v_new, block_table=No
         for i in range(sn):
             p = int(pos[b, i])
             if block_table is None:
+                if p >= rows:
+                    continue
                 slot, r = b, p
             else:
+                if p // rows >= len(block_table[b]):
+                    continue
                 slot, r = int(block_table[b][p // rows]), p % rows
             kc[slot, r] = kn[b, i]
             vc[slot, r] = v_new[b, i]
