@@ -21,7 +21,7 @@ ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 
 EXPORTED = (
     "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
-    "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
+    "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size", "attn_kvcache_append", "attn_rotary",
     "attn_fwd_varlen", "attn_fwd_varlen_workspace_size", "attn_bwd_varlen",
     "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable", "attn_timing_select",
     "attn_timing_read",
@@ -68,6 +68,9 @@ def load_library():
     lib.attn_bwd_workspace_size.argtypes = [P, i64, i64, i64, i32]
     lib.attn_fwd_kvcache.argtypes = [P, i64, i64, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, sz, vp]
     lib.attn_fwd_kvcache_workspace_size.argtypes = [P, i64, i64, vp, i32, i32, i64]
+    lib.attn_kvcache_append.argtypes = [P, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, i32, i32,
+                                        i64, vp]
+    lib.attn_rotary.argtypes = [P, i64, i64, i32, vp, vp, vp, i32, vp, vp, i32, i32, i64, vp]
     lib.attn_fwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attn_fwd_varlen_workspace_size.argtypes = [P, i32, i64, i64, i32, i32]
     lib.attn_bwd_varlen.argtypes = [P, i32, i64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -220,14 +223,71 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, s
     return dq, dk, dv, dsinks
 
 
+def _check_rotary(rotary_cos, rotary_sin):
+    for t in (rotary_cos, rotary_sin):
+        if t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("rotary_cos / rotary_sin must be contiguous fp32 [seqlen_ro, rotary_dim / 2]")
+    if rotary_cos.shape != rotary_sin.shape:
+        raise ValueError("rotary_cos and rotary_sin must have the same shape")
+    return 2 * int(rotary_cos.shape[1]), int(rotary_cos.shape[0])
+
+
+def attn_rotary(x, positions, rotary_cos, rotary_sin, interleaved=True, per_token=True, out=None):
+    """Rotary embedding of x [B,S,H,D] at positions[b] + i (per_token) or positions[b]
+    (int32 [B]); rotary_cos, rotary_sin fp32 [seqlen_ro, rotary_dim / 2] -> out."""
+    lib = load_library()
+    B, S, H, d = x.shape
+    rdim, nro = _check_rotary(rotary_cos, rotary_sin)
+    p = make_params(x, x)
+    out = torch.empty_like(x) if out is None else out
+    _check(lib.attn_rotary(ctypes.byref(p), B, S, H, _ptr(x), _ptr(out), _ptr(positions), 1 if per_token else 0,
+                           _ptr(rotary_cos), _ptr(rotary_sin), rdim, 1 if interleaved else 0, nro,
+                           _stream(x.device)))
+    return out
+
+
+def attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table=None, rotary_cos=None,
+                        rotary_sin=None, rotary_interleaved=True, seqlens_out=None):
+    """Write k_new, v_new [B,Sn,Hkv,D] into the cache in place at positions
+    cache_seqlens[b] + i (keys rotated there when rotary tables are given);
+    returns seqlens_out (int32 [B]) = cache_seqlens + Sn."""
+    lib = load_library()
+    B, sn, hkv, d = k_new.shape
+    p = make_params(k_new, k_new)
+    if block_table is not None:
+        nblk, page, cap = int(block_table.shape[1]), int(k_cache.shape[1]), 0
+    else:
+        nblk, page, cap = 0, 0, int(k_cache.shape[1])
+    rdim, nro = _check_rotary(rotary_cos, rotary_sin) if rotary_cos is not None else (0, 0)
+    seqlens_out = torch.empty_like(cache_seqlens) if seqlens_out is None else seqlens_out
+    _check(lib.attn_kvcache_append(ctypes.byref(p), B, sn, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(cache_seqlens), _ptr(seqlens_out), _ptr(block_table), nblk, page, cap,
+                                   _ptr(rotary_cos), _ptr(rotary_sin), rdim, 1 if rotary_interleaved else 0, nro,
+                                   _stream(k_new.device)))
+    return seqlens_out
+
+
 def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causal=False, window=(-1, -1),
                      sinks=None, softmax_scale=None, softcap=0.0, alibi_slopes=None, sinks_shared=False, seqused_q=None,
-                     seqused_k=None, out=None, lse=None):
+                     seqused_k=None, out=None, lse=None, k_new=None, v_new=None, rotary_cos=None, rotary_sin=None,
+                     rotary_interleaved=True):
     """Forward over a KV cache: q [B,Sq,Hq,D]; cache_seqlens int32 [B] (used keys per slot);
     k_cache, v_cache [B,capacity,Hkv,D], or pages [num_blocks,page,Hkv,D] with
-    block_table int32 [B,max_blocks] -> (o, lse [B,Hq,Sq])."""
+    block_table int32 [B,max_blocks] -> (o, lse [B,Hq,Sq]).  With k_new, v_new
+    [B,Sn,Hkv,D] the cache is first updated in place at cache_seqlens (the
+    caller then advances its lengths by Sn) and attention covers the grown
+    cache; with rotary tables the new keys, and q, are rotated at their
+    positions (q at cache_seqlens + i when causal or windowed, else all at
+    cache_seqlens), as flash_attn_with_kvcache does."""
     lib = load_library()
     B, sq, hq, d = q.shape
+    if k_new is not None:
+        old = cache_seqlens  # the first new token's position in each slot
+        cache_seqlens = attn_kvcache_append(k_new, v_new, k_cache, v_cache, old, block_table, rotary_cos,
+                                            rotary_sin, rotary_interleaved)
+        if rotary_cos is not None:
+            local = causal or tuple(window) != (-1, -1)
+            q = attn_rotary(q, old, rotary_cos, rotary_sin, rotary_interleaved, per_token=local)
     p = make_params(q, k_cache, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
                     nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
     o = torch.empty_like(q) if out is None else out

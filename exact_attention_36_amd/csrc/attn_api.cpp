@@ -368,6 +368,78 @@ attn_status attn_fwd_kvcache(const attn_params* p, int64_t batch, int64_t seqlen
                  v_cache, o, lse, ws, ws_bytes, stream, kvc);
 }
 
+// Rotary tables: a rotary_dim that is a positive multiple of 16 no larger
+// than the head dim, tables of at least one row.
+static attn_status check_rotary(const attn_params* p, const float* cos, const float* sin, int32_t rotary_dim,
+                                int32_t interleaved, int64_t seqlen_ro) {
+  if (!cos || !sin) return fail(ATTN_EINVAL, "rotary_cos and rotary_sin must be non-NULL");
+  if (rotary_dim < 16 || rotary_dim % 16 || rotary_dim > p->head_dim)
+    return fail(ATTN_EINVAL, "rotary_dim must be a multiple of 16 in [16, head_dim] (got %d)", rotary_dim);
+  if (interleaved != 0 && interleaved != 1) return fail(ATTN_EINVAL, "rotary_interleaved must be 0 or 1");
+  if (seqlen_ro < 1 || seqlen_ro >= INT32_MAX) return fail(ATTN_EINVAL, "seqlen_ro must be >= 1");
+  return ATTN_OK;
+}
+
+attn_status attn_kvcache_append(const attn_params* p, int64_t batch, int64_t seqlen_new, const void* k_new,
+                                const void* v_new, void* k_cache, void* v_cache, const int32_t* cache_seqlens,
+                                int32_t* seqlens_out, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                int32_t page_block_size, int64_t cache_capacity, const float* rotary_cos,
+                                const float* rotary_sin, int32_t rotary_dim, int32_t rotary_interleaved,
+                                int64_t seqlen_ro, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if (batch < 1 || seqlen_new < 1 || batch >= INT32_MAX || seqlen_new >= INT32_MAX)
+    return fail(ATTN_EINVAL, "batch and seqlen_new must be >= 1 (got %lld, %lld)", (long long)batch,
+                (long long)seqlen_new);
+  if (!k_new || !v_new || !k_cache || !v_cache || !cache_seqlens)
+    return fail(ATTN_EINVAL, "k_new, v_new, k_cache, v_cache and cache_seqlens must be non-NULL");
+  if (block_table) {
+    if (max_blocks_per_seq < 1) return fail(ATTN_EINVAL, "max_blocks_per_seq must be >= 1 (got %d)", max_blocks_per_seq);
+    if (page_block_size < 1) return fail(ATTN_EINVAL, "page_block_size must be >= 1 (got %d)", page_block_size);
+  } else if (cache_capacity < 1) {
+    return fail(ATTN_EINVAL, "cache_capacity must be >= 1 without a block table (got %lld)", (long long)cache_capacity);
+  }
+  RotaryArgs r{};
+  if (rotary_dim != 0 || rotary_cos || rotary_sin) {
+    if ((st = check_rotary(p, rotary_cos, rotary_sin, rotary_dim, rotary_interleaved, seqlen_ro)) != ATTN_OK)
+      return st;
+    r = RotaryArgs{rotary_cos, rotary_sin, rotary_dim, rotary_interleaved, (int32_t)seqlen_ro};
+  }
+  AppendArgs a{};
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_cache = (uint16_t*)k_cache;
+  a.v_cache = (uint16_t*)v_cache;
+  a.seqlens = cache_seqlens;
+  a.block_table = block_table;
+  a.page_rows = block_table ? page_block_size : 0;
+  a.pages_per_seq = block_table ? max_blocks_per_seq : 0;
+  a.capacity = cache_capacity;
+  a.rows = batch * seqlen_new * p->heads_kv;
+  a.batch = (int32_t)batch;
+  a.seqlen_new = (int32_t)seqlen_new;
+  a.hkv = p->heads_kv;
+  a.D = p->head_dim;
+  a.rot = r;
+  return launched(launch_append(a, seqlens_out, p->dtype == ATTN_FP16, (hipStream_t)stream));
+}
+
+attn_status attn_rotary(const attn_params* p, int64_t batch, int64_t seqlen, int32_t heads, const void* x, void* out,
+                        const int32_t* positions, int32_t per_token, const float* rotary_cos, const float* rotary_sin,
+                        int32_t rotary_dim, int32_t rotary_interleaved, int64_t seqlen_ro, void* stream) {
+  attn_status st = check_params(p);
+  if (st != ATTN_OK) return st;
+  if (batch < 1 || seqlen < 1 || heads < 1 || batch >= INT32_MAX || seqlen >= INT32_MAX)
+    return fail(ATTN_EINVAL, "batch, seqlen and heads must be >= 1");
+  if (!x || !out || !positions) return fail(ATTN_EINVAL, "x, out and positions must be non-NULL");
+  if (per_token != 0 && per_token != 1) return fail(ATTN_EINVAL, "per_token must be 0 or 1");
+  if ((st = check_rotary(p, rotary_cos, rotary_sin, rotary_dim, rotary_interleaved, seqlen_ro)) != ATTN_OK)
+    return st;
+  const RotaryArgs r{rotary_cos, rotary_sin, rotary_dim, rotary_interleaved, (int32_t)seqlen_ro};
+  return launched(launch_rotary(x, out, batch * seqlen * heads, (int)seqlen, heads, p->head_dim, positions, per_token,
+                                r, p->dtype == ATTN_FP16, (hipStream_t)stream));
+}
+
 size_t attn_fwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
                                       int32_t max_seqlen_q, int32_t max_seqlen_k) {
   (void)p;

@@ -113,9 +113,32 @@ enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_DSINK, K_BWD_DQ, K_BWD_DKDV, K_C
 void timing_begin(int kid, hipStream_t st);
 void timing_end(int kid, hipStream_t st);
 
+// Rotary tables and layout: cos, sin [seqlen_ro][dim / 2] fp32; dim = 0: none.
+struct RotaryArgs {
+  const float* cos; const float* sin;
+  int32_t dim, interleaved, seqlen_ro;
+};
+// The in-place KV-cache append: new rows [batch][seqlen_new][hkv][D] into a
+// cache [batch][capacity][hkv][D], or pages [num_blocks][page_rows][hkv][D]
+// through block_table [batch][pages_per_seq], at positions seqlens[b] + i.
+struct AppendArgs {
+  const uint16_t* k_new; const uint16_t* v_new;
+  uint16_t* k_cache; uint16_t* v_cache;
+  const int32_t* seqlens;
+  const int32_t* block_table;
+  int32_t page_rows, pages_per_seq;
+  int64_t capacity;
+  int64_t rows;  // batch * seqlen_new * hkv
+  int32_t batch, seqlen_new, hkv, D;
+  RotaryArgs rot;
+};
+
 // Launchers (defined in the .hip files).  Return hipGetLastError().
 hipError_t launch_fwd(const FwdArgs& a, int tile_d, bool f16, hipStream_t st);
 hipError_t launch_fwd_combine(const FwdArgs& a, int tile_d, bool f16, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st);
+hipError_t launch_rotary(const void* x, void* out, int64_t rows, int S, int H, int D, const int32_t* pos0,
+                         int per_token, const RotaryArgs& r, bool f16, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, int32_t* seqlens_out, bool f16, hipStream_t st);
 
 }  // namespace attn

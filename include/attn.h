@@ -188,6 +188,51 @@ size_t attn_fwd_kvcache_workspace_size(const attn_params *params, int64_t batch,
                                        int32_t page_block_size, int64_t cache_capacity);
 
 /*
+ * In-place KV-cache append (vllm-project/flash-attention README on the
+ * GitHub search page, flash_attn_with_kvcache: k, v are written into the
+ * cache starting at cache_seqlens, keys rotated by rotary_cos / rotary_sin
+ * at their positions).  New token i of slot b (k_new, v_new
+ * [batch, seqlen_new, Hkv, D], params->dtype) goes to key position
+ * cache_seqlens[b] + i of the slot: row cache_seqlens[b] + i of
+ * k_cache[b] ([batch, cache_capacity, Hkv, D]), or, with a block table, row
+ * p % page_block_size of page block_table[b][p / page_block_size] (pages
+ * [num_blocks, page_block_size, Hkv, D]).  With rotary_dim > 0 the keys are
+ * rotated first (see attn_rotary); values are copied as they are.  Positions
+ * past the slot (the capacity, or max_blocks_per_seq pages) are dropped: the
+ * caller keeps the cache large enough.  When seqlens_out is non-NULL it
+ * receives cache_seqlens[b] + seqlen_new after the append, in stream order,
+ * so it may be cache_seqlens itself.  All pointers are device memory,
+ * 16-byte aligned; cache_seqlens and block_table contents are not checked.
+ * Errors: ATTN_EINVAL for NULL tensors, sizes < 1, a bad page or rotary
+ * setting; ATTN_EHIP for a launch failure.
+ */
+attn_status attn_kvcache_append(const attn_params *params, int64_t batch, int64_t seqlen_new, const void *k_new,
+                                const void *v_new, void *k_cache, void *v_cache, const int32_t *cache_seqlens,
+                                int32_t *seqlens_out, const int32_t *block_table, int32_t max_blocks_per_seq,
+                                int32_t page_block_size, int64_t cache_capacity, const float *rotary_cos,
+                                const float *rotary_sin, int32_t rotary_dim, int32_t rotary_interleaved,
+                                int64_t seqlen_ro, void *stream);
+
+/*
+ * Rotary embedding of x [batch, seqlen, heads, D] (params->dtype) into out
+ * (same shape; may be x): token i of batch b sits at position
+ * positions[b] + i (per_token = 1) or positions[b] (per_token = 0; the
+ * non-causal, non-local query rule of flash_attn_with_kvcache).  The first
+ * rotary_dim dims (a multiple of 16, at most D) form rotary_dim / 2 pairs --
+ * dims (2j, 2j+1) when rotary_interleaved, else (j, j + rotary_dim / 2), the
+ * GPT-NeoX form -- and pair j at position p becomes
+ * (a cos - b sin, a sin + b cos) with cos = rotary_cos[p][j],
+ * sin = rotary_sin[p][j] (fp32 [seqlen_ro, rotary_dim / 2]), in fp32 and
+ * rounded to nearest even; the other dims are copied.  Positions past the
+ * table use its last row (the caller keeps seqlen_ro large enough).
+ * Errors: as attn_kvcache_append.
+ */
+attn_status attn_rotary(const attn_params *params, int64_t batch, int64_t seqlen, int32_t heads, const void *x,
+                        void *out, const int32_t *positions, int32_t per_token, const float *rotary_cos,
+                        const float *rotary_sin, int32_t rotary_dim, int32_t rotary_interleaved, int64_t seqlen_ro,
+                        void *stream);
+
+/*
  * Forward, packed [T,H,D] with device int32 cu_seqlens_q/k [num_seqs+1].
  * total_q / total_k are the token counts (cu_seqlens_*[num_seqs]);
  * max_seqlen_q / max_seqlen_k bound every sequence's length.  lse is fp32

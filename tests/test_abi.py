@@ -148,3 +148,36 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load_library()
+
+
+def test_append_and_rotary_reject_bad_arguments():
+    lib = ea.load_library()
+    p = _params(dtype=_lib.ATTN_BF16, head_dim=64)
+    def app(**kw):
+        a = dict(B=1, sn=1, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, out=None, bt=None, nb=0, page=0, cap=16,
+                 cos=None, sin=None, rd=0, inter=1, nro=0)
+        a.update(kw)
+        return lib.attn_kvcache_append(ctypes.byref(p), a["B"], a["sn"], a["kn"], a["vn"], a["kc"], a["vc"], a["lens"],
+                                       a["out"], a["bt"], a["nb"], a["page"], a["cap"], a["cos"], a["sin"], a["rd"],
+                                       a["inter"], a["nro"], None)
+    assert app(sn=0) == _lib.ATTN_EINVAL
+    assert app(kn=None) == _lib.ATTN_EINVAL
+    assert app(lens=None) == _lib.ATTN_EINVAL
+    assert app(cap=0) == _lib.ATTN_EINVAL
+    assert app(bt=FAKE, nb=0, page=64) == _lib.ATTN_EINVAL
+    assert app(bt=FAKE, nb=4, page=0) == _lib.ATTN_EINVAL
+    assert app(cos=FAKE, sin=FAKE, rd=24, nro=8) == _lib.ATTN_EINVAL  # not a multiple of 16
+    assert "rotary_dim" in ea.last_error()
+    assert app(cos=FAKE, sin=FAKE, rd=80, nro=8) == _lib.ATTN_EINVAL  # above the head dim
+    assert app(cos=FAKE, sin=None, rd=32, nro=8) == _lib.ATTN_EINVAL
+    assert app(cos=FAKE, sin=FAKE, rd=32, nro=0) == _lib.ATTN_EINVAL
+    assert app(cos=FAKE, sin=FAKE, rd=32, nro=8, inter=2) == _lib.ATTN_EINVAL
+    def rot(**kw):
+        a = dict(B=1, S=1, H=1, x=FAKE, out=FAKE, pos=FAKE, per=1, cos=FAKE, sin=FAKE, rd=32, inter=0, nro=4)
+        a.update(kw)
+        return lib.attn_rotary(ctypes.byref(p), a["B"], a["S"], a["H"], a["x"], a["out"], a["pos"], a["per"], a["cos"],
+                               a["sin"], a["rd"], a["inter"], a["nro"], None)
+    assert rot(H=0) == _lib.ATTN_EINVAL
+    assert rot(pos=None) == _lib.ATTN_EINVAL
+    assert rot(per=3) == _lib.ATTN_EINVAL
+    assert rot(rd=0) == _lib.ATTN_EINVAL
