@@ -169,12 +169,41 @@ def run_kvcache(steps, warmup, page=256):
     per_call_ms = (ms_s + ms_c) / steps
     kv_bytes = 2 * d["B"] * d["SK"] * d["HKV"] * d["D"] * 2
     gbps = kv_bytes / (per_call_ms * 1e-3) / 1e9
-    del q, k, v, o, lse, table
+    # The cache update of a decode step: the SQ new keys/values of every slot
+    # written at its used length (keys rotated, rotary over all D dims) and q
+    # rotated -- attn_kvcache_append + attn_rotary, timed together with events.
+    kn, vn = synth.device_normal(6, [(d["B"], d["SQ"], d["HKV"], d["D"])] * 2)
+    ang = torch.arange(d["SK"], device="cuda", dtype=torch.float64)[:, None] * \
+        (10000.0 ** (-torch.arange(0, d["D"], 2, device="cuda", dtype=torch.float64) / d["D"]))[None, :]
+    cos, sin = torch.cos(ang).float().contiguous(), torch.sin(ang).float().contiguous()
+    lens0 = lens - d["SQ"]
+    grown = torch.empty_like(lens)
+    qr = torch.empty_like(q)
+    def update():
+        ea.attn_kvcache_append(kn, vn, k, v, lens0, block_table=table, rotary_cos=cos, rotary_sin=sin,
+                               rotary_interleaved=False, seqlens_out=grown)
+        ea.attn_rotary(q, lens0, cos, sin, interleaved=False, per_token=True, out=qr)
+    for _ in range(warmup):
+        update()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        update()
+    e1.record()
+    torch.cuda.synchronize()
+    upd_ms = e0.elapsed_time(e1) / steps
+    upd_bytes = 2 * (2 * kn.numel() * 2 + q.numel() * 2)  # k, v new rows and q: read once, written once
+    del q, k, v, o, lse, table, kn, vn, qr
     torch.cuda.empty_cache()
     return {"workload": d["name"] + " paged KV cache (pages of %d rows, shuffled)" % page,
             "ms_per_call": round(per_call_ms, 4), "split_kernel_ms": round(ms_s / max(n_s, 1), 4),
             "combine_ms": round(ms_c / max(n_c, 1), 4), "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1),
-            "hbm_peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4)}
+            "hbm_peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4),
+            "update": {"what": "append %d new keys/values per slot (keys rotated) + rotate q; eager calls, "
+                               "three small launches: launch-bound" % d["SQ"],
+                       "ms": round(upd_ms, 4), "bytes": upd_bytes,
+                       "GBps": round(upd_bytes / (upd_ms * 1e-3) / 1e9, 1)}}
 
 
 def run_sweep(steps, warmup):

@@ -4,10 +4,11 @@
 // flash_attn_with_kvcache: k, v, cache_seqlens, rotary_cos, rotary_sin,
 // rotary_interleaved, block_table).
 //
-// One wave per row of D 16-bit values; lane c < D/8 owns the 16-byte chunk
-// 8c .. 8c+7.  The first rotary_dim dims form rotary_dim/2 pairs: (2j, 2j+1)
-// when interleaved -- both in one chunk -- else (j, j + rotary_dim/2), whose
-// partner chunk the lower lane reads and writes too.  rotary_dim is a
+// Rows of D 16-bit values, D/8 lanes per row and 64 / (D/8) rows per wave;
+// lane c of a row's group owns the 16-byte chunk 8c .. 8c+7.  The first
+// rotary_dim dims form rotary_dim/2 pairs: (2j, 2j+1) when interleaved --
+// both in one chunk -- else (j, j + rotary_dim/2), whose partner chunk the
+// lower lane reads and writes too.  rotary_dim is a
 // multiple of 16, so no pair straddles chunks and rotating in place is safe.
 // Pair j at position p turns by the angle whose cosine and sine are
 // cos[p][j], sin[p][j]: (a, b) -> (a c - b s, a s + b c), in fp32, rounded to
@@ -17,7 +18,16 @@
 namespace attn {
 namespace {
 
-constexpr int ROWS_PER_BLOCK = THREADS / 64;
+// lanes per row and rows per workgroup for head dim D
+__host__ __device__ constexpr int lanes_per_row(int D) { return D / 8; }
+__host__ __device__ constexpr int rows_per_block(int D) { return (64 / lanes_per_row(D)) * (THREADS / 64); }
+// this thread's row within the workgroup's rows (-1: an idle lane) and its chunk
+__device__ __forceinline__ int row_slot(int D, int& chunk) {
+  const int lpr = lanes_per_row(D), per_wave = 64 / lpr, lane = threadIdx.x & 63;
+  chunk = lane % lpr;
+  const int sub = lane / lpr;
+  return sub < per_wave ? (int)(threadIdx.x >> 6) * per_wave + sub : -1;
+}
 
 template <bool F16>
 __device__ __forceinline__ void unpack8(const u32x4& v, float (&x)[8]) {
@@ -77,20 +87,23 @@ __device__ __forceinline__ void rotary_row(const uint16_t* src, uint16_t* dst, i
 template <bool F16>
 __global__ __launch_bounds__(THREADS) void rotary_kernel(const uint16_t* x, uint16_t* out, int64_t rows, int S, int H,
                                                           int D, const int32_t* pos0, int per_token, RotaryArgs r) {
-  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  int chunk;
+  const int slot = row_slot(D, chunk);
+  const int64_t row = (int64_t)blockIdx.x * rows_per_block(D) + slot;
+  if (slot < 0 || row >= rows) return;
   const int64_t tok = row / H;
   const int b = (int)(tok / S), i = (int)(tok - (int64_t)b * S);
-  rotary_row<F16>(x + row * D, out + row * D, D, pos0[b] + (per_token ? i : 0), r, threadIdx.x & 63);
+  rotary_row<F16>(x + row * D, out + row * D, D, pos0[b] + (per_token ? i : 0), r, chunk);
 }
 
 // New token i of slot b, kv head h -> key position len[b] + i of the slot;
 // keys rotated there, values copied.  Rows past the slot are dropped.
 template <bool F16>
 __global__ __launch_bounds__(THREADS) void append_kernel(AppendArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const int lane = threadIdx.x & 63;
+  int lane;  // this thread's chunk of the row
+  const int slot = row_slot(a.D, lane);
+  const int64_t row = (int64_t)blockIdx.x * rows_per_block(a.D) + slot;
+  if (slot < 0 || row >= a.rows) return;
   const int h = (int)(row % a.hkv);
   const int64_t tok = row / a.hkv;
   const int b = (int)(tok / a.seqlen_new), i = (int)(tok - (int64_t)b * a.seqlen_new);
@@ -118,7 +131,7 @@ __global__ void grow_lengths_kernel(const int32_t* in, int32_t* out, int n, int 
 
 hipError_t launch_rotary(const void* x, void* out, int64_t rows, int S, int H, int D, const int32_t* pos0,
                          int per_token, const RotaryArgs& r, bool f16, hipStream_t st) {
-  const dim3 grid((unsigned)((rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK));
+  const dim3 grid((unsigned)((rows + rows_per_block(D) - 1) / rows_per_block(D)));
   if (f16)
     hipLaunchKernelGGL(rotary_kernel<true>, grid, dim3(THREADS), 0, st, (const uint16_t*)x, (uint16_t*)out, rows, S,
                        H, D, pos0, per_token, r);
@@ -129,7 +142,7 @@ hipError_t launch_rotary(const void* x, void* out, int64_t rows, int S, int H, i
 }
 
 hipError_t launch_append(const AppendArgs& a, int32_t* seqlens_out, bool f16, hipStream_t st) {
-  const dim3 grid((unsigned)((a.rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK));
+  const dim3 grid((unsigned)((a.rows + rows_per_block(a.D) - 1) / rows_per_block(a.D)));
   if (f16) hipLaunchKernelGGL(append_kernel<true>, grid, dim3(THREADS), 0, st, a);
   else hipLaunchKernelGGL(append_kernel<false>, grid, dim3(THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
