@@ -79,3 +79,25 @@ def scale_of(d, scale=None):
 def oracle_batched(inp, causal, window, scale, dtype="bf16"):
     return oracle.batched(inp["q"], inp["k"], inp["v"], scale, causal=causal, window=window,
                           dout=inp["dout"], sinks=inp["sinks"], dtype=dtype)
+
+
+def check_dsinks(name, got, ref, p):
+    """d(sink) to the documented bound 2e-2 + 1e-3 * sum_i |(1 - g_i) D_i| (D_i
+    comes from the stored 16-bit O and the sum runs over every row of the
+    head), that sum split over a head's sinks by their softmax share."""
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    seqs, heads, rws = [], [], []
+    for sq_ in range(p.nseq):
+        for h in range(p.hq):
+            for i in range(int(p.q_len[sq_])):
+                seqs.append(sq_), heads.append(h), rws.append(i)
+    r = oracle.rows(p, seqs, heads, rws, grads=True)
+    mag = np.zeros(p.hq)
+    np.add.at(mag, np.asarray(heads), np.abs((1.0 - r["gate"]) * r["delta"]))
+    tab = p.sink_table()
+    share = np.exp(tab - tab.max(axis=1, keepdims=True))
+    share /= share.sum(axis=1, keepdims=True)
+    m = mag[:, None] * share
+    m = (m.sum(axis=0) if p.sinks_shared else m).reshape(ref.shape)
+    err = np.abs(got - ref)
+    assert np.all(err <= 2e-2 + 1e-3 * m), (name, err.max(), m)

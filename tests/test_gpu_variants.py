@@ -13,7 +13,7 @@ import torch
 import oracle
 from exact_attention_36_amd import synth
 import exact_attention_36_amd as ea
-from _helpers import assert_close, assert_lse, dev_tensor, host, scale_of
+from _helpers import assert_close, assert_lse, check_dsinks, dev_tensor, host, scale_of
 
 pytestmark = pytest.mark.gpu
 
@@ -37,28 +37,6 @@ def _slopes(kind, hq, nseq, seed):
 
 def _dev(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-
-def _check_dsinks(name, got, ref, p):
-    """d(sink) to the documented bound 2e-2 + 1e-3 * sum_i |(1 - g_i) D_i| (D_i
-    comes from the stored 16-bit O and the sum runs over every row of the
-    head), that sum split over a head's sinks by their softmax share."""
-    assert got.shape == ref.shape, (name, got.shape, ref.shape)
-    seqs, heads, rws = [], [], []
-    for sq_ in range(p.nseq):
-        for h in range(p.hq):
-            for i in range(int(p.q_len[sq_])):
-                seqs.append(sq_), heads.append(h), rws.append(i)
-    r = oracle.rows(p, seqs, heads, rws, grads=True)
-    mag = np.zeros(p.hq)
-    np.add.at(mag, np.asarray(heads), np.abs((1.0 - r["gate"]) * r["delta"]))
-    tab = p.sink_table()
-    share = np.exp(tab - tab.max(axis=1, keepdims=True))
-    share /= share.sum(axis=1, keepdims=True)
-    m = mag[:, None] * share
-    m = (m.sum(axis=0) if p.sinks_shared else m).reshape(ref.shape)
-    err = np.abs(got - ref)
-    assert np.all(err <= 2e-2 + 1e-3 * m), (name, err.max(), m)
 
 
 BATCHED = [
@@ -108,7 +86,7 @@ def test_variant_batched_matches_oracle(case):
         assert_close(name + ".dk", host(dk).reshape(B * sk, hkv, d), ref["dk"], od)
         assert_close(name + ".dv", host(dv).reshape(B * sk, hkv, d), ref["dv"], od)
         if sinks is not None:
-            _check_dsinks(name, host(ds), ref["dsinks"], prob)
+            check_dsinks(name, host(ds), ref["dsinks"], prob)
 
 
 VARLEN = [
@@ -150,7 +128,7 @@ def test_variant_varlen_matches_oracle(case):
     assert_close(name + ".dk", host(dk), ref["dk"], "f32")
     assert_close(name + ".dv", host(dv), ref["dv"], "f32")
     if sinks is not None:
-        _check_dsinks(name, host(ds), ref["dsinks"], prob)
+        check_dsinks(name, host(ds), ref["dsinks"], prob)
 
 
 def test_variant_kvcache_matches_oracle():
