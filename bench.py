@@ -492,7 +492,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the attention kernels run on a single device and this "
-              "build has no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
+              "library has no multi-GPU path (got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -87,7 +87,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_EINVAL = 1,   /* bad argument: null pointer, bad shape, Hq % Hkv != 0,
                           window < -1, workspace too small, bad dtype */
-    ATTN_ENOTSUP = 2,  /* valid request outside this build: sizes whose byte
+    ATTN_ENOTSUP = 2,  /* valid request the kernels do not support: byte
                           offsets exceed 2^31, more than 128 q heads per kv head */
     ATTN_EHIP = 3      /* the HIP runtime reported an error at launch */
 } attn_status;
