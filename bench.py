@@ -11,7 +11,8 @@ HIP events on the library's stream (the other kernels run untimed there);
 Hq=64, Hkv=8) as K/V HBM GB/s;
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
 prefill workload.  `--workload decode` runs only the decode shape;
-`--workload sweep`, `headdims` and `variants` print one line per shape;
+`--workload sweep`, `headdims`, `variants` and `configs` (the five parity
+workloads) print one line per shape;
 `--workload latency` times the launch-bound shape eagerly and as graph replays.
 """
 from __future__ import annotations
@@ -418,6 +419,70 @@ def read_power_clock():
     return float(pw.group(1)), sum(gfx) / len(gfx) if gfx else None
 
 
+def run_configs(steps, warmup):
+    """Kernel times of the five parity workloads, one JSON line each, from the
+    library's HIP-event timing: the tiny non-causal forward (B=1, H=2, S=128,
+    D=64), causal prefill (B=4, H=16, S=2048), GQA 32/8 with window (127, 0)
+    and sinks (B=2, S=8192), the packed batch (65536 tokens in 64 sequences,
+    GQA 16/4, causal) and the decode shape (B=32, s_q=16, s_kv=32768, GQA
+    64/8).  TFLOP/s count 4·D flops per visible pair forward, 10·D backward."""
+    import numpy as np
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    names = list(ea._lib.KERNELS)
+
+    def timed(fn, reps):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ea.attn_timing_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        r = {n: ea.attn_timing_read(n) for n in names}
+        ea.attn_timing_enable(False)
+        return {n: (ms / reps) for n, (c, ms) in r.items()}
+
+    def line(name, D, pairs, tf, tb=None, kv_bytes=None):
+        f = tf["fwd"] + tf["fwd_combine"]
+        r = {"workload": name, "fwd_ms": round(f, 4), "fwd_tflops": round(4.0 * D * pairs / (f * 1e-3) / 1e12, 1)}
+        if kv_bytes:
+            r["kv_GBps"] = round(kv_bytes / (f * 1e-3) / 1e9, 1)
+        if tb:
+            b = tb["bwd_dsink"] + tb["bwd_dq"] + tb["bwd_dkdv"]
+            r.update(bwd_ms=round(b, 4), dq_ms=round(tb["bwd_dq"], 4), dkdv_ms=round(tb["bwd_dkdv"], 4),
+                     dsink_ms=round(tb["bwd_dsink"], 4), bwd_tflops=round(10.0 * D * pairs / (b * 1e-3) / 1e12, 1),
+                     fwdbwd_tflops=round(14.0 * D * pairs / ((f + b) * 1e-3) / 1e12, 1))
+        print(json.dumps(r), flush=True)
+
+    batched = [
+        ("fwd B1 H2 S128 D64 non-causal", 1, 128, 128, 2, 2, 64, False, (-1, -1), False, False),
+        ("causal prefill B4 H16 S2048 D128", 4, 2048, 2048, 16, 16, 128, True, (-1, -1), False, True),
+        ("GQA 32/8 window (127,0) sinks B2 S8192 D128", 2, 8192, 8192, 32, 8, 128, True, (127, 0), True, True),
+        ("decode B32 s_q16 s_kv32768 GQA 64/8 D128 causal", 32, 16, 32768, 64, 8, 128, True, (-1, -1), False, False),
+    ]
+    for name, B, sq, sk, hq, hkv, D, causal, win, sinks, bwd in batched:
+        q, k, v, do = synth.device_normal(sq + hq, [(B, sq, hq, D), (B, sk, hkv, D), (B, sk, hkv, D), (B, sq, hq, D)])
+        s = torch.from_numpy(np.random.default_rng(3).standard_normal(hq).astype(np.float32)).cuda() if sinks else None
+        o, lse = ea.attn_fwd(q, k, v, causal=causal, window=win, sinks=s)
+        tf = timed(lambda: ea.attn_fwd(q, k, v, causal=causal, window=win, sinks=s, out=o, lse=lse), steps)
+        tb = timed(lambda: ea.attn_bwd(q, k, v, o, lse, do, causal=causal, window=win, sinks=s), steps) if bwd else None
+        kv = 2 * B * sk * hkv * D * 2 if sq < 64 else None
+        line(name, D, visible_pairs(B, sq, sk, hq, causal, win), tf, tb, kv)
+        del q, k, v, do, o, lse
+    w = synth.packed_workload(seed=4)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    q, k, v, do = (dev(w[n]) for n in ("q", "k", "v", "dout"))
+    cu = torch.from_numpy(w["cu_q"]).cuda()
+    mx = int(w["lengths"].max())
+    o, lse = ea.attn_fwd_varlen(q, k, v, cu, cu, mx, mx, causal=True)
+    tf = timed(lambda: ea.attn_fwd_varlen(q, k, v, cu, cu, mx, mx, causal=True, out=o, lse=lse), steps)
+    tb = timed(lambda: ea.attn_bwd_varlen(q, k, v, o, lse, do, cu, cu, mx, mx, causal=True), steps)
+    pairs = 16 * sum(int(L) * (int(L) + 1) // 2 for L in w["lengths"])
+    line("packed 65536 tokens 64 seqs GQA 16/4 D128 causal", 128, pairs, tf, tb)
+
+
 def run_power(seconds):
     """Socket power and shader clock while the workload's forward, backward
     and whole step each run back to back for `seconds` (sampled after the
@@ -478,10 +543,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
-    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power", "configs"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
-                         "sweep: context sweep over S = 512..16384 (one JSON line per shape); "
+                         "sweep: context sweep over S = 512..16384 (one JSON line per shape); configs: kernel times of the five "
+                         "parity workloads; "
                          "headdims: causal prefill at D = 32..256 (one JSON line per head dim); "
                          "variants: causal prefill with soft cap / ALiBi / 4 sinks (one line each); "
                          "latency: launch-bound forward, eager calls vs HIP graph replays; "
@@ -511,6 +577,9 @@ def main():
         return
     if args.workload == "latency":
         run_latency(args.steps, args.warmup)
+        return
+    if args.workload == "configs":
+        run_configs(args.steps, args.warmup)
         return
     if args.workload == "power":
         run_power(args.seconds)
