@@ -419,7 +419,7 @@ def read_power_clock():
     return float(pw.group(1)), sum(gfx) / len(gfx) if gfx else None
 
 
-def run_configs(steps, warmup):
+def run_configs(steps, warmup, only=None):
     """Kernel times of the five parity workloads, one JSON line each, from the
     library's HIP-event timing: the tiny non-causal forward (B=1, H=2, S=128,
     D=64), causal prefill (B=4, H=16, S=2048), GQA 32/8 with window (127, 0)
@@ -462,7 +462,9 @@ def run_configs(steps, warmup):
         ("GQA 32/8 window (127,0) sinks B2 S8192 D128", 2, 8192, 8192, 32, 8, 128, True, (127, 0), True, True),
         ("decode B32 s_q16 s_kv32768 GQA 64/8 D128 causal", 32, 16, 32768, 64, 8, 128, True, (-1, -1), False, False),
     ]
-    for name, B, sq, sk, hq, hkv, D, causal, win, sinks, bwd in batched:
+    for cfg, (name, B, sq, sk, hq, hkv, D, causal, win, sinks, bwd) in zip((1, 2, 3, 5), batched):
+        if only is not None and cfg != only:
+            continue
         q, k, v, do = synth.device_normal(sq + hq, [(B, sq, hq, D), (B, sk, hkv, D), (B, sk, hkv, D), (B, sq, hq, D)])
         s = torch.from_numpy(np.random.default_rng(3).standard_normal(hq).astype(np.float32)).cuda() if sinks else None
         o, lse = ea.attn_fwd(q, k, v, causal=causal, window=win, sinks=s)
@@ -471,6 +473,8 @@ def run_configs(steps, warmup):
         kv = 2 * B * sk * hkv * D * 2 if sq < 64 else None
         line(name, D, visible_pairs(B, sq, sk, hq, causal, win), tf, tb, kv)
         del q, k, v, do, o, lse
+    if only is not None and only != 4:
+        return
     w = synth.packed_workload(seed=4)
     dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
     q, k, v, do = (dev(w[n]) for n in ("q", "k", "v", "dout"))
@@ -553,6 +557,8 @@ def main():
                          "latency: launch-bound forward, eager calls vs HIP graph replays; "
                          "power: socket power and shader clock (amd-smi) under the step's kernels")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
+    ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=None,
+                    help="with --workload configs: run only this workload (1..5 in the order listed there)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 256 MiB elementwise copy first (reference for HBM counter runs)")
     args = ap.parse_args()
@@ -579,7 +585,9 @@ def main():
         run_latency(args.steps, args.warmup)
         return
     if args.workload == "configs":
-        run_configs(args.steps, args.warmup)
+        if args.copy_calibration:
+            copy_calibration()
+        run_configs(args.steps, args.warmup, args.config)
         return
     if args.workload == "power":
         run_power(args.seconds)

@@ -128,6 +128,53 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(named, dtype=None, shapes=None):
+    """Reject what the C ABI cannot see: every tensor in `named` (name ->
+    tensor or None) must be contiguous and on one CUDA device; `dtype` names
+    the tensors that must share the 16-bit input dtype; `shapes` maps a name
+    to its required shape (None entries of a shape are free).  Shape and
+    dtype are checked before the device, so host tensors of a wrong shape
+    are reported by shape."""
+    present = {n: t for n, t in named.items() if t is not None}
+    for n, want in (shapes or {}).items():
+        t = present.get(n)
+        if t is None or want is None:
+            continue
+        got = tuple(t.shape)
+        ok = len(got) == len(want) and all(w is None or int(w) == g for w, g in zip(want, got))
+        _need(ok, "%s must have shape %s, got %s" % (n, tuple("*" if w is None else int(w) for w in want), got))
+    if dtype:
+        ref = present[dtype[0]].dtype
+        _need(ref in (torch.bfloat16, torch.float16), "%s must be bf16 or fp16, got %s" % (dtype[0], ref))
+        for n in dtype[1:]:
+            if n in present:
+                _need(present[n].dtype == ref, "%s must have %s's dtype %s, got %s" % (n, dtype[0], ref,
+                                                                                       present[n].dtype))
+    for n, t in present.items():
+        _need(t.is_contiguous(), "%s must be contiguous (got strides %s)" % (n, tuple(t.stride())))
+    devs = {t.device for t in present.values()}
+    _need(len(devs) == 1, "all tensors must be on one device, got %s" % sorted(str(d) for d in devs))
+    dev = devs.pop()
+    _need(dev.type == "cuda", "tensors must be on a GPU (got %s)" % dev)
+
+
+def _check_f32(name, t, shape):
+    if t is not None:
+        _need(t.dtype == torch.float32, "%s must be fp32, got %s" % (name, t.dtype))
+        _need(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_i32(name, t, shape):
+    if t is not None:
+        _need(t.dtype == torch.int32, "%s must be int32, got %s" % (name, t.dtype))
+        _need(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
 def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
                 alibi_slopes=None, sinks_shared=False, nseq=None, seqused_q=None,
                 seqused_k=None) -> attn_params:
@@ -166,6 +213,7 @@ def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
         if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (nseq,) or not t.is_contiguous()):
             raise ValueError("%s must be contiguous int32 [%s]; got %s %s" % (name, nseq, tuple(t.shape), t.dtype))
         setattr(p, name, _ptr(t))
+    _check_tensors(dict(q=q, sinks=sinks, alibi_slopes=alibi_slopes, seqused_q=seqused_q, seqused_k=seqused_k))
     return p
 
 
@@ -188,8 +236,12 @@ def attn_fwd(q, k, v, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
              alibi_slopes=None, sinks_shared=False, seqused_q=None, seqused_k=None, out=None, lse=None):
     """Batched forward: q [B,Sq,Hq,D], k, v [B,Sk,Hkv,D] -> (o, lse [B,Hq,Sq] fp32)."""
     lib = load_library()
+    _need(q.dim() == 4 and k.dim() == 4, "q, k, v must be [B, S, H, D]")
     B, sq, hq, d = q.shape
-    sk = k.shape[1]
+    sk, hkv = k.shape[1], k.shape[2]
+    _check_f32("lse", lse, (B, hq, sq))
+    _check_tensors(dict(q=q, k=k, v=v, out=out, lse=lse), dtype=("q", "k", "v", "out"),
+                   shapes=dict(k=(B, None, None, d), v=(B, sk, hkv, d), out=(B, sq, hq, d)))
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
                     nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
     o = torch.empty_like(q) if out is None else out
@@ -206,8 +258,14 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, s
              grad_dtype=None):
     """Batched backward -> (dq, dk, dv, dsinks or None)."""
     lib = load_library()
+    _need(q.dim() == 4 and k.dim() == 4, "q, k, v must be [B, S, H, D]")
     B, sq, hq, d = q.shape
-    sk = k.shape[1]
+    sk, hkv = k.shape[1], k.shape[2]
+    _need(grad_dtype in (None, q.dtype, torch.float32),
+          "grad_dtype must be the input dtype or torch.float32, got %s" % grad_dtype)
+    _check_f32("lse", lse, (B, hq, sq))
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dout=dout), dtype=("q", "k", "v", "o", "dout"),
+                   shapes=dict(k=(B, None, None, d), v=(B, sk, hkv, d), o=(B, sq, hq, d), dout=(B, sq, hq, d)))
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
                     nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
     gd = q.dtype if grad_dtype is None else grad_dtype
@@ -236,8 +294,12 @@ def attn_rotary(x, positions, rotary_cos, rotary_sin, interleaved=True, per_toke
     """Rotary embedding of x [B,S,H,D] at positions[b] + i (per_token) or positions[b]
     (int32 [B]); rotary_cos, rotary_sin fp32 [seqlen_ro, rotary_dim / 2] -> out."""
     lib = load_library()
+    _need(x.dim() == 4, "x must be [B, S, H, D]")
     B, S, H, d = x.shape
     rdim, nro = _check_rotary(rotary_cos, rotary_sin)
+    _check_i32("positions", positions, (B,))
+    _check_tensors(dict(x=x, out=out, positions=positions, rotary_cos=rotary_cos, rotary_sin=rotary_sin),
+                   dtype=("x", "out"), shapes=dict(out=tuple(x.shape)))
     p = make_params(x, x)
     out = torch.empty_like(x) if out is None else out
     _check(lib.attn_rotary(ctypes.byref(p), B, S, H, _ptr(x), _ptr(out), _ptr(positions), 1 if per_token else 0,
@@ -252,7 +314,19 @@ def attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_tab
     cache_seqlens[b] + i (keys rotated there when rotary tables are given);
     returns seqlens_out (int32 [B]) = cache_seqlens + Sn."""
     lib = load_library()
+    _need(k_new.dim() == 4 and k_cache.dim() == 4, "k_new, v_new and the caches must be 4-d")
     B, sn, hkv, d = k_new.shape
+    _check_i32("cache_seqlens", cache_seqlens, (B,))
+    _check_i32("seqlens_out", seqlens_out, (B,))
+    if block_table is not None:
+        _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be int32 [B, max_blocks]")
+        _check_i32("block_table", block_table, tuple(block_table.shape))
+    _check_tensors(dict(k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, cache_seqlens=cache_seqlens,
+                        seqlens_out=seqlens_out, block_table=block_table, rotary_cos=rotary_cos,
+                        rotary_sin=rotary_sin),
+                   dtype=("k_new", "v_new", "k_cache", "v_cache"),
+                   shapes=dict(v_new=tuple(k_new.shape), k_cache=(None if block_table is not None else B, None, hkv, d),
+                               v_cache=tuple(k_cache.shape)))
     p = make_params(k_new, k_new)
     if block_table is not None:
         nblk, page, cap = int(block_table.shape[1]), int(k_cache.shape[1]), 0
@@ -280,7 +354,23 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None, causa
     positions (q at cache_seqlens + i when causal or windowed, else all at
     cache_seqlens), as flash_attn_with_kvcache does."""
     lib = load_library()
+    _need(seqused_k is None, "attn_fwd_kvcache takes the used keys per slot from cache_seqlens; "
+                             "seqused_k is not accepted here")
+    _need(q.dim() == 4 and k_cache.dim() == 4, "q and the caches must be 4-d")
     B, sq, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    _check_i32("cache_seqlens", cache_seqlens, (B,))
+    if block_table is not None:
+        _need(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be int32 [B, max_blocks]")
+        _check_i32("block_table", block_table, tuple(block_table.shape))
+    _check_f32("lse", lse, (B, hq, sq))
+    _check_tensors(dict(q=q, k_cache=k_cache, v_cache=v_cache, cache_seqlens=cache_seqlens, block_table=block_table,
+                        out=out, lse=lse, k_new=k_new, v_new=v_new),
+                   dtype=("q", "k_cache", "v_cache", "out", "k_new", "v_new"),
+                   shapes=dict(k_cache=(None if block_table is not None else B, None, hkv, d),
+                               v_cache=tuple(k_cache.shape), out=(B, sq, hq, d),
+                               k_new=(B, None, hkv, d),
+                               v_new=tuple(k_new.shape) if k_new is not None else None))
     if k_new is not None:
         old = cache_seqlens  # the first new token's position in each slot
         cache_seqlens = attn_kvcache_append(k_new, v_new, k_cache, v_cache, old, block_table, rotary_cos,
@@ -309,9 +399,16 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                     sinks_shared=False, seqused_q=None, seqused_k=None, out=None, lse=None):
     """Packed forward: q [Tq,Hq,D], k, v [Tk,Hkv,D], int32 cu_seqlens [N+1] -> (o, lse [Hq,Tq])."""
     lib = load_library()
+    _need(q.dim() == 3 and k.dim() == 3, "packed q, k, v must be [T, H, D]")
     tq, hq, d = q.shape
-    tk = k.shape[0]
+    tk, hkv = k.shape[0], k.shape[1]
+    _need(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape[0] >= 2, "cu_seqlens_q must be int32 [N+1], N >= 1")
     n = cu_seqlens_q.shape[0] - 1
+    _check_i32("cu_seqlens_q", cu_seqlens_q, (n + 1,))
+    _check_i32("cu_seqlens_k", cu_seqlens_k, (n + 1,))
+    _check_f32("lse", lse, (hq, tq))
+    _check_tensors(dict(q=q, k=k, v=v, out=out, lse=lse, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k),
+                   dtype=("q", "k", "v", "out"), shapes=dict(k=(None, None, d), v=(tk, hkv, d), out=(tq, hq, d)))
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
                     nseq=n, seqused_q=seqused_q, seqused_k=seqused_k)
     o = torch.empty_like(q) if out is None else out
@@ -329,9 +426,20 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
                     sinks_shared=False, seqused_q=None, seqused_k=None, grad_dtype=None):
     """Packed backward -> (dq, dk, dv, dsinks or None)."""
     lib = load_library()
+    _need(q.dim() == 3 and k.dim() == 3, "packed q, k, v must be [T, H, D]")
     tq, hq, d = q.shape
-    tk = k.shape[0]
+    tk, hkv = k.shape[0], k.shape[1]
+    _need(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape[0] >= 2, "cu_seqlens_q must be int32 [N+1], N >= 1")
     n = cu_seqlens_q.shape[0] - 1
+    _check_i32("cu_seqlens_q", cu_seqlens_q, (n + 1,))
+    _check_i32("cu_seqlens_k", cu_seqlens_k, (n + 1,))
+    _need(grad_dtype in (None, q.dtype, torch.float32),
+          "grad_dtype must be the input dtype or torch.float32, got %s" % grad_dtype)
+    _check_f32("lse", lse, (hq, tq))
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dout=dout, cu_seqlens_q=cu_seqlens_q,
+                        cu_seqlens_k=cu_seqlens_k),
+                   dtype=("q", "k", "v", "o", "dout"),
+                   shapes=dict(k=(None, None, d), v=(tk, hkv, d), o=(tq, hq, d), dout=(tq, hq, d)))
     p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
                     nseq=n, seqused_q=seqused_q, seqused_k=seqused_k)
     gd = q.dtype if grad_dtype is None else grad_dtype

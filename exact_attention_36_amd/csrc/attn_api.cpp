@@ -87,6 +87,12 @@ ScoreArgs score_args(const attn_params* p, float scale) {
 
 attn_status check_extent(int64_t max_q, int64_t max_k, const attn_params* p) {
   const int64_t D = p->head_dim;
+  const int64_t G = p->heads_q / p->heads_kv;
+  // The kernels divide a sequence's packed row index n < max_q * G by G with a
+  // multiply-high by ceil(2^32 / G), exact for n < 2^32 / G.
+  if (G >= 2 && max_q * G * G >= ((int64_t)1 << 32))
+    return fail(ATTN_ENOTSUP, "a sequence of %lld queries with %lld q heads per kv head exceeds the exact range "
+                "of the kernels' group division (queries * G^2 < 2^32)", (long long)max_q, (long long)G);
   if ((max_q + 256) * p->heads_q * D * 4 >= OFF_LIMIT)
     return fail(ATTN_ENOTSUP, "a sequence of %lld queries exceeds the 32-bit offset range", (long long)max_q);
   if ((max_k + BWD_BN) * p->heads_kv * D * 4 >= OFF_LIMIT)
@@ -150,12 +156,10 @@ int64_t dq_blocks(const attn_params* p, bool packed, int64_t nseq, int64_t sq, i
 }
 
 // Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like
-// lse; for bf16 inputs an fp16 copy of Q (layout of Q) that the dQ kernel
-// writes and the dK/dV kernel reads; with sinks, each dQ workgroup's sums of
-// the sink gradient per q head of its group ([Hkv][blocks][G]), which a last
-// kernel adds up in a fixed order.
+// lse; with sinks, each dQ workgroup's sums of the sink gradient per q head of
+// its group ([Hkv][blocks][G]), which a last kernel adds up in a fixed order.
 struct BwdWs {
-  size_t delta, lse2, q16, dsink_part, total;
+  size_t delta, lse2, dsink_part, total;
 };
 BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) {
   (void)grad_dtype;
@@ -163,9 +167,8 @@ BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) 
   const int64_t rows = tq * p->heads_q;
   w.delta = align_up(rows * 4);
   w.lse2 = align_up(rows * 4);
-  w.q16 = p->dtype == ATTN_BF16 ? align_up(rows * p->head_dim * 2) : 0;
   w.dsink_part = p->sinks ? align_up(nbq * p->heads_q * 4) : 0;  // Hkv * nbq * G = nbq * Hq
-  w.total = w.delta + w.lse2 + w.q16 + w.dsink_part;
+  w.total = w.delta + w.lse2 + w.dsink_part;
   return w;
 }
 
@@ -246,6 +249,11 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   const bool packed = cu_q != nullptr;
   const int64_t tq = packed ? total_q : nseq * sq;
   const int64_t nbq = dq_blocks(p, packed, nseq, sq, total_q);
+  // the row statistics (fp32 per query row and q head) are read through one
+  // buffer descriptor whose byte size must stay below 2^31
+  if (tq * p->heads_q >= ((int64_t)1 << 29))
+    return fail(ATTN_ENOTSUP, "%lld query rows x %d q heads exceed the backward's 2^29 row-statistics limit",
+                (long long)tq, p->heads_q);
   const BwdWs w = bwd_ws(p, tq, nbq, grad_dtype);
   attn_status st = check_ws(ws, ws_bytes, w.total);
   if (st != ATTN_OK) return st;
@@ -268,8 +276,6 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   wp += w.delta;
   a.lse2 = (float*)wp;
   wp += w.lse2;
-  a.q16 = w.q16 ? (uint16_t*)wp : nullptr;
-  wp += w.q16;
   a.dsink_part = w.dsink_part ? (float*)wp : nullptr;
   a.nbq = (int32_t)nbq;
   const float scale = resolve_scale(p);

@@ -133,13 +133,6 @@ void bwd_dq_kernel(const BwdArgs a) {
     qf[s] = buf_load16(rq, chunk_off(qoff, 2 * s + hh, dg));
     df[s] = buf_load16(rdo, chunk_off(qoff, 2 * s + hh, dg));
   }
-  // The fp16 copy of Q that the dK/dV kernel stages (bf16 inputs): every
-  // (query, q head) row is in exactly one of these work tiles.
-  if (a.q16) {
-    const auto rq16 = make_rsrc(a.q16 + qbase_e, qbytes);
-#pragma unroll
-    for (int s = 0; s < KS; s++) buf_store16(bf16x8_to_f16x8(qf[s]), rq16, chunk_off(qoff, 2 * s + hh, dg));
-  }
   // Row statistics, computed here once per (query row, q head) and left in
   // the workspace for the dK/dV kernel that runs after this one:
   //   D = rowsum(dO * O), O being the stored (sink-gated) output;
@@ -381,9 +374,10 @@ void bwd_dq_kernel(const BwdArgs a) {
 // column, registers = query rows), P and dS with the rows' lse' and D from
 // LDS, dV^T += dO^T P and dK^T += Q^T dS (dO, Q through transposing LDS
 // reads).  dS is kept in fp16 (10 fraction bits) for dK; the Q tiles are
-// therefore fp16 (for bf16 inputs, the copy the dQ kernel wrote; exact for
-// inputs inside fp16's range) and K, used for S, is converted likewise.  Q,
-// dO and the row statistics reach LDS by DMA, double buffered.
+// therefore fp16 and K, used for S, is converted likewise (exact for inputs
+// inside fp16's range, |x| <= 65504).  dO and the row statistics reach LDS by
+// DMA, double buffered; bf16 Q is loaded into registers one step ahead,
+// converted and written to LDS by the waves (fp16 Q goes by DMA as it is).
 template <int D, bool F16, bool PAD, int EXT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void bwd_dkdv_kernel(const BwdArgs a) {
@@ -448,7 +442,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const uint32_t kbytes = si.lk > 0 ? (uint32_t)(((int64_t)(si.lk - 1) * krow + dg) * 2) : 0u;
   // dK, dV are stored for every key row of the slot (zero past the used keys)
   const uint32_t kbytes_slot = (uint32_t)(((int64_t)(si.lk_slot - 1) * krow + dg) * 2);
-  const i32x4 rq16 = make_rsrc_words((F16 ? (const uint16_t*)a.q : (const uint16_t*)a.q16) + qbase_e, qbytes);
+  const i32x4 rq16 = make_rsrc_words((const uint16_t*)a.q + qbase_e, qbytes);  // DMA of fp16 Q
+  const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);            // register loads of bf16 Q
   const i32x4 rdo = make_rsrc_words((const uint16_t*)a.dout + qbase_e, qbytes);
   const auto rk = make_rsrc((const uint16_t*)a.k + kbase_e, kbytes);
   const int64_t st_base = a.s.cu_q ? si.q0 : (int64_t)seq * a.s.hq * a.s.sq;
@@ -481,22 +476,38 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
 
-  // Q (fp16) and dO tiles of one block of BM packed rows -> LDS by DMA, and
-  // the rows' lse' and D; rows past the sequence read as 0 (and are masked).
+  // Q and dO tiles of one block of BM packed rows -> LDS, and the rows' lse'
+  // and D; rows past the sequence read as 0 (and are masked).  Each wave
+  // moves SL 1 KB slabs of a tile: lane l's 16 bytes of slab n are global
+  // chunk pos ^ swz(r) of tile row r, stored at LDS byte slab * 1024 + 16 l.
+  constexpr int SL = QTILE / 1024 / 4;  // 1 KB slabs per wave
+  auto slab_src = [&](int pb, int n) __attribute__((always_inline)) {
+    const int slab = wave * SL + n;
+    const int byte = slab * 1024 + lane * 16;
+    const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
+    const int p = pb * BM + r;
+    const int i = div_group(p, a.s), hl = p - i * G;
+    return chunk_off((uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2), pos ^ swz<D>(r), dg);
+  };
   auto tile_dma = [&](const i32x4& rs, char* dst, int pb) __attribute__((always_inline)) {
-    constexpr int SL = QTILE / 1024 / 4;  // 1 KB slabs per wave
 #pragma unroll
-    for (int n = 0; n < SL; n++) {
-      const int slab = wave * SL + n;
-      const int byte = slab * 1024 + lane * 16;
-      const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
-      const int p = pb * BM + r;
-      const int i = div_group(p, a.s), hl = p - i * G;
-      dma_lds16(rs, dst + slab * 1024, chunk_off((uint32_t)(((int64_t)i * qrow + (int64_t)hl * dg) * 2), pos ^ swz<D>(r), dg));
-    }
+    for (int n = 0; n < SL; n++) dma_lds16(rs, dst + (wave * SL + n) * 1024, slab_src(pb, n));
+  };
+  // bf16 Q: this wave's slabs into registers (q_load), then as fp16 into LDS
+  // (q_store) once they have landed
+  u32x4 q_stage[F16 ? 1 : SL];
+  auto q_load = [&](int pb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < SL; n++) q_stage[n] = buf_load16(rq, slab_src(pb, n));
+  };
+  auto q_store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < SL; n++)
+      *LDS_PTR(u32x4, q_lds + buf * QTILE + (wave * SL + n) * 1024 + lane * 16) = bf16x8_to_f16x8(q_stage[n]);
   };
   auto do_fetch = [&](int pb, int buf) __attribute__((always_inline)) {
-    tile_dma(rq16, q_lds + buf * QTILE, pb);
+    if constexpr (F16) tile_dma(rq16, q_lds + buf * QTILE, pb);
+    else q_load(pb);
     tile_dma(rdo, do_lds + buf * QTILE, pb);
     if constexpr (ALIBI) {
       // each row's diagonal i + Lk - Lq and slope/scale, for the variant logits
@@ -510,8 +521,10 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int p = pb * BM + l32;
       const int i = div_group(p, a.s), hl = p - i * G;
       const int64_t idx = st_base + (int64_t)(g * G + hl) * st_hs + i;
-      // rows past the sequence read index 0 (valid memory); they are masked
-      const uint32_t off = p < prows ? (uint32_t)(idx * 4) : 0u;
+      // rows past the sequence fall outside the descriptor and read as 0
+      // (lse' = 0, D = 0): their scores are masked to -inf, so P = 0 and
+      // dS = 0 * (dP - 0) = 0 whatever the workspace holds there
+      const uint32_t off = p < prows ? (uint32_t)(idx * 4) : DROP_ROW;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(st_lds + buf * 64));
       // lanes 0-31 fetch lse', lanes 32-63 fetch D: lane l's dword lands at m0 + 4 l
       if (hh == 0)
@@ -562,13 +575,26 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     __syncthreads();
   }
   const float keyf = (float)my_key;
-  if (pb_begin < pb_end) do_fetch(pb_begin, 0);
-  for (int pb = pb_begin; pb < pb_end; pb++) {
-    const int buf = (pb - pb_begin) & 1;
-    wait_vmcnt<0>();               // Q, dO tiles, row statistics (and V block) are in LDS
-    if constexpr (ALIBI) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the per-row ALiBi terms
-    __builtin_amdgcn_s_barrier();  // everyone's writes visible; everyone is done with step pb-1
-    if (pb + 1 < pb_end) do_fetch(pb + 1, buf ^ 1);  // buffers of step pb-1, which everyone has left
+  // The query blocks are visited last to first: under a causal mask every key
+  // block of a sequence sees its last query block, so the workgroups of one
+  // sequence (dispatched together, on one XCD) start at the same Q / dO tiles
+  // and walk them in step, sharing them in L2.
+  const int nsteps = pb_end - pb_begin;
+  if (nsteps > 0) {
+    do_fetch(pb_end - 1, 0);
+    if constexpr (!F16) {
+      wait_vmcnt<0>();
+      q_store(0);
+    }
+  }
+  for (int it = 0; it < nsteps; it++) {
+    const int pb = pb_end - 1 - it;
+    const int buf = it & 1;
+    wait_vmcnt<0>();               // dO tile, row statistics (and V block) are in LDS
+    // the Q tile's LDS writes (and with ALiBi the per-row terms) are done
+    if constexpr (ALIBI || !F16) wait_lgkm0();
+    __builtin_amdgcn_s_barrier();  // everyone's writes visible; everyone is done with the previous step
+    if (it + 1 < nsteps) do_fetch(pb - 1, buf ^ 1);  // buffers of the previous step, which everyone has left
     const char* qt = q_lds + buf * QTILE;
     const char* dot = do_lds + buf * QTILE;
     const float* stt = st_lds + buf * 64;
@@ -683,6 +709,14 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     // dV/dK: 4 transposing reads feed 2 MFMAs per step, 2 steps ahead
     sched_reads_ahead<KS, 2, 3, 2>();
     sched_reads_ahead<2 * DB, 2, 4, 2>();
+    if constexpr (!F16) {
+      // the next step's Q into the other buffer, which every wave left before
+      // this step's barrier
+      if (it + 1 < nsteps) {
+        wait_vmcnt<0>();
+        q_store(buf ^ 1);
+      }
+    }
   }
 
   // ---- epilogue: dK = scale * dK_acc, dV; lane = key, registers = dims

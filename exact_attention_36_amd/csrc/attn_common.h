@@ -9,9 +9,11 @@ namespace attn {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
-// n / group for 0 <= n < 2^23 (packed rows of one sequence; the host bounds
-// sequence extents so that this holds): with M = ceil(2^32 / G) the error of
-// n*M/2^32 is below n/2^32 < 1/512 < 1/G, so the high word is the quotient.
+// n / group for 0 <= n < 2^32 / G (packed rows of one sequence; the host
+// rejects sequences with queries * G^2 >= 2^32): with M = ceil(2^32 / G),
+// n*M/2^32 = n/G + n*(M - 2^32/G)/2^32 exceeds n/G by less than n/2^32 < 1/G,
+// which cannot carry past the next multiple of 1/G, so the high word is the
+// quotient.
 __device__ __forceinline__ int div_group(int n, const SeqArgs& s) {
   return s.group == 1 ? n : (int)__umulhi((uint32_t)n, s.group_magic);
 }

@@ -91,7 +91,6 @@ struct BwdArgs {
   int32_t nbq;            // dQ workgroups per kv head (batched: nseq * nmb; packed: nblk_q)
   float* delta;           // fp32, laid out like lse: D_i = <dO_i, O_i>
   float* lse2;            // fp32, laid out like lse: log-sum-exp with the sink, in log2 units
-  uint16_t* q16;          // fp16 copy of Q (layout of Q) for bf16 inputs, written by the dQ kernel; nullptr for fp16
   void* dq; void* dk; void* dv;
   int32_t grad_f32;       // gradients written as fp32 (else the input dtype)
   float scale;            // softmax scale

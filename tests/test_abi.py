@@ -181,3 +181,20 @@ def test_append_and_rotary_reject_bad_arguments():
     assert rot(pos=None) == _lib.ATTN_EINVAL
     assert rot(per=3) == _lib.ATTN_EINVAL
     assert rot(rd=0) == _lib.ATTN_EINVAL
+
+
+def test_thirty_two_bit_limits_are_rejected():
+    """Sizes past the kernels' 32-bit index arithmetic: the fast division of a
+    sequence's packed rows by the group size (exact for queries * G^2 < 2^32)
+    and the backward's row-statistics descriptor (query rows x q heads < 2^29)."""
+    lib = ea.load_library()
+    # G = 128, D = 8: the byte-offset check passes, the group division does not
+    p = _params(heads_q=128, heads_kv=1, head_dim=8)
+    assert _fwd(p, sq=300000, sk=16) == _lib.ATTN_ENOTSUP
+    assert "group division" in ea.last_error()
+    assert _fwd(p, sq=200000, sk=16, lse=None) == _lib.ATTN_EINVAL  # within range: fails on the NULL lse instead
+    p = _params(heads_q=64, heads_kv=64, head_dim=8, causal=0)
+    args = [FAKE] * 9
+    st = lib.attn_bwd(ctypes.byref(p), 16, 600000, 16, *args, None, _lib.ATTN_BF16, FAKE, 1 << 40, None)
+    assert st == _lib.ATTN_ENOTSUP
+    assert "row-statistics" in ea.last_error()

@@ -12,7 +12,7 @@ import torch
 import oracle
 from exact_attention_36_amd import synth
 import exact_attention_36_amd as ea
-from _helpers import assert_close, assert_lse, dev_tensor, host, scale_of
+from _helpers import check_dsinks, assert_close, assert_lse, dev_tensor, host, scale_of
 
 pytestmark = pytest.mark.gpu
 
@@ -145,4 +145,4 @@ def test_seqused_forward_backward(case):
     assert_close(name + ".dk", dkh, ref["dk"], "f32")  # unused keys: exactly 0 on both sides
     assert_close(name + ".dv", dvh, ref["dv"], "f32")
     if sinks:
-        assert np.abs(host(ds) - ref["dsinks"]).max() <= 2e-2 + 1e-3 * np.abs(ref["dsinks"]).max()
+        check_dsinks(name + ".dsinks", host(ds), ref["dsinks"], p)
