@@ -20,7 +20,7 @@ ATTN_OK, ATTN_EINVAL, ATTN_ENOTSUP, ATTN_EHIP = 0, 1, 2, 3
 ATTN_BF16, ATTN_FP16, ATTN_FP32 = 0, 1, 2
 
 EXPORTED = (
-    "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size",
+    "attn_fwd", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_workspace_size", "attn_bwd_noalloc",
     "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size", "attn_kvcache_append", "attn_rotary",
     "attn_fwd_varlen", "attn_fwd_varlen_workspace_size", "attn_bwd_varlen",
     "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable", "attn_timing_select",
@@ -66,6 +66,7 @@ def load_library():
     lib.attn_fwd_workspace_size.argtypes = [P, i64, i64, i64]
     lib.attn_bwd.argtypes = [P, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.attn_bwd_workspace_size.argtypes = [P, i64, i64, i64, i32]
+    lib.attn_bwd_noalloc.argtypes = [P, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
     lib.attn_fwd_kvcache.argtypes = [P, i64, i64, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, sz, vp]
     lib.attn_fwd_kvcache_workspace_size.argtypes = [P, i64, i64, vp, i32, i32, i64]
     lib.attn_kvcache_append.argtypes = [P, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, i32, i64, vp, vp, i32, i32,
@@ -279,6 +280,44 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, s
                         _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _dtype_code(gd),
                         _ptr(ws), n, _stream(q.device)))
     return dq, dk, dv, dsinks
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks=None, softmax_scale=None,
+                     softcap=0.0, alibi_slopes=None, sinks_shared=False, seqused_q=None, seqused_k=None,
+                     grad_dtype=None, dq=None, dk=None, dv=None, dsinks=None):
+    """Batched backward through attn_bwd_noalloc (the library's fixed scratch
+    instead of a workspace) -> (dq, dk, dv, dsinks or None).  Pass dq, dk, dv
+    (and dsinks) to have nothing allocated on this side either."""
+    lib = load_library()
+    _need(q.dim() == 4 and k.dim() == 4, "q, k, v must be [B, S, H, D]")
+    B, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    _need(grad_dtype in (None, q.dtype, torch.float32),
+          "grad_dtype must be the input dtype or torch.float32, got %s" % grad_dtype)
+    gd = q.dtype if grad_dtype is None else grad_dtype
+    _check_f32("lse", lse, (B, hq, sq))
+    for n, t, shp in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, v.shape)):
+        if t is not None:
+            _need(t.dtype == gd and tuple(t.shape) == tuple(shp), "%s must be %s %s" % (n, gd, tuple(shp)))
+    if dsinks is not None and sinks is not None:
+        _check_f32("dsinks", dsinks, tuple(sinks.shape))
+    _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, dsinks=dsinks),
+                   dtype=("q", "k", "v", "o", "dout"),
+                   shapes=dict(k=(B, None, None, d), v=(B, sk, hkv, d), o=(B, sq, hq, d), dout=(B, sq, hq, d)))
+    p = make_params(q, k, causal, window, sinks, softmax_scale, softcap, alibi_slopes, sinks_shared,
+                    nseq=B, seqused_q=seqused_q, seqused_k=seqused_k)
+    dq = torch.empty(q.shape, dtype=gd, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=gd, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=gd, device=q.device) if dv is None else dv
+    if sinks is not None and dsinks is None:
+        dsinks = torch.empty(sinks.shape, dtype=torch.float32, device=q.device)
+    _check(lib.attn_bwd_noalloc(ctypes.byref(p), B, sq, sk, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks if sinks is not None else None),
+                                _dtype_code(gd), _stream(q.device)))
+    return dq, dk, dv, (dsinks if sinks is not None else None)
 
 
 def _check_rotary(rotary_cos, rotary_sin):

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libattn36.so")
-SOURCES = ["attn_api.cpp", "attn_timing.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_cache.hip",
+SOURCES = ["attn_api.cpp", "attn_timing.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_cache.hip", "attn_noalloc.hip",
            # one translation unit per score variant, compiled in parallel
            "attn_fwd_cap.hip", "attn_fwd_alibi.hip", "attn_fwd_cap_alibi.hip",
            "attn_bwd_cap.hip", "attn_bwd_alibi.hip", "attn_bwd_cap_alibi.hip"]

@@ -485,10 +485,9 @@ attn_status attn_fwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int6
                  lse, ws, ws_bytes, stream);
 }
 
-attn_status attn_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
-                     const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-                     void* dk, void* dv, float* dsinks, int32_t grad_dtype, void* ws, size_t ws_bytes,
-                     void* stream) {
+static attn_status check_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
+                             const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv, float* dsinks, int32_t grad_dtype) {
   attn_status st = check_params(p);
   if (st != ATTN_OK) return st;
   if ((st = check_grad_dtype(p, grad_dtype)) != ATTN_OK) return st;
@@ -501,6 +500,33 @@ attn_status attn_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int6
   if ((st = check_extent(seqlen_q, seqlen_k, p)) != ATTN_OK) return st;
   if (batch * seqlen_q * (p->heads_q / p->heads_kv) >= INT32_MAX || batch >= INT32_MAX)
     return fail(ATTN_ENOTSUP, "problem too large");
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_noalloc(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
+                             const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float* dsinks, int32_t grad_dtype,
+                             void* stream) {
+  attn_status st = check_bwd(p, batch, seqlen_q, seqlen_k, q, k, v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = bwd_ws(p, batch * seqlen_q, dq_blocks(p, false, batch, seqlen_q, 0), grad_dtype).total;
+  if (need > ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTN_ENOTSUP, "attn_bwd_noalloc: this call needs %zu bytes of workspace, more than the %zu bytes "
+                "of fixed scratch (use attn_bwd with a workspace)", need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(ATTN_EHIP, "attn_bwd_noalloc: scratch lookup failed: %s", hipGetErrorString(e));
+  return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k, q, k,
+                 v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ATTN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+attn_status attn_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
+                     const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                     void* dk, void* dv, float* dsinks, int32_t grad_dtype, void* ws, size_t ws_bytes,
+                     void* stream) {
+  const attn_status st =
+      check_bwd(p, batch, seqlen_q, seqlen_k, q, k, v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype);
+  if (st != ATTN_OK) return st;
   return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k, q, k,
                  v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ws_bytes, stream);
 }

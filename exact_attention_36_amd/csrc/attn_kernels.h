@@ -139,5 +139,8 @@ hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st);
 hipError_t launch_rotary(const void* x, void* out, int64_t rows, int S, int H, int D, const int32_t* pos0,
                          int per_token, const RotaryArgs& r, bool f16, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int32_t* seqlens_out, bool f16, hipStream_t st);
+// Device address of the fixed scratch behind attn_bwd_noalloc on the current
+// device (attn_noalloc.hip).
+hipError_t noalloc_scratch(void** out);
 
 }  // namespace attn

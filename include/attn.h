@@ -160,6 +160,29 @@ size_t attn_bwd_workspace_size(const attn_params *params, int64_t batch, int64_t
                                int64_t seqlen_k, int32_t grad_dtype);
 
 /*
+ * Backward that allocates nothing: attn_bwd with the library's own fixed
+ * device scratch in place of a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc).  Arguments, outputs and
+ * results are attn_bwd's.  The scratch is a static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load on that
+ * GPU until the process ends; its address is looked up on the first call on
+ * each device (so make that first call before capturing a graph).  A call
+ * needing more than ATTN_NOALLOC_SCRATCH_BYTES of workspace (what
+ * attn_bwd_workspace_size returns: 8 bytes per query row and q head, plus
+ * 4 bytes per q head and 128-row query block with sinks) returns ATTN_ENOTSUP
+ * before anything is launched.  Nothing in the scratch needs clearing
+ * between calls (every byte a call reads, that call's kernels wrote first),
+ * but all calls on one GPU share it: calls that can overlap on one GPU (two
+ * streams, two threads) race and must be ordered by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status attn_bwd_noalloc(const attn_params *params, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
+                             const void *q, const void *k, const void *v, const void *o, const float *lse,
+                             const void *dout, void *dq, void *dk, void *dv, float *dsinks,
+                             int32_t grad_dtype, void *stream);
+
+/*
  * Forward over a KV cache (decode / chunked prefill; forward only).  q is
  * [B, seqlen_q, Hq, D]; slot b of the cache holds cache_seqlens[b] valid keys
  * (device int32 [B]): later keys are invisible and the causal / window band

@@ -198,3 +198,20 @@ def test_thirty_two_bit_limits_are_rejected():
     st = lib.attn_bwd(ctypes.byref(p), 16, 600000, 16, *args, None, _lib.ATTN_BF16, FAKE, 1 << 40, None)
     assert st == _lib.ATTN_ENOTSUP
     assert "row-statistics" in ea.last_error()
+
+
+def test_noalloc_backward_refuses_oversize_and_bad_arguments():
+    """attn_bwd_noalloc checks its arguments like attn_bwd and refuses, on the
+    host, a call whose workspace would not fit the fixed scratch."""
+    lib = ea.load_library()
+    args = [FAKE] * 9
+    p = _params(heads_q=64, heads_kv=64)
+    assert lib.attn_bwd_noalloc(ctypes.byref(p), 64, 8192, 8192, *args, None, _lib.ATTN_BF16, None) == \
+        _lib.ATTN_ENOTSUP
+    assert "fixed scratch" in ea.last_error()
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params()), 1, 16, 16, *args, None, _lib.ATTN_FP16, None) == \
+        _lib.ATTN_EINVAL
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params()), 0, 16, 16, *args, None, _lib.ATTN_BF16, None) == \
+        _lib.ATTN_EINVAL
+    assert lib.attn_bwd_noalloc(ctypes.byref(_params(sinks=0x2000)), 1, 16, 16, *args, None, _lib.ATTN_BF16,
+                                None) == _lib.ATTN_EINVAL
