@@ -2,18 +2,23 @@
 causal prefill workload B=4, Hq=Hkv=16, S=2048, D=128, bf16 (seeded synthetic
 N(0,1) inputs resident in HBM), through the C ABI.
 
-Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s
-(14 * D * visible (query, key) pairs per step: 4*D forward, 10*D backward).
+Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s (14 * D * visible
+(query, key) pairs per step: 4*D forward, 10*D backward) at the median of the
+K timed steps, each timed with HIP events after a 512 MB write that flushes
+the MALL (min, p90 and the unflushed "warm" steps are reported beside it).
 `roofline` reports the kernel with the most time per step (found in a pass
 with every launch timed), whose launches in the timed region are bracketed by
-HIP events on the library's stream (the other kernels run untimed there);
-`decode` measures the decode-shaped forward (B=32, s_q=16, s_kv=32768,
-Hq=64, Hkv=8) as K/V HBM GB/s;
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the
-prefill workload.  `--workload decode` runs only the decode shape;
-`--workload sweep`, `headdims`, `variants` and `configs` (the five parity
-workloads) print one line per shape;
-`--workload latency` times the launch-bound shape eagerly and as graph replays.
+HIP events on the library's stream.  `config_lines` measures the other
+workloads the same way -- the tiny forward (config 1, µs per call), GQA with a
+window and sinks (config 3) and the packed batch (config 4), forward and
+backward against the MFMA and HBM rooflines -- and `decode` the decode-shaped
+forward (config 5) as K/V HBM GB/s, contiguous and paged.  `cpu_baseline`
+times the fp64 CPU oracle on whole (batch, head) slices of the workload,
+checks the GPU's outputs of the timed steps against those slices, and samples
+query rows of the other configs.  `--workload decode` runs only the decode
+shape; `--workload sweep`, `headdims`, `variants` and `configs` (the five
+parity workloads) print one line per shape; `--workload latency` times the
+launch-bound shape eagerly and as graph replays.
 """
 from __future__ import annotations
 
@@ -104,11 +109,52 @@ def copy_calibration():
 
 DECODE = dict(name="decode / chunked-prefill fwd B32 s_q16 s_kv32768 Hq64 Hkv8 D128 bf16 causal", B=32, SQ=16,
               SK=32768, HQ=64, HKV=8, D=128)
+FLUSH_BYTES = 512 << 20  # twice the 256 MB MALL (last-level cache)
 
 
-def run_decode(steps, warmup):
-    """The decode-shaped forward (split-KV): time per call (split kernel +
-    combine, HIP events on the library's stream) and the K/V bytes it must
+class Flusher:
+    """Writes a 512 MB buffer (a fill kernel on the current stream), which
+    evicts the K/V tiles the previous repetition left in the MALL."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i = (self.i + 1) & 0xFF
+        self.buf.fill_(self.i)
+
+
+def time_each(fn, reps, flush=None):
+    """Per-repetition milliseconds of fn() from HIP events on the current
+    stream (the library's stream); with `flush`, the MALL flush runs before
+    each repetition, outside its events."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def summary(ts):
+    """median, min and p90 (nearest rank) of a list of milliseconds."""
+    a = sorted(ts)
+    n = len(a)
+    med = a[n // 2] if n % 2 else 0.5 * (a[n // 2 - 1] + a[n // 2])
+    p90 = a[min(n - 1, max(0, -(-9 * n // 10) - 1))]
+    return {"median": round(med, 5), "min": round(a[0], 5), "p90": round(p90, 5), "n": n}
+
+
+def run_decode(steps, warmup, flush=None):
+    """The decode-shaped forward (split-KV split kernel + combine): per call
+    milliseconds (HIP events around the whole call, median of `steps`, the
+    MALL flushed before each unless flush is None) and the K/V bytes it must
     stream from HBM, as GB/s and a fraction of the 8 TB/s peak."""
     import torch
     import exact_attention_36_amd as ea
@@ -117,31 +163,25 @@ def run_decode(steps, warmup):
     q, k, v = synth.device_normal(5, [(d["B"], d["SQ"], d["HQ"], d["D"]), (d["B"], d["SK"], d["HKV"], d["D"]),
                                       (d["B"], d["SK"], d["HKV"], d["D"])])
     o, lse = ea.attn_fwd(q, k, v, causal=True)
+    call = lambda: ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
     for _ in range(warmup):
-        ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+        call()
     torch.cuda.synchronize()
-    ea.attn_timing_enable(True)
-    for _ in range(steps):
-        ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
-    torch.cuda.synchronize()
-    n_s, ms_s = ea.attn_timing_read("fwd")
-    n_c, ms_c = ea.attn_timing_read("fwd_combine")
-    ea.attn_timing_enable(False)
-    per_call_ms = (ms_s + ms_c) / steps
+    st = summary(time_each(call, steps, flush))
+    warm = summary(time_each(call, steps))
     kv_bytes = 2 * d["B"] * d["SK"] * d["HKV"] * d["D"] * 2
-    gbps = kv_bytes / (per_call_ms * 1e-3) / 1e9
+    gbps = kv_bytes / (st["median"] * 1e-3) / 1e9
     pairs = visible_pairs(d["B"], d["SQ"], d["SK"], d["HQ"], True, (-1, -1))
     del q, k, v, o, lse
     torch.cuda.empty_cache()
-    return {"workload": d["name"], "ms_per_call": round(per_call_ms, 4),
-            "split_kernel_ms": round(ms_s / max(n_s, 1), 4), "combine_ms": round(ms_c / max(n_c, 1), 4),
-            "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1), "hbm_peak_GBps": HBM_PEAK_GBS,
-            "frac": round(gbps / HBM_PEAK_GBS, 4),
+    return {"workload": d["name"], "ms_per_call": st, "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1),
+            "hbm_peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4),
+            "warm_ms_per_call": warm, "warm_kv_GBps": round(kv_bytes / (warm["median"] * 1e-3) / 1e9, 1),
             "traffic": traffic_from_profile("fwd_decode"), "traffic_unit": "bytes per split-kernel launch",
-            "tflops": round(4.0 * d["D"] * pairs / (per_call_ms * 1e-3) / 1e12, 2)}
+            "tflops": round(4.0 * d["D"] * pairs / (st["median"] * 1e-3) / 1e12, 2)}
 
 
-def run_kvcache(steps, warmup, page=256):
+def run_kvcache(steps, warmup, flush=None, page=256):
     """The decode shape served from a paged KV cache (attn_fwd_kvcache): every
     slot full (cache_seqlens = 32768), pages of `page` rows dealt to the slots
     in a seeded random order; time per call and K/V GB/s as run_decode."""
@@ -157,19 +197,13 @@ def run_kvcache(steps, warmup, page=256):
                              .reshape(d["B"], npg)).cuda()
     lens = torch.full((d["B"],), d["SK"], dtype=torch.int32, device="cuda")
     o, lse = ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True)
+    call = lambda: ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True, out=o, lse=lse)  # noqa: E731
     for _ in range(warmup):
-        ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True, out=o, lse=lse)
+        call()
     torch.cuda.synchronize()
-    ea.attn_timing_enable(True)
-    for _ in range(steps):
-        ea.attn_fwd_kvcache(q, k, v, lens, block_table=table, causal=True, out=o, lse=lse)
-    torch.cuda.synchronize()
-    n_s, ms_s = ea.attn_timing_read("fwd")
-    n_c, ms_c = ea.attn_timing_read("fwd_combine")
-    ea.attn_timing_enable(False)
-    per_call_ms = (ms_s + ms_c) / steps
+    st = summary(time_each(call, steps, flush))
     kv_bytes = 2 * d["B"] * d["SK"] * d["HKV"] * d["D"] * 2
-    gbps = kv_bytes / (per_call_ms * 1e-3) / 1e9
+    gbps = kv_bytes / (st["median"] * 1e-3) / 1e9
     # The cache update of a decode step: the SQ new keys/values of every slot
     # written at its used length (keys rotated, rotary over all D dims) and q
     # rotated -- attn_kvcache_append + attn_rotary, timed together with events.
@@ -180,6 +214,7 @@ def run_kvcache(steps, warmup, page=256):
     lens0 = lens - d["SQ"]
     grown = torch.empty_like(lens)
     qr = torch.empty_like(q)
+
     def update():
         ea.attn_kvcache_append(kn, vn, k, v, lens0, block_table=table, rotary_cos=cos, rotary_sin=sin,
                                rotary_interleaved=False, seqlens_out=grown)
@@ -187,24 +222,17 @@ def run_kvcache(steps, warmup, page=256):
     for _ in range(warmup):
         update()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        update()
-    e1.record()
-    torch.cuda.synchronize()
-    upd_ms = e0.elapsed_time(e1) / steps
+    upd = summary(time_each(update, steps))
     upd_bytes = 2 * (2 * kn.numel() * 2 + q.numel() * 2)  # k, v new rows and q: read once, written once
     del q, k, v, o, lse, table, kn, vn, qr
     torch.cuda.empty_cache()
     return {"workload": d["name"] + " paged KV cache (pages of %d rows, shuffled)" % page,
-            "ms_per_call": round(per_call_ms, 4), "split_kernel_ms": round(ms_s / max(n_s, 1), 4),
-            "combine_ms": round(ms_c / max(n_c, 1), 4), "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1),
+            "ms_per_call": st, "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1),
             "hbm_peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4),
             "update": {"what": "append %d new keys/values per slot (keys rotated) + rotate q; eager calls, "
-                               "three small launches: launch-bound" % d["SQ"],
-                       "ms": round(upd_ms, 4), "bytes": upd_bytes,
-                       "GBps": round(upd_bytes / (upd_ms * 1e-3) / 1e9, 1)}}
+                               "three small launches: launch-bound (warm)" % d["SQ"],
+                       "ms": upd, "bytes": upd_bytes,
+                       "GBps": round(upd_bytes / (upd["median"] * 1e-3) / 1e9, 1)}}
 
 
 def run_sweep(steps, warmup):
@@ -367,33 +395,234 @@ def run_latency(steps, warmup):
     return row
 
 
-def cpu_baseline(inp, w, seconds_target=15.0):
-    """Time the fp64 oracle on whole (batch, head) slices of the workload."""
+def compulsory_bytes(qt, kvt, rows, bwd):
+    """HBM bytes a pass must move, each tensor once: forward Q K V in, O and
+    the fp32 LSE out; backward Q K V O dO and LSE in, dQ dK dV out."""
+    return (4 * qt + 4 * kvt + 4 * rows) if bwd else (2 * qt + 2 * kvt + 4 * rows)
+
+
+def roof(flop, nbytes, st):
+    """Rates of one timed pass (`st` from summary()) against the MFMA and HBM
+    rooflines: the attainable time is max(flop / 2.5 PFLOP/s, bytes / 8 TB/s)."""
+    ms = st["median"]
+    t_mfma = flop / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"ms": st, "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_bytes": int(nbytes), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "attainable_ms": round(max(t_mfma, t_hbm), 5), "frac_of_attainable": round(max(t_mfma, t_hbm) / ms, 4)}
+
+
+def config3_inputs():
+    """GQA 32/8, S = 8192, B = 2, window (127, 0), fp32 sinks [32]."""
+    import numpy as np
+    import torch
+    from exact_attention_36_amd import synth
+    q, k, v, do = synth.device_normal(3, [(2, 8192, 32, 128), (2, 8192, 8, 128), (2, 8192, 8, 128), (2, 8192, 32, 128)])
+    sinks = torch.from_numpy(np.random.default_rng(3).standard_normal(32).astype(np.float32)).cuda()
+    return q, k, v, do, sinks
+
+
+def config4_inputs():
+    """Packed batch: 64 sequence lengths of the packed-workload recipe (seed 4,
+    the same lengths as the parity tests), tensors drawn on the device."""
+    import numpy as np
+    import torch
+    from exact_attention_36_amd import synth
+    L = synth.packed_lengths(np.random.default_rng(4))
+    cu = synth.cu_seqlens(L)
+    T = int(cu[-1])
+    q, k, v, do = synth.device_normal(4, [(T, 16, 128), (T, 4, 128), (T, 4, 128), (T, 16, 128)])
+    return q, k, v, do, torch.from_numpy(cu).cuda(), L
+
+
+def run_config_lines(steps, warmup, flush):
+    """Configs 1, 3 and 4 (config 2 is the headline step, config 5 the decode
+    line): forward and backward each timed `steps` times (MALL flushed before
+    each), median / min / p90 and rates against the rooflines."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    out = {}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        return summary(time_each(fn, steps, flush))
+
+    q, k, v = synth.device_normal(1, [(1, 128, 2, 64)] * 3)
+    o, lse = ea.attn_fwd(q, k, v)
+    st = timed(lambda: ea.attn_fwd(q, k, v, out=o, lse=lse))
+    out["config1"] = {"workload": "fwd B1 H2 S128 D64 bf16 non-causal (launch-bound: µs per eager call)",
+                      "us_per_call": {k_: (round(v_ * 1e3, 2) if k_ != "n" else v_) for k_, v_ in st.items()}}
+    del q, k, v, o, lse
+
+    q, k, v, do, sinks = config3_inputs()
+    kw = dict(causal=True, window=(127, 0), sinks=sinks)
+    o, lse = ea.attn_fwd(q, k, v, **kw)
+    pairs = visible_pairs(2, 8192, 8192, 32, True, (127, 0))
+    qt, kvt, rows = q.numel() * 2, k.numel() * 2, 2 * 32 * 8192
+    sf = timed(lambda: ea.attn_fwd(q, k, v, out=o, lse=lse, **kw))
+    sb = timed(lambda: ea.attn_bwd(q, k, v, o, lse, do, **kw))
+    out["config3"] = {"workload": "GQA 32/8 causal window (127,0) sinks B2 S8192 D128 bf16 fwd+bwd",
+                      "fwd": roof(4.0 * 128 * pairs, compulsory_bytes(qt, kvt, rows, False), sf),
+                      "bwd": roof(10.0 * 128 * pairs, compulsory_bytes(qt, kvt, rows, True), sb)}
+    del q, k, v, do, sinks, o, lse
+    torch.cuda.empty_cache()
+
+    q, k, v, do, cu, L = config4_inputs()
+    mx = int(L.max())
+    o, lse = ea.attn_fwd_varlen(q, k, v, cu, cu, mx, mx, causal=True)
+    pairs = 16 * sum(int(x) * (int(x) + 1) // 2 for x in L)
+    qt, kvt, rows = q.numel() * 2, k.numel() * 2, 16 * q.shape[0]
+    sf = timed(lambda: ea.attn_fwd_varlen(q, k, v, cu, cu, mx, mx, causal=True, out=o, lse=lse))
+    sb = timed(lambda: ea.attn_bwd_varlen(q, k, v, o, lse, do, cu, cu, mx, mx, causal=True))
+    out["config4"] = {"workload": "packed 65536 tokens in 64 sequences (8 empty) GQA 16/4 D128 bf16 causal fwd+bwd",
+                      "fwd": roof(4.0 * 128 * pairs, compulsory_bytes(qt, kvt, rows, False), sf),
+                      "bwd": roof(10.0 * 128 * pairs, compulsory_bytes(qt, kvt, rows, True), sb)}
+    del q, k, v, do, o, lse
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _max_err(got, ref):
+    import numpy as np
+    e = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    return float(e.max()), float(e.mean())
+
+
+def cpu_baseline(inp, w, gpu_out, seconds_target=10.0):
+    """The fp64 oracle (unchanged) on the host's cores.
+
+    Headline: whole (batch, head) slices of the benchmarked workload, forward
+    and backward, for about `seconds_target` seconds, as TFLOP/s (14 * D flops
+    per visible pair, the GPU's convention); the same slices of the GPU's own
+    outputs from the timed steps are compared with them (max-abs and mean-abs
+    errors of O, dQ, dK, dV, LSE).  Per other config: a seeded sample of query
+    rows (their O, LSE, D and dQ), with seconds, rows/s and visible pairs/s,
+    and the full-config fwd+bwd time extrapolated from that rate (rows plus
+    key columns: two passes over the visible pairs)."""
     import numpy as np
     import oracle
     from exact_attention_36_amd import synth
     D, S = w["D"], w["S"]
     scale = synth.default_scale(D)
-    done_pairs, t_used, slices = 0, 0.0, 0
+    host = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    go = {n: host(t) for n, t in gpu_out.items()}
+    done_pairs, t_used, slices, worst = 0, 0.0, 0, {}
     for b in range(w["B"]):
         for h in range(w["HQ"]):
-            sl = lambda a, hh=h: np.ascontiguousarray(a[b:b + 1, :, hh:hh + 1, :])
+            sl = lambda a, hh=h: np.ascontiguousarray(a[b:b + 1, :, hh:hh + 1, :])  # noqa: E731
             p = oracle.batched(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), scale, causal=w["causal"],
                                window=w["window"], dout=sl(inp["dout"]))
             t0 = time.perf_counter()
-            oracle.full(p, grads=True)
+            ref = oracle.full(p, grads=True)
             t_used += time.perf_counter() - t0
             done_pairs += visible_pairs(1, S, S, 1, w["causal"], w["window"])
             slices += 1
+            for name, got, r in (("o", go["o"][b, :, h], ref["o"][:, 0]), ("dq", go["dq"][b, :, h], ref["dq"][:, 0]),
+                                 ("dk", go["dk"][b, :, h], ref["dk"][:, 0]), ("dv", go["dv"][b, :, h], ref["dv"][:, 0]),
+                                 ("lse", go["lse"][b, h], ref["lse"][0])):
+                mx, mn = _max_err(got, r)
+                m0 = worst.get(name, (0.0, 0.0))
+                worst[name] = (max(m0[0], mx), max(m0[1], mn))
             if t_used >= seconds_target:
                 break
         if t_used >= seconds_target:
             break
     flops = 14.0 * D * done_pairs
-    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "%d full (batch, head) slices of %dx%d causal, fwd+bwd (O, LSE, dQ, dK, dV), "
-                      "%.1f s" % (slices, S, S, t_used)}
+    ok = all(worst[n][0] <= (1e-3 if n == "lse" else 2e-2 + 2 ** -5) and (n == "lse" or worst[n][1] <= 2e-3)
+             for n in worst)
+    res = {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": "%d full (batch, head) slices of the %dx%d causal workload, fwd+bwd (O, LSE, dQ, dK, dV), "
+                     "%.1f s" % (slices, S, S, t_used),
+           "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+           "threads_used": oracle.num_threads(),
+           "full_config_seconds_extrapolated": round(14.0 * D * visible_pairs(w["B"], S, S, w["HQ"], w["causal"],
+                                                                              w["window"]) / (flops / t_used), 1),
+           "gpu_output_check": {"slices": slices, "max_abs": {n: float("%.3g" % v[0]) for n, v in worst.items()},
+                                "mean_abs": {n: float("%.3g" % v[1]) for n, v in worst.items()},
+                                "within_tolerance": bool(ok),
+                                "tolerance": "max-abs 2e-2 (+ half a bf16 ulp, at most 2^-5, for |x| >= 4), "
+                                             "mean-abs 2e-3, LSE 1e-3"}}
+    res["configs"] = oracle_config_rates()
+    return res
+
+
+def oracle_config_rates(rows_per_config=192, seed=1000):
+    """Seeded samples of query rows of configs 1, 3, 4 and 5 through the oracle
+    (forward and backward row quantities), with the rate and the full-config
+    fwd+bwd time extrapolated from it."""
+    import numpy as np
+    import torch
+    import oracle
+    from exact_attention_36_amd import synth
+    rng = np.random.default_rng(seed)
+    res = {}
+
+    def sample(name, p, seq_pool, hq, lq_of, full_pairs, vis_of):
+        n = rows_per_config
+        seqs = rng.choice(np.asarray(seq_pool), n)
+        heads = rng.integers(0, hq, n)
+        rows = np.array([rng.integers(0, max(1, lq_of(s_))) for s_ in seqs])
+        pairs = sum(vis_of(int(s_), int(r_)) for s_, r_ in zip(seqs, rows))
+        t0 = time.perf_counter()
+        oracle.rows(p, seqs, heads, rows, grads=True)
+        dt = time.perf_counter() - t0
+        rate = pairs / dt
+        res[name] = {"rows": n, "seconds": round(dt, 3), "rows_per_s": round(n / dt, 1),
+                     "visible_pairs_per_s": round(rate, 1),
+                     "full_fwd_bwd_seconds_extrapolated": round(2.0 * full_pairs / rate, 1)}
+
+    hb = synth.host_bits
+    # config 1: everything, timed as a whole
+    inp = synth.batched_inputs(1, 1, 128, 128, 2, 2, 64, grads=True)
+    p = oracle.batched(inp["q"], inp["k"], inp["v"], synth.default_scale(64), dout=inp["dout"])
+    t0 = time.perf_counter()
+    oracle.full(p)
+    dt = time.perf_counter() - t0
+    res["config1"] = {"rows": 256, "seconds": round(dt, 4), "full_fwd_bwd_seconds": round(dt, 4)}
+    # config 3: batch entry 0 (its rows see 128 keys)
+    q, k, v, do, sinks = config3_inputs()
+    p = oracle.batched(hb(q[:1]), hb(k[:1]), hb(v[:1]), synth.default_scale(128), causal=True, window=(127, 0),
+                       dout=hb(do[:1]), sinks=sinks.cpu().numpy())
+    sample("config3", p, [0], 32, lambda s_: 8192, visible_pairs(2, 8192, 8192, 32, True, (127, 0)),
+           lambda s_, r_: min(r_ + 1, 128))
+    del q, k, v, do, sinks
+    # config 4: the packed batch
+    q, k, v, do, cu, L = config4_inputs()
+    cuh = cu.cpu().numpy()
+    p = oracle.varlen(hb(q), hb(k), hb(v), cuh, cuh, synth.default_scale(128), causal=True, dout=hb(do))
+    live = np.flatnonzero(L > 0)
+    sample("config4", p, live, 16, lambda s_: int(L[s_]), 16 * sum(int(x) * (int(x) + 1) // 2 for x in L),
+           lambda s_, r_: (r_ + 1) if L[s_] > 0 else 0)
+    del q, k, v, do, cu, live
+    torch.cuda.empty_cache()
+    # config 5: batch entry 0 of the decode shape
+    d = DECODE
+    q, k, v = synth.device_normal(5, [(d["B"], d["SQ"], d["HQ"], d["D"]), (d["B"], d["SK"], d["HKV"], d["D"]),
+                                      (d["B"], d["SK"], d["HKV"], d["D"])])
+    dout = synth.device_normal(55, [(1, d["SQ"], d["HQ"], d["D"])])[0]
+    p = oracle.batched(hb(q[:1]), hb(k[:1]), hb(v[:1]), synth.default_scale(128), causal=True, dout=hb(dout))
+    sample("config5", p, [0], d["HQ"], lambda s_: d["SQ"], visible_pairs(d["B"], d["SQ"], d["SK"], d["HQ"], True, (-1, -1)),
+           lambda s_, r_: d["SK"] - d["SQ"] + r_ + 1)
+    del q, k, v, dout
+    torch.cuda.empty_cache()
+    return res
 
 
 def read_power_clock():
@@ -543,10 +772,11 @@ def run_power(seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode-shape measurement")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the other workloads (configs 1, 3, 4 and the decode shape)")
     ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power", "configs"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
@@ -595,11 +825,12 @@ def main():
     if args.workload == "decode":
         if args.copy_calibration:
             copy_calibration()
-        dec = run_decode(args.steps, args.warmup)
-        dec["paged"] = run_kvcache(args.steps, args.warmup)
+        flush = Flusher()
+        dec = run_decode(args.steps, args.warmup, flush)
+        dec["paged"] = run_kvcache(args.steps, args.warmup, flush)
         print(json.dumps({"metric": "decode-shaped forward, K/V HBM GB/s, 1 MI355X", "value": dec["kv_GBps"],
                           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-                          "ms_per_step": dec["ms_per_call"], "higher_is_better": True, "scaling": "weak",
+                          "ms_per_step": dec["ms_per_call"]["median"], "higher_is_better": True, "scaling": "weak",
                           "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) rounded to bf16",
                           "config": {"workload": dec["workload"]}, "decode": dec}))
         return
@@ -607,26 +838,28 @@ def main():
     w = WORKLOAD
     B, S, HQ, HKV, D = w["B"], w["S"], w["HQ"], w["HKV"], w["D"]
     inp = synth.batched_inputs(2, B, S, S, HQ, HKV, D, grads=True)
-    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
     q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["dout"])
     torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration()
+    flush = Flusher()
+    last = {}
 
     def step():
         o, lse = ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"])
-        ea.attn_bwd(q, k, v, o, lse, do, causal=w["causal"], window=w["window"])
+        dq, dk, dv, _ = ea.attn_bwd(q, k, v, o, lse, do, causal=w["causal"], window=w["window"])
+        last.update(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Per-kernel breakdown, from a pass of its own with every launch bracketed
-    # by HIP events (the events cost ~5 % of a step, so the timed region below
-    # brackets only the dominant kernel).
+    # Per-kernel breakdown, from a pass of its own (MALL flushed before each
+    # step) with every launch bracketed by HIP events; the events inflate the
+    # kernels a little, so their sum is reported beside the same pass's step
+    # time.  The timed region below brackets only the dominant kernel.
     ea.attn_timing_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
+    bd_steps = summary(time_each(step, args.steps, flush))
     kern = {}
     for name in ea._lib.KERNELS:
         n, tot = ea.attn_timing_read(name)
@@ -635,22 +868,23 @@ def main():
     ea.attn_timing_enable(False)
     dom = max(kern, key=lambda n: kern[n][1])  # dominant kernel: most total time
 
-    # Timed region: K steps, the dominant kernel's launches timed live with
-    # HIP events on the library's stream (the step's own stream).
+    # Timed region: exactly K steps, the MALL flushed before each (outside the
+    # step's events), the dominant kernel's launches timed live with HIP events
+    # on the library's stream (the step's own stream).
     ea.attn_timing_enable(True, kernels=[dom])
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
+    cold = time_each(step, args.steps, flush)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / args.steps
     n_l, tot = ea.attn_timing_read(dom)
     ea.attn_timing_enable(False)
     avg_ms = tot / n_l
+    st = summary(cold)
+    ms = st["median"]
+    warm = summary(time_each(step, args.steps))
+    fwd_only = summary(time_each(lambda: ea.attn_fwd(q, k, v, causal=w["causal"], window=w["window"]),
+                                 args.steps, flush))
 
     pairs = visible_pairs(B, S, S, HQ, w["causal"], w["window"])
     fwd_flop, bwd_flop = 4.0 * D * pairs, 10.0 * D * pairs
@@ -661,17 +895,18 @@ def main():
     flop_of = {"fwd": fwd_flop, "bwd_dkdv": 8.0 * D * pairs, "bwd_dq": 6.0 * D * pairs}
     # compulsory HBM bytes per launch (each tensor read or written once)
     qt, kvt, rows = B * S * HQ * D * 2, B * S * HKV * D * 2, B * HQ * S
-    algo_bytes = {"fwd": 2 * qt + 2 * kvt + 4 * rows,              # Q K V in, O out, lse out
-                  "bwd_dq": 5 * qt + 2 * kvt + 12 * rows,          # Q O dO K V in, dQ and fp16 Q out; lse in, D lse' out
-                  "bwd_dkdv": 2 * qt + 4 * kvt + 8 * rows}         # Q dO K V in, dK dV out; D lse' in
-    roof = None
+    algo_bytes = {"fwd": 2 * qt + 2 * kvt + 4 * rows,              # Q K V in, O and lse out
+                  "bwd_dq": 4 * qt + 2 * kvt + 12 * rows,          # Q O dO K V, lse in; dQ, D, lse' out
+                  "bwd_dkdv": 2 * qt + 4 * kvt + 8 * rows}         # Q dO K V, D, lse' in; dK dV out
+    roof_ = None
     if dom in flop_of:
         ach = flop_of[dom] / (avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_profile(dom), "traffic_unit": "bytes per launch",
-                "algorithmic_bytes": algo_bytes[dom], "avg_launch_ms": round(avg_ms, 5)}
-
+        roof_ = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                 "traffic": traffic_from_profile(dom), "traffic_unit": "bytes per launch",
+                 "algorithmic_bytes": algo_bytes[dom], "avg_launch_ms": round(avg_ms, 5)}
+    kms = {n: round(t / args.steps, 5) for n, (c, t) in kern.items()}
+    fwd_tf = fwd_flop / (fwd_only["median"] * 1e-3) / 1e12
     out = {
         "metric": "attention fwd+bwd TFLOPS (and % of MFMA bf16 peak), 1 MI355X",
         "value": round(tflops, 2),
@@ -687,18 +922,26 @@ def main():
         "data": "synthetic: seeded i.i.d. N(0,1) q, k, v, dout rounded to bf16",
         "config": {"workload": w["name"], "batch": B, "seq_len": S, "heads_q": HQ, "heads_kv": HKV,
                    "head_dim": D, "causal": w["causal"], "parallelism": "single GPU"},
+        "timing": "per-step HIP events, MALL (512 MB) flushed before each step outside its events; value and "
+                  "ms_per_step use the median over the K timed steps",
+        "ms_per_step_stats": st,
+        "warm": {"what": "the same steps without the flush (K/V may hit the 256 MB MALL)", "ms_per_step": warm,
+                 "value": round((fwd_flop + bwd_flop) / (warm["median"] * 1e-3) / 1e12, 2)},
         "pct_mfma_peak": round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
-        # from the breakdown pass (every launch timed); the roofline's launch time is the timed region's
-        "kernels_ms_per_step": {n: round(t / args.steps, 5) for n, (c, t) in kern.items()},
-        "fwd_tflops": round(fwd_flop / (kern["fwd"][1] / kern["fwd"][0] * 1e-3) / 1e12, 2) if "fwd" in kern else None,
-        "roofline": roof,
+        "fwd": {"ms": fwd_only, "tflops": round(fwd_tf, 2), "frac_of_mfma_peak": round(fwd_tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels_ms_per_step": kms,
+        "kernels_breakdown": {"what": "a pass of its own with every launch bracketed by HIP events (they add a few "
+                                      "µs per launch); kernel means beside that pass's median step",
+                              "kernels_sum_ms": round(sum(kms.values()), 5), "step_ms": bd_steps},
+        "roofline": roof_,
         "wall_s": round(wall, 3),
     }
     if not args.no_decode:
-        out["decode"] = run_decode(max(3, args.steps // 4), 2)
-        out["decode"]["paged"] = run_kvcache(max(3, args.steps // 4), 2)
+        out["config_lines"] = run_config_lines(args.steps, 2, flush)
+        out["decode"] = run_decode(args.steps, 2, flush)
+        out["decode"]["paged"] = run_kvcache(args.steps, 2, flush)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, w)
+        out["cpu_baseline"] = cpu_baseline(inp, w, last)
     print(json.dumps(out))
 
 

@@ -79,3 +79,25 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_summary_statistics():
+    """median of an even count is the mean of the middle two; p90 is the
+    nearest-rank 90th percentile; min is the smallest."""
+    s = bench.summary([5.0, 1.0, 3.0, 2.0])
+    assert s["median"] == 2.5 and s["min"] == 1.0 and s["p90"] == 5.0 and s["n"] == 4
+    s = bench.summary([float(x) for x in range(1, 31)])  # 1..30
+    assert s["median"] == 15.5 and s["p90"] == 27.0 and s["min"] == 1.0
+    assert bench.summary([7.0])["p90"] == 7.0
+
+
+def test_roofline_fields():
+    """attainable time is the larger of the MFMA-bound and HBM-bound times."""
+    st = {"median": 0.1, "min": 0.1, "p90": 0.1, "n": 1}
+    r = bench.roof(2.5e11, 8e8, st)          # 0.1 ms at 2.5 PF; 8e8 B at 8 TB/s = 0.1 ms
+    assert abs(r["frac_of_mfma_peak"] - 1.0) < 1e-9 and abs(r["frac_of_attainable"] - 1.0) < 1e-9
+    r = bench.roof(2.5e10, 1.6e9, st)        # HBM-bound: 0.2 ms attainable against 0.1 measured
+    assert r["bound"] == "hbm" and abs(r["attainable_ms"] - 0.2) < 1e-12
+    # compulsory bytes: forward Q K V in, O and lse out; backward Q K V O dO lse in, dQ dK dV out
+    assert bench.compulsory_bytes(10, 3, 2, False) == 2 * 10 + 2 * 3 + 8
+    assert bench.compulsory_bytes(10, 3, 2, True) == 4 * 10 + 4 * 3 + 8
