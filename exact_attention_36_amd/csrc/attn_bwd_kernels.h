@@ -378,7 +378,10 @@ void bwd_dq_kernel(const BwdArgs a) {
 // inside fp16's range, |x| <= 65504).  dO and the row statistics reach LDS by
 // DMA, double buffered; bf16 Q is loaded into registers one step ahead,
 // converted and written to LDS by the waves (fp16 Q goes by DMA as it is).
-template <int D, bool F16, bool PAD, int EXT>
+// WSKIP (windows with a left bound): each wave skips the compute of the query
+// blocks that see none of its keys; the plain instance has no such branch in
+// its loop (it measured a few per cent slower on causal-only problems).
+template <int D, bool F16, bool PAD, int EXT, bool WSKIP>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
@@ -575,6 +578,22 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     __syncthreads();
   }
   const float keyf = (float)my_key;
+  // Query blocks that see any of this wave's 32 keys: [ws_lo, ws_hi] (the
+  // inverse band's bounds are nondecreasing in the key).  On the other steps
+  // the wave only takes part in the loads and barriers.
+  int ws_lo = 0, ws_hi = 1 << 30;
+  if constexpr (WSKIP) {
+    ws_lo = 1;
+    ws_hi = 0;
+    const int kw0 = j0 + 32 * wave, kw1 = min(kw0 + 31, si.lk - 1);
+    if (kw0 < si.lk && prows > 0) {
+      const int qlo = qband.qmin(kw0), qhi = qband.qmax(kw1);
+      if (qhi >= qlo) {
+        ws_lo = (qlo * G) / BM;
+        ws_hi = ((qhi + 1) * G - 1) / BM;
+      }
+    }
+  }
   // The query blocks are visited last to first: under a causal mask every key
   // block of a sequence sees its last query block, so the workgroups of one
   // sequence (dispatched together, on one XCD) start at the same Q / dO tiles
@@ -599,116 +618,118 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const char* dot = do_lds + buf * QTILE;
     const float* stt = st_lds + buf * 64;
 
-    // S and dP, [32 queries x 32 keys]: lane = key column, registers = query rows
-    f32x16 s_acc, dp;
+    if (!WSKIP || (pb >= ws_lo && pb <= ws_hi)) {
+      // S and dP, [32 queries x 32 keys]: lane = key column, registers = query rows
+      f32x16 s_acc, dp;
 #pragma unroll
-    for (int s = 0; s < KS; s++) {
-      s_acc = mfma32<true>(lds_read16(qt + q_off[s]), kf[s], s == 0 ? f32x16{} : s_acc);
-      dp = mfma32<F16>(lds_read16(dot + q_off[s]), lds_read16(vrow + q_off[s]), s == 0 ? f32x16{} : dp);
-    }
-    const int p0 = pb * BM;
-    const int qi_lo = div_group(p0, a.s), qi_hi = div_group(min(p0 + BM, prows) - 1, a.s);
-    const bool interior = (p0 + BM <= prows) && j0 + wave * 32 >= band.kmin(qi_hi) &&
-                          j0 + wave * 32 + 31 <= band.kmax(qi_lo);
-    // P and dS from the row statistics of this lane's 16 rows (rows
-    // 8a + 4hh + 0..3); only steps that straddle the band, the last query
-    // rows or the last keys mask
-    if constexpr ((EXT & EXT_CAP) == 0) {
-      if constexpr (EXT != 0) {
-        // ALiBi alone: the variant logit in place of the raw score, with the
-        // rows' terms from LDS, before the mask
+      for (int s = 0; s < KS; s++) {
+        s_acc = mfma32<true>(lds_read16(qt + q_off[s]), kf[s], s == 0 ? f32x16{} : s_acc);
+        dp = mfma32<F16>(lds_read16(dot + q_off[s]), lds_read16(vrow + q_off[s]), s == 0 ? f32x16{} : dp);
+      }
+      const int p0 = pb * BM;
+      const int qi_lo = div_group(p0, a.s), qi_hi = div_group(min(p0 + BM, prows) - 1, a.s);
+      const bool interior = (p0 + BM <= prows) && j0 + wave * 32 >= band.kmin(qi_hi) &&
+                            j0 + wave * 32 + 31 <= band.kmax(qi_lo);
+      // P and dS from the row statistics of this lane's 16 rows (rows
+      // 8a + 4hh + 0..3); only steps that straddle the band, the last query
+      // rows or the last keys mask
+      if constexpr ((EXT & EXT_CAP) == 0) {
+        if constexpr (EXT != 0) {
+          // ALiBi alone: the variant logit in place of the raw score, with the
+          // rows' terms from LDS, before the mask
+          const float* ext = ext_lds + buf * 64;
+#pragma unroll
+          for (int a4 = 0; a4 < 4; a4++) {
+            const f32x4 dg4 = *(const f32x4*)(ext + 8 * a4 + 4 * hh);
+            const f32x4 kb4 = *(const f32x4*)(ext + 32 + 8 * a4 + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              float th;
+              s_acc[4 * a4 + e] = ext_score<EXT>(s_acc[4 * a4 + e], a.x, kb4[e], dg4[e] - keyf, th);
+            }
+          }
+        }
+        if (!interior) {
+          // scores of invisible (row, key) pairs -> -inf, so that P = 0 there
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if ((uint32_t)(pr - pr_lo) > pr_span) s_acc[i] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int a4 = 0; a4 < 4; a4++) {
+          const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
+          const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const int i = 4 * a4 + e;
+            const float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
+            s_acc[i] = p;
+            dp[i] = p * (dp[i] - dl[e]);  // dS
+          }
+        }
+      } else {
+        // soft cap (and ALiBi, rows' terms from LDS): variant logits, P, and dS
+        // with 1 - tanh^2 in one pass; invisible pairs are zeroed after
         const float* ext = ext_lds + buf * 64;
 #pragma unroll
         for (int a4 = 0; a4 < 4; a4++) {
-          const f32x4 dg4 = *(const f32x4*)(ext + 8 * a4 + 4 * hh);
-          const f32x4 kb4 = *(const f32x4*)(ext + 32 + 8 * a4 + 4 * hh);
+          const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
+          const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
+          f32x4 dg4{}, kb4{};
+          if constexpr (ALIBI) {
+            dg4 = *(const f32x4*)(ext + 8 * a4 + 4 * hh);
+            kb4 = *(const f32x4*)(ext + 32 + 8 * a4 + 4 * hh);
+          }
 #pragma unroll
           for (int e = 0; e < 4; e++) {
-            float th;
-            s_acc[4 * a4 + e] = ext_score<EXT>(s_acc[4 * a4 + e], a.x, kb4[e], dg4[e] - keyf, th);
+            const int i = 4 * a4 + e;
+            float th = 0.f;
+            const float x = ext_score<EXT>(s_acc[i], a.x, kb4[e], dg4[e] - keyf, th);
+            const float p = exp2_fast(fmaf(x, c, -l2[e]));
+            float ds = p * (dp[i] - dl[e]);
+            if constexpr ((EXT & EXT_CAP) != 0) ds *= fmaf(-th, th, 1.f);
+            s_acc[i] = p;
+            dp[i] = ds;
+          }
+        }
+        if (!interior) {
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if ((uint32_t)(pr - pr_lo) > pr_span) {
+              s_acc[i] = 0.f;
+              dp[i] = 0.f;
+            }
           }
         }
       }
-      if (!interior) {
-        // scores of invisible (row, key) pairs -> -inf, so that P = 0 there
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if ((uint32_t)(pr - pr_lo) > pr_span) s_acc[i] = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int a4 = 0; a4 < 4; a4++) {
-        const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
-        const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int i = 4 * a4 + e;
-          const float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
-          s_acc[i] = p;
-          dp[i] = p * (dp[i] - dl[e]);  // dS
-        }
-      }
-    } else {
-      // soft cap (and ALiBi, rows' terms from LDS): variant logits, P, and dS
-      // with 1 - tanh^2 in one pass; invisible pairs are zeroed after
-      const float* ext = ext_lds + buf * 64;
-#pragma unroll
-      for (int a4 = 0; a4 < 4; a4++) {
-        const f32x4 l2 = *(const f32x4*)(stt + 8 * a4 + 4 * hh);
-        const f32x4 dl = *(const f32x4*)(stt + 32 + 8 * a4 + 4 * hh);
-        f32x4 dg4{}, kb4{};
-        if constexpr (ALIBI) {
-          dg4 = *(const f32x4*)(ext + 8 * a4 + 4 * hh);
-          kb4 = *(const f32x4*)(ext + 32 + 8 * a4 + 4 * hh);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int i = 4 * a4 + e;
-          float th = 0.f;
-          const float x = ext_score<EXT>(s_acc[i], a.x, kb4[e], dg4[e] - keyf, th);
-          const float p = exp2_fast(fmaf(x, c, -l2[e]));
-          float ds = p * (dp[i] - dl[e]);
-          if constexpr ((EXT & EXT_CAP) != 0) ds *= fmaf(-th, th, 1.f);
-          s_acc[i] = p;
-          dp[i] = ds;
-        }
-      }
-      if (!interior) {
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int pr = p0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if ((uint32_t)(pr - pr_lo) > pr_span) {
-            s_acc[i] = 0.f;
-            dp[i] = 0.f;
-          }
-        }
-      }
-    }
-    // P^T / dS^T as B operands: k-step u covers queries 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}
-    u32x4 pf[2], sf[2];
-#pragma unroll
-    for (int u = 0; u < 2; u++) {
-      pf[u] = u32x4{pack2<F16>(s_acc[8 * u + 0], s_acc[8 * u + 1]), pack2<F16>(s_acc[8 * u + 2], s_acc[8 * u + 3]),
-                    pack2<F16>(s_acc[8 * u + 4], s_acc[8 * u + 5]), pack2<F16>(s_acc[8 * u + 6], s_acc[8 * u + 7])};
-      sf[u] = u32x4{pack2<true>(dp[8 * u + 0], dp[8 * u + 1]), pack2<true>(dp[8 * u + 2], dp[8 * u + 3]),
-                    pack2<true>(dp[8 * u + 4], dp[8 * u + 5]), pack2<true>(dp[8 * u + 6], dp[8 * u + 7])};
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS   (M = dims, N = this wave's keys, K = queries)
-#pragma unroll
-    for (int d = 0; d < DB; d++)
+      // P^T / dS^T as B operands: k-step u covers queries 16u + {4hh..4hh+3, 8+4hh..8+4hh+3}
+      u32x4 pf[2], sf[2];
 #pragma unroll
       for (int u = 0; u < 2; u++) {
-        const int rb = u * 16 * ROWB;
-        const u32x2 o1 = lds_read_tr(dot + rb + t_off[d][0]), o2 = lds_read_tr(dot + rb + t_off[d][1]);
-        dv[d] = mfma32<F16>(u32x4{o1[0], o1[1], o2[0], o2[1]}, pf[u], dv[d]);
-        const u32x2 q1 = lds_read_tr(qt + rb + t_off[d][0]), q2 = lds_read_tr(qt + rb + t_off[d][1]);
-        dk[d] = mfma32<true>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
+        pf[u] = u32x4{pack2<F16>(s_acc[8 * u + 0], s_acc[8 * u + 1]), pack2<F16>(s_acc[8 * u + 2], s_acc[8 * u + 3]),
+                      pack2<F16>(s_acc[8 * u + 4], s_acc[8 * u + 5]), pack2<F16>(s_acc[8 * u + 6], s_acc[8 * u + 7])};
+        sf[u] = u32x4{pack2<true>(dp[8 * u + 0], dp[8 * u + 1]), pack2<true>(dp[8 * u + 2], dp[8 * u + 3]),
+                      pack2<true>(dp[8 * u + 4], dp[8 * u + 5]), pack2<true>(dp[8 * u + 6], dp[8 * u + 7])};
       }
-    // S/dP: 3 reads (Q, dO, V) feed 2 MFMAs per step, 2 steps ahead;
-    // dV/dK: 4 transposing reads feed 2 MFMAs per step, 2 steps ahead
-    sched_reads_ahead<KS, 2, 3, 2>();
-    sched_reads_ahead<2 * DB, 2, 4, 2>();
+      // dV^T += dO^T P,  dK^T += Q^T dS   (M = dims, N = this wave's keys, K = queries)
+#pragma unroll
+      for (int d = 0; d < DB; d++)
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+          const int rb = u * 16 * ROWB;
+          const u32x2 o1 = lds_read_tr(dot + rb + t_off[d][0]), o2 = lds_read_tr(dot + rb + t_off[d][1]);
+          dv[d] = mfma32<F16>(u32x4{o1[0], o1[1], o2[0], o2[1]}, pf[u], dv[d]);
+          const u32x2 q1 = lds_read_tr(qt + rb + t_off[d][0]), q2 = lds_read_tr(qt + rb + t_off[d][1]);
+          dk[d] = mfma32<true>(u32x4{q1[0], q1[1], q2[0], q2[1]}, sf[u], dk[d]);
+        }
+      // S/dP: 3 reads (Q, dO, V) feed 2 MFMAs per step, 2 steps ahead;
+      // dV/dK: 4 transposing reads feed 2 MFMAs per step, 2 steps ahead
+      sched_reads_ahead<KS, 2, 3, 2>();
+      sched_reads_ahead<2 * DB, 2, 4, 2>();
+    }  // this wave's step
     if constexpr (!F16) {
       // the next step's Q into the other buffer, which every wave left before
       // this step's barrier
@@ -760,10 +781,12 @@ hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st) {
   }
   if (a.total_ctas > 0) {
     timing_begin(K_BWD_DKDV, st);
-    if (!pad)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false, EXT>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    if (pad)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, true, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    else if (a.s.wl >= 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false, EXT, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, true, EXT>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
     timing_end(K_BWD_DKDV, st);
   }
   return hipGetLastError();
