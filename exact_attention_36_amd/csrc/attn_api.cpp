@@ -156,10 +156,13 @@ int64_t dq_blocks(const attn_params* p, bool packed, int64_t nseq, int64_t sq, i
 }
 
 // Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like
-// lse; with sinks, each dQ workgroup's sums of the sink gradient per q head of
-// its group ([Hkv][blocks][G]), which a last kernel adds up in a fixed order.
+// lse; each dQ workgroup's largest row norm of dO and largest |D_i|
+// ([Hkv][blocks][2]), from which the dK/dV kernel scales dS into fp16's
+// range; with sinks, each dQ workgroup's sums of the sink gradient per q head
+// of its group ([Hkv][blocks][G]), which a last kernel adds up in a fixed
+// order.
 struct BwdWs {
-  size_t delta, lse2, dsink_part, total;
+  size_t delta, lse2, dscale_part, dsink_part, total;
 };
 BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) {
   (void)grad_dtype;
@@ -167,8 +170,9 @@ BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) 
   const int64_t rows = tq * p->heads_q;
   w.delta = align_up(rows * 4);
   w.lse2 = align_up(rows * 4);
+  w.dscale_part = align_up(nbq * p->heads_kv * 2 * 4);
   w.dsink_part = p->sinks ? align_up(nbq * p->heads_q * 4) : 0;  // Hkv * nbq * G = nbq * Hq
-  w.total = w.delta + w.lse2 + w.dsink_part;
+  w.total = w.delta + w.lse2 + w.dscale_part + w.dsink_part;
   return w;
 }
 
@@ -276,6 +280,8 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   wp += w.delta;
   a.lse2 = (float*)wp;
   wp += w.lse2;
+  a.dscale_part = (float*)wp;
+  wp += w.dscale_part;
   a.dsink_part = w.dsink_part ? (float*)wp : nullptr;
   a.nbq = (int32_t)nbq;
   const float scale = resolve_scale(p);

@@ -87,8 +87,10 @@ void bwd_dq_kernel(const BwdArgs a) {
   const SeqInfo si = seq_info(a.s, seq);
   const int prows = si.lq * G;
   const int p0 = mb * BM;
+  float* const dscale_out = a.dscale_part + ((int64_t)g * a.nbq + blk) * 2;
   if (p0 >= prows) {  // idle slot of the packed grid (whole workgroup)
     if (dsink_out && (int)threadIdx.x < G) dsink_out[threadIdx.x] = 0.f;
+    if (threadIdx.x < 2) dscale_out[threadIdx.x] = 0.f;
     return;
   }
 
@@ -139,20 +141,43 @@ void bwd_dq_kernel(const BwdArgs a) {
   //   lse' = log2(2^lse + 2^sink) in log2 units (+inf for an empty row, so
   //   that P = 0 there);  dsink = -sum_rows (1 - gate) D, gate = sigmoid(lse - sink)
   //   (dew-flash-attn page, sinks paragraph).
-  float row_d;
+  float row_d, row_dn;  // D_i and |dO_i|_2
   {
     const auto ro = make_rsrc((const uint16_t*)a.o + qbase_e, qbytes);
-    float part = 0.f;
+    float part = 0.f, sq = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; s++) {
       const u32x4 ov = buf_load16(ro, chunk_off(qoff, 2 * s + hh, dg));
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), part);
-        part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), to_f32<F16>((uint16_t)(df[s][e] >> 16)), part);
+        const float d0 = to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), d1 = to_f32<F16>((uint16_t)(df[s][e] >> 16));
+        part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), d0, part);
+        part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), d1, part);
+        sq = fmaf(d0, d0, fmaf(d1, d1, sq));
       }
     }
     row_d = half_sum(part);  // the two lanes holding one row's halves
+    row_dn = my_p < prows ? __builtin_sqrtf(half_sum(sq)) : 0.f;
+  }
+  // The workgroup's largest |dO_i|_2 and |D_i| (every row of one sequence and
+  // kv head), for the dK/dV kernel's bound on |dS|.
+  {
+    float m0 = row_dn, m1 = my_p < prows ? fabsf(row_d) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      m0 = fmaxf(m0, __shfl_xor(m0, o));
+      m1 = fmaxf(m1, __shfl_xor(m1, o));
+    }
+    __shared__ float nrm[2][4];
+    if (lane == 0) {
+      nrm[0][wave] = m0;
+      nrm[1][wave] = m1;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const float* r = nrm[threadIdx.x];
+      dscale_out[threadIdx.x] = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
+    }
   }
   float row_lse2 = INFINITY, dsink_part = 0.f;
   if (my_p < prows) {
@@ -378,9 +403,10 @@ void bwd_dq_kernel(const BwdArgs a) {
 // inside fp16's range, |x| <= 65504).  dO and the row statistics reach LDS by
 // DMA, double buffered; bf16 Q is loaded into registers one step ahead,
 // converted and written to LDS by the waves (fp16 Q goes by DMA as it is).
-// WSKIP (windows with a left bound): each wave skips the compute of the query
-// blocks that see none of its keys; the plain instance has no such branch in
-// its loop (it measured a few per cent slower on causal-only problems).
+// WSKIP (windows with a left bound; bf16 up to 128 wide): each wave skips the
+// compute of the query blocks that see none of its keys; the plain instance
+// has no such branch in its loop (it measured a few per cent slower on
+// causal-only problems).
 template <int D, bool F16, bool PAD, int EXT, bool WSKIP>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void bwd_dkdv_kernel(const BwdArgs a) {
@@ -478,6 +504,50 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       kf[s] = F16 ? k : bf16x8_to_f16x8(k);
     }
   }
+  // dS reaches dK through fp16 (11 significant bits, normal from 2^-14, at
+  // most 65504).  For every row i that sees this key j,
+  //   |dS_ij| = P_ij |<dO_i, v_j> - D_i| <= max_i |dO_i|_2 |v_j|_2 + max_i |D_i|
+  // (P <= 1, Cauchy-Schwarz; the maxima over the sequence's rows come from
+  // the dQ kernel's workgroups), so dS * 2^ds_e with 2^ds_e bringing that
+  // bound to 2^14 stays in fp16's normal range whatever the scale of dO and
+  // V; the epilogue divides the factor out of dK.
+  int ds_e = 0;
+  {
+    int b0, b1;  // this sequence's dQ workgroups
+    if (a.s.cu_q) {
+      b0 = packed_block_start(a.s.cu_q, seq, G, BWD_QBM);
+      b1 = packed_block_start(a.s.cu_q, seq + 1, G, BWD_QBM);
+    } else {
+      b0 = seq * a.nmb;
+      b1 = b0 + a.nmb;
+    }
+    float mdo = 0.f, md = 0.f;
+    for (int b = b0 + lane; b < b1; b += 64) {
+      const float* sl = a.dscale_part + ((int64_t)g * a.nbq + b) * 2;
+      mdo = fmaxf(mdo, sl[0]);
+      md = fmaxf(md, sl[1]);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      mdo = fmaxf(mdo, __shfl_xor(mdo, o));
+      md = fmaxf(md, __shfl_xor(md, o));
+    }
+    const auto rv = make_rsrc((const uint16_t*)a.v + kbase_e, kbytes);
+    const uint32_t vo = (uint32_t)((int64_t)my_key * krow * 2);
+    float sq = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+      const u32x4 vv = buf_load16(rv, chunk_off(vo, 2 * s + hh, dg));
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float v0 = to_f32<F16>((uint16_t)(vv[e] & 0xFFFF)), v1 = to_f32<F16>((uint16_t)(vv[e] >> 16));
+        sq = fmaf(v0, v0, fmaf(v1, v1, sq));
+      }
+    }
+    const float bound = fmaf(mdo, __builtin_sqrtf(half_sum(sq)), md);
+    if (bound > 0.f && bound < INFINITY) ds_e = min(max(14 - __builtin_amdgcn_frexp_expf(bound), -100), 100);
+  }
+  const float ds_sc = __builtin_amdgcn_ldexpf(1.f, ds_e);
 
   // Q and dO tiles of one block of BM packed rows -> LDS, and the rows' lse'
   // and D; rows past the sequence read as 0 (and are masked).  Each wave
@@ -666,7 +736,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
             const int i = 4 * a4 + e;
             const float p = exp2_fast(fmaf(s_acc[i], c, -l2[e]));
             s_acc[i] = p;
-            dp[i] = p * (dp[i] - dl[e]);  // dS
+            dp[i] = (p * ds_sc) * (dp[i] - dl[e]);  // dS * 2^ds_e
           }
         }
       } else {
@@ -688,7 +758,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
             float th = 0.f;
             const float x = ext_score<EXT>(s_acc[i], a.x, kb4[e], dg4[e] - keyf, th);
             const float p = exp2_fast(fmaf(x, c, -l2[e]));
-            float ds = p * (dp[i] - dl[e]);
+            float ds = (p * ds_sc) * (dp[i] - dl[e]);  // dS * 2^ds_e
             if constexpr ((EXT & EXT_CAP) != 0) ds *= fmaf(-th, th, 1.f);
             s_acc[i] = p;
             dp[i] = ds;
@@ -749,18 +819,20 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       const int kk = j0 + wave * 32 + r;
       return kk < si.lk_slot ? (uint32_t)((int64_t)kk * krow * 2) : DROP_ROW;
     };
-    store_rows16<D, F16>(dk, a.scale, stg, make_rsrc((uint16_t*)a.dk + kbase_e, kbytes_slot), row_off, dg);
+    store_rows16<D, F16>(dk, a.scale * __builtin_amdgcn_ldexpf(1.f, -ds_e), stg,
+                         make_rsrc((uint16_t*)a.dk + kbase_e, kbytes_slot), row_off, dg);
     store_rows16<D, F16>(dv, 1.f, stg + 32 * ROWB, make_rsrc((uint16_t*)a.dv + kbase_e, kbytes_slot), row_off, dg);
   } else if (my_key < si.lk_slot) {
     const int64_t ob = ((int64_t)(si.k0 + my_key) * a.s.hkv + g) * dg;
+    const float ksc = a.scale * __builtin_amdgcn_ldexpf(1.f, -ds_e);
 #pragma unroll
     for (int d = 0; d < DB; d++)
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const int dd = d * 32 + 8 * j4 + 4 * hh;
         if (dd >= dg) continue;  // zero tile columns past the head dim
-        *(f32x4*)((float*)a.dk + ob + dd) = f32x4{dk[d][4 * j4] * a.scale, dk[d][4 * j4 + 1] * a.scale,
-                                                  dk[d][4 * j4 + 2] * a.scale, dk[d][4 * j4 + 3] * a.scale};
+        *(f32x4*)((float*)a.dk + ob + dd) = f32x4{dk[d][4 * j4] * ksc, dk[d][4 * j4 + 1] * ksc,
+                                                  dk[d][4 * j4 + 2] * ksc, dk[d][4 * j4 + 3] * ksc};
         *(f32x4*)((float*)a.dv + ob + dd) = f32x4{dv[d][4 * j4], dv[d][4 * j4 + 1], dv[d][4 * j4 + 2], dv[d][4 * j4 + 3]};
       }
   }
@@ -771,6 +843,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 template <int EXT, int D, bool F16>
 hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st) {
   const bool pad = a.s.dg != D;
+  // the skipping instance only where it fits in registers without spills
+  constexpr bool WSKIP_OK = D <= 128 && !F16;
   if (a.total_ctas_q > 0) {
     timing_begin(K_BWD_DQ, st);
     if (!pad)
@@ -783,8 +857,8 @@ hipError_t launch_bwd_dt(const BwdArgs& a, hipStream_t st) {
     timing_begin(K_BWD_DKDV, st);
     if (pad)
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, true, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-    else if (a.s.wl >= 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false, EXT, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    else if (WSKIP_OK && a.s.wl >= 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false, EXT, WSKIP_OK>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, F16, false, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
     timing_end(K_BWD_DKDV, st);

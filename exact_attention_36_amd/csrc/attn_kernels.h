@@ -88,6 +88,7 @@ struct BwdArgs {
   float* dsinks;          // gradient, laid out like sinks, or nullptr
   int32_t dsink_count;    // floats in dsinks
   float* dsink_part;      // [hkv][nbq][G]: each dQ workgroup's per-head sums (workspace)
+  float* dscale_part;     // [hkv][nbq][2]: each dQ workgroup's max |dO_i|_2 and max |D_i| (workspace)
   int32_t nbq;            // dQ workgroups per kv head (batched: nseq * nmb; packed: nblk_q)
   float* delta;           // fp32, laid out like lse: D_i = <dO_i, O_i>
   float* lse2;            // fp32, laid out like lse: log-sum-exp with the sink, in log2 units

@@ -151,6 +151,13 @@ size_t attn_fwd_workspace_size(const attn_params *params, int64_t batch, int64_t
  * non-NULL; heads that share a row of sinks add into it).
  * dK/dV of a kv head sum over the q heads that share it (fa4-jax page,
  * restrictions paragraph: fp32 accumulation across the q heads).
+ * Numeric range: products accumulate in fp32.  The dK/dV pass holds Q, K and
+ * dS in fp16 for bf16 inputs too (10 fraction bits, which dK's long sums
+ * need): bf16 values of q and k are exact there up to |x| <= 65504 (beyond,
+ * the results are not finite) and keep fewer bits below 6.1e-5 (fp16
+ * subnormals); dS is scaled per key by a power of two chosen from
+ * max |dO_i|_2 |v_j|_2 + max |D_i| and divided out again, so the magnitudes of
+ * dout and v do not limit it.  dS for dQ is in the input dtype.
  */
 attn_status attn_bwd(const attn_params *params, int64_t batch, int64_t seqlen_q, int64_t seqlen_k,
                      const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -171,7 +178,8 @@ size_t attn_bwd_workspace_size(const attn_params *params, int64_t batch, int64_t
  * needing more than ATTN_NOALLOC_SCRATCH_BYTES of workspace (what
  * attn_bwd_workspace_size returns: 8 bytes per query row and q head, plus
  * 4 bytes per q head and 128-row query block with sinks) returns ATTN_ENOTSUP
- * before anything is launched.  Nothing in the scratch needs clearing
+ * before anything is launched (8 bytes per 128 packed query rows per kv head
+ * are added for the dS scaling statistics).  Nothing in the scratch needs clearing
  * between calls (every byte a call reads, that call's kernels wrote first),
  * but all calls on one GPU share it: calls that can overlap on one GPU (two
  * streams, two threads) race and must be ordered by the caller.

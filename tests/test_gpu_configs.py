@@ -82,21 +82,31 @@ def _check_cols(name, p, dk, dv, s, g, cols, k0):
     assert_close(name + ".dv[cols]", dv[k0 + cols, g], rdv, "f32")
 
 
-def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bwd, n_rows, col_slices,
-                  n_cols, softcap=0.0, alibi=None, sink_table=None, dsink_rows=True):
-    """sinks: one per head; sink_table: [hq, n] sinks instead; softcap, alibi
-    ([hq] slopes): the score variants; dsink_rows: check d(sink) against the
-    oracle over every row (slow for long causal rows with no window)."""
+def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bwd, n_rows, full_slices,
+                  n_cols, softcap=0.0, alibi=None, sink_table=None, dsink_rows=True, host_inputs=False):
+    """full_slices: (batch, kv group) pairs whose every query row (all G q
+    heads: O, LSE, dQ) and, with bwd, every key (dK, dV) are compared; sinks:
+    one per head; sink_table: [hq, n] sinks instead; softcap, alibi ([hq]
+    slopes): the score variants; dsink_rows: check d(sink) against the oracle
+    over every row (slow for long causal rows with no window); host_inputs:
+    draw the inputs on the host with numpy (seed = the workload's), exactly as
+    the benchmark does, instead of on the device."""
     print("case", name, flush=True)
-    shapes = [(B, S_q, hq, d), (B, S_k, hkv, d), (B, S_k, hkv, d)] + ([(B, S_q, hq, d)] if bwd else [])
-    tens = synth.device_normal(seed, shapes)
-    q, k, v = tens[:3]
     if sink_table is not None:
         sinks = True
-    inp = dict(q=synth.host_bits(q), k=synth.host_bits(k), v=synth.host_bits(v),
-               dout=synth.host_bits(tens[3]) if bwd else None,
-               sinks=(sink_table if sink_table is not None else
-                      np.random.default_rng(seed).standard_normal(hq, dtype=np.float32)) if sinks else None)
+    if host_inputs:
+        inp = synth.batched_inputs(seed, B, S_q, S_k, hq, hkv, d, grads=bwd, sinks=sinks and sink_table is None)
+        if sink_table is not None:
+            inp["sinks"] = sink_table
+        tens = [dev_tensor(inp[n]) for n in (("q", "k", "v", "dout") if bwd else ("q", "k", "v"))]
+    else:
+        shapes = [(B, S_q, hq, d), (B, S_k, hkv, d), (B, S_k, hkv, d)] + ([(B, S_q, hq, d)] if bwd else [])
+        tens = synth.device_normal(seed, shapes)
+        inp = dict(q=synth.host_bits(tens[0]), k=synth.host_bits(tens[1]), v=synth.host_bits(tens[2]),
+                   dout=synth.host_bits(tens[3]) if bwd else None,
+                   sinks=(sink_table if sink_table is not None else
+                          np.random.default_rng(seed).standard_normal(hq, dtype=np.float32)) if sinks else None)
+    q, k, v = tens[:3]
     scale = synth.default_scale(d)
     s_dev = torch.from_numpy(inp["sinks"]).cuda() if sinks else None
     kw = dict(causal=causal, window=window, sinks=s_dev, softcap=softcap,
@@ -128,6 +138,11 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
                 seqs = np.r_[seqs, s_]
                 heads = np.r_[heads, h_]
                 rows = np.r_[rows, r_]
+    # full slices: every row of the group's G heads in that batch entry
+    G = hq // hkv
+    for (s_, g_) in full_slices:
+        hh_, rr_ = (a.ravel() for a in np.meshgrid(np.arange(g_ * G, (g_ + 1) * G), np.arange(S_q), indexing="ij"))
+        seqs, heads, rows = np.r_[seqs, np.full(len(rr_), s_)], np.r_[heads, hh_], np.r_[rows, rr_]
     tok = seqs * S_q + rows
     dqh = host(grads[0]).reshape(Tq, hq, d) if bwd else None
     _check_rows(name, p, oh, lh, dqh, seqs, heads, rows, tok)
@@ -135,7 +150,7 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
         return
     dkh = host(grads[1]).reshape(Tk, hkv, d)
     dvh = host(grads[2]).reshape(Tk, hkv, d)
-    for (s_, g_) in col_slices:
+    for (s_, g_) in full_slices:
         _check_cols(name + "[slice %d,%d]" % (s_, g_), p, dkh, dvh, s_, g_, np.arange(S_k), s_ * S_k)
     s_ = int(rng.integers(0, B))
     g_ = int(rng.integers(0, hkv))
@@ -167,12 +182,14 @@ def _batched_case(name, seed, B, S_q, S_k, hq, hkv, d, causal, window, sinks, bw
 
 
 def test_config2_causal_prefill():
+    """On the benchmark's own inputs (numpy seed 2, drawn on the host): 1024
+    sampled rows, 4 full (batch, head) slices, 256 sampled keys."""
     _batched_case("cfg2", 2, 4, 2048, 2048, 16, 16, 128, True, (-1, -1), False, True, 1024,
-                  [(0, 0), (3, 15)], 256)
+                  [(0, 0), (1, 5), (2, 10), (3, 15)], 256, host_inputs=True)
 
 
 def test_config3_gqa_window_sinks():
-    _batched_case("cfg3", 3, 2, 8192, 8192, 32, 8, 128, True, (127, 0), True, True, 1024, [(1, 7)], 256)
+    _batched_case("cfg3", 3, 2, 8192, 8192, 32, 8, 128, True, (127, 0), True, True, 1024, [(0, 0), (1, 7)], 256)
 
 
 def test_headdim256_causal_prefill():
@@ -193,7 +210,9 @@ def test_variants_causal_prefill():
 
 
 def test_config5_decode_split_kv():
-    _batched_case("cfg5", 5, 32, 16, 32768, 64, 8, 128, True, (-1, -1), False, False, 256, [], 0)
+    """256 sampled rows and 2 full (batch, kv group) slices: every query row of
+    the group's 8 q heads against all 32768 keys."""
+    _batched_case("cfg5", 5, 32, 16, 32768, 64, 8, 128, True, (-1, -1), False, False, 256, [(0, 0), (31, 7)], 0)
 
 
 def test_config4_packed_varlen():

@@ -38,6 +38,10 @@ BATCHED = [
 ]
 
 
+# the small forward workload is drawn with its workload number as the seed
+SEEDS = {"cfg1_fwd": 1}
+
+
 def _torch_dtype(dt):
     return torch.bfloat16 if dt == "bf16" else torch.float16
 
@@ -46,7 +50,7 @@ def _torch_dtype(dt):
 def test_batched_matches_oracle(case):
     name, B, sq, sk, hq, hkv, d, causal, window, sinks, dt, bwd = case
     print("case", name, flush=True)
-    seed = zlib.crc32(name.encode()) % 1000
+    seed = SEEDS.get(name, zlib.crc32(name.encode()) % 1000)
     inp = synth.batched_inputs(seed, B, sq, sk, hq, hkv, d, grads=True, sinks=sinks, dtype=dt)
     scale = scale_of(d)
     ref = oracle.full(oracle_batched(inp, causal, window, scale, dt), grads=bwd)
@@ -149,3 +153,39 @@ def test_varlen_equals_batched_calls():
         torch.cuda.synchronize()
         assert torch.equal(o[a:b], ob[0]), s
         assert torch.equal(lse[:, a:b], lb[0]), s
+
+
+RANGE = [
+    # id, multipliers of q, k, v, dout (mq * mk = 1 keeps every score, hence P, unchanged)
+    ("q_x1e3_k_x1e-3", 1e3, 1e-3, 1.0, 1.0),
+    ("q_x1e-4_k_x1e4", 1e-4, 1e4, 1.0, 1.0),
+    ("dout_x1e3", 1.0, 1.0, 1.0, 1e3),
+    ("v_x1e-4_dout_x1e-2", 1.0, 1.0, 1e-4, 1e-2),
+]
+
+
+@pytest.mark.parametrize("case", RANGE, ids=[c[0] for c in RANGE])
+def test_bf16_backward_numeric_range(case):
+    """bf16 inputs far from unit scale.  The dK/dV kernel holds Q, K and dS in
+    fp16 (exact for bf16 values within fp16's range, |x| <= 65504; fp16
+    subnormals below 6.1e-5 keep fewer bits).  With q, k, v, dout scaled by
+    mq, mk, mv, mdo (mq * mk = 1), P is unchanged, dS scales by mdo * mv, and
+    dQ, dK, dV by mdo * mv * mk, mdo * mv * mq and mdo: each fp32 gradient,
+    divided by its factor, must meet the unit-scale tolerance against the
+    oracle's gradient of the same scaled inputs, divided likewise."""
+    name, mq, mk, mv, mdo = case
+    print("case", name, flush=True)
+    B, S, hq, hkv, d = 1, 300, 4, 2, 128
+    base = synth.batched_inputs(zlib.crc32(name.encode()) % 1000, B, S, S, hq, hkv, d, grads=True)
+    scaled = lambda bits, m: synth.f32_to_bf16_bits(synth.bits_to_f32(bits) * np.float32(m))  # noqa: E731
+    inp = dict(q=scaled(base["q"], mq), k=scaled(base["k"], mk), v=scaled(base["v"], mv),
+               dout=scaled(base["dout"], mdo), sinks=None)
+    ref = oracle.full(oracle_batched(inp, True, (100, 0), scale_of(d)))
+    q, k, v, do = (dev_tensor(inp[n]) for n in ("q", "k", "v", "dout"))
+    o, lse = ea.attn_fwd(q, k, v, causal=True, window=(100, 0))
+    dq, dk, dv, _ = ea.attn_bwd(q, k, v, o, lse, do, causal=True, window=(100, 0), grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    fq, fk, fv = mdo * mv * mk, mdo * mv * mq, mdo
+    assert_close(name + ".dq", host(dq).reshape(B * S, hq, d) / fq, ref["dq"] / fq, "f32")
+    assert_close(name + ".dk", host(dk).reshape(B * S, hkv, d) / fk, ref["dk"] / fk, "f32")
+    assert_close(name + ".dv", host(dv).reshape(B * S, hkv, d) / fv, ref["dv"] / fv, "f32")
