@@ -27,7 +27,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ATTN36_ORACLE_LIB selects another build of the same source (the tests run
+# an AddressSanitizer build through it)
+_LIB_PATH = os.environ.get("ATTN36_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 

@@ -1,0 +1,46 @@
+// Host-only stand-ins for the kernel launchers and the scratch lookup, so that
+// the C ABI's argument checks, workspace layout and grid set-up can run (and
+// be checked) on a machine with no GPU, under AddressSanitizer.  Each stub
+// keeps the argument block it was given.
+#include "../../exact_attention_36_amd/csrc/attn_kernels.h"
+
+namespace stub {
+attn::FwdArgs last_fwd;
+attn::BwdArgs last_bwd;
+int fwd_calls = 0, combine_calls = 0, bwd_calls = 0, append_calls = 0, rotary_calls = 0;
+int last_tile_d = 0;
+}  // namespace stub
+
+namespace attn {
+hipError_t launch_fwd(const FwdArgs& a, int tile_d, bool, hipStream_t) {
+  stub::last_fwd = a;
+  stub::last_tile_d = tile_d;
+  stub::fwd_calls++;
+  return hipSuccess;
+}
+hipError_t launch_fwd_combine(const FwdArgs& a, int, bool, hipStream_t) {
+  stub::last_fwd = a;
+  stub::combine_calls++;
+  return hipSuccess;
+}
+hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool, hipStream_t) {
+  stub::last_bwd = a;
+  stub::last_tile_d = tile_d;
+  stub::bwd_calls++;
+  return hipSuccess;
+}
+hipError_t launch_rotary(const void*, void*, int64_t, int, int, int, const int32_t*, int, const RotaryArgs&, bool,
+                         hipStream_t) {
+  stub::rotary_calls++;
+  return hipSuccess;
+}
+hipError_t launch_append(const AppendArgs&, int32_t*, bool, hipStream_t) {
+  stub::append_calls++;
+  return hipSuccess;
+}
+static char fake_scratch[64];
+hipError_t noalloc_scratch(void** out) {
+  *out = fake_scratch;  // never dereferenced: the launch is a stub
+  return hipSuccess;
+}
+}  // namespace attn

@@ -1,0 +1,98 @@
+"""AddressSanitizer builds of the host code, on the CPU (SURVEY's memory-safety
+plan): the C ABI's host side -- attn_api.cpp with host stand-ins for the
+kernel launchers, driven through every entry point by tests/asan/abi_driver.cpp,
+which also checks that each workspace region handed to the kernels lies
+inside the caller's workspace -- and the oracle, on small problems covering
+its mask, sink, variant, used-length, cache and packed paths.  Any invalid
+host memory access aborts the run with an AddressSanitizer report."""
+import os
+import shutil
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HIPCC = "/opt/rocm/bin/hipcc"
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1")
+
+
+def _run(cmd, **kw):
+    r = subprocess.run(cmd, capture_output=True, text=True, **kw)
+    assert r.returncode == 0, "%s\n%s%s" % (" ".join(cmd), r.stdout[-4000:], r.stderr[-4000:])
+    return r
+
+
+@pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANGXX)), reason="ROCm compilers not found")
+def test_abi_host_code_under_asan(tmp_path):
+    srcs = [os.path.join(ROOT, "tests", "asan", "abi_driver.cpp"), os.path.join(ROOT, "tests", "asan", "launch_stubs.cpp"),
+            os.path.join(ROOT, "exact_attention_36_amd", "csrc", "attn_api.cpp"),
+            os.path.join(ROOT, "exact_attention_36_amd", "csrc", "attn_timing.cpp")]
+    objs = []
+    for s in srcs:
+        o = str(tmp_path / (os.path.basename(s) + ".o"))
+        # host code only is instrumented (-Xarch_host before each sanitizer flag)
+        _run([HIPCC, "-O1", "-g", "-std=c++17", "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"), "-c", s, "-o", o])
+        objs.append(o)
+    exe = str(tmp_path / "abi_asan")
+    _run([CLANGXX, "-fsanitize=address", *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe])
+    r = subprocess.run([exe], capture_output=True, text=True, env=ENV, timeout=300)
+    out = r.stdout + r.stderr
+    assert "AddressSanitizer" not in out, out[-4000:]
+    assert r.returncode == 0 and "all checks passed" in r.stdout, out[-4000:]
+
+
+ORACLE_SCRIPT = textwrap.dedent('''
+    import numpy as np
+    import oracle
+
+    rng = np.random.default_rng(0)
+
+    def bits(shape):
+        x = rng.standard_normal(shape).astype(np.float32)
+        u = x.view(np.uint32)
+        return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+    s = 1.0 / np.sqrt(32.0)
+    # batched, GQA, causal + window, sinks, used lengths
+    q, k, v, do = bits((2, 9, 4, 32)), bits((2, 11, 2, 32)), bits((2, 11, 2, 32)), bits((2, 9, 4, 32))
+    p = oracle.batched(q, k, v, s, causal=True, window=(3, 1), dout=do, sinks=rng.standard_normal(4).astype(np.float32),
+                       seqused_q=[9, 4], seqused_k=[11, 0])
+    r = oracle.full(p)
+    assert all(np.all(np.isfinite(r[n])) for n in ("o", "dq", "dk", "dv", "dsinks"))
+    # packed with empty sequences, soft cap + ALiBi + several sinks per head
+    lens = [0, 5, 17, 0, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v, do = bits((T, 4, 32)), bits((T, 1, 32)), bits((T, 1, 32)), bits((T, 4, 32))
+    p = oracle.varlen(q, k, v, cu, cu, s, causal=True, dout=do, sinks=rng.standard_normal((4, 3)).astype(np.float32),
+                      softcap=5.0, alibi=np.full(4, 0.25, np.float32))
+    r = oracle.full(p)
+    rows = oracle.rows(p, [1, 2, 4], [0, 3, 1], [0, 16, 2], grads=True)
+    cols = oracle.cols(p, 2, 0, np.arange(17))
+    # paged KV cache gather, rotary and the cache append
+    kc, vc = bits((6, 8, 2, 32)), bits((6, 8, 2, 32))
+    table = np.array([[5, 0, 3], [1, 4, 2]], np.int32)
+    p = oracle.kvcache(bits((2, 3, 4, 32)), kc, vc, np.array([20, 7], np.int32), s, block_table=table, causal=True)
+    oracle.full(p, grads=False)
+    ang = np.arange(64)[:, None] * 0.1 * np.arange(1, 9)[None, :]
+    x = rng.standard_normal((2, 3, 2, 32))
+    oracle.rotary(x, np.cos(ang), np.sin(ang), np.array([[0, 1, 2], [7, 8, 9]]), 16, True)
+    print("oracle under asan: ok")
+''')
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
+def test_oracle_under_asan(tmp_path):
+    lib = str(tmp_path / "liboracle_asan.so")
+    _run(["gcc", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer", "-fopenmp", "-fPIC", "-shared",
+          "-std=c11", "-fno-fast-math", "-ffp-contract=off", os.path.join(ROOT, "oracle", "attn_oracle.c"), "-o", lib,
+          "-lm"])
+    libasan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    env = dict(ENV, LD_PRELOAD=libasan, ATTN36_ORACLE_LIB=lib, OMP_NUM_THREADS="2", PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", ORACLE_SCRIPT], capture_output=True, text=True, env=env, timeout=600)
+    out = r.stdout + r.stderr
+    assert "AddressSanitizer" not in out, out[-4000:]
+    assert r.returncode == 0 and "oracle under asan: ok" in r.stdout, out[-4000:]
