@@ -129,114 +129,13 @@ void bwd_dq_kernel(const BwdArgs a) {
   const auto rq = make_rsrc((const uint16_t*)a.q + qbase_e, qbytes);
   const auto rdo = make_rsrc((const uint16_t*)a.dout + qbase_e, qbytes);
 
-  u32x4 qf[KS], df[KS];
-#pragma unroll
-  for (int s = 0; s < KS; s++) {
-    qf[s] = buf_load16(rq, chunk_off(qoff, 2 * s + hh, dg));
-    df[s] = buf_load16(rdo, chunk_off(qoff, 2 * s + hh, dg));
-  }
-  // Row statistics, computed here once per (query row, q head) and left in
-  // the workspace for the dK/dV kernel that runs after this one:
-  //   D = rowsum(dO * O), O being the stored (sink-gated) output;
-  //   lse' = log2(2^lse + 2^sink) in log2 units (+inf for an empty row, so
-  //   that P = 0 there);  dsink = -sum_rows (1 - gate) D, gate = sigmoid(lse - sink)
-  //   (dew-flash-attn page, sinks paragraph).
-  float row_d, row_dn;  // D_i and |dO_i|_2
-  {
-    const auto ro = make_rsrc((const uint16_t*)a.o + qbase_e, qbytes);
-    float part = 0.f, sq = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; s++) {
-      const u32x4 ov = buf_load16(ro, chunk_off(qoff, 2 * s + hh, dg));
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const float d0 = to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), d1 = to_f32<F16>((uint16_t)(df[s][e] >> 16));
-        part = fmaf(to_f32<F16>((uint16_t)(ov[e] & 0xFFFF)), d0, part);
-        part = fmaf(to_f32<F16>((uint16_t)(ov[e] >> 16)), d1, part);
-        sq = fmaf(d0, d0, fmaf(d1, d1, sq));
-      }
-    }
-    row_d = half_sum(part);  // the two lanes holding one row's halves
-    row_dn = my_p < prows ? __builtin_sqrtf(half_sum(sq)) : 0.f;
-  }
-  // The workgroup's largest |dO_i|_2 and |D_i| (every row of one sequence and
-  // kv head), for the dK/dV kernel's bound on |dS|.
-  {
-    float m0 = row_dn, m1 = my_p < prows ? fabsf(row_d) : 0.f;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      m0 = fmaxf(m0, __shfl_xor(m0, o));
-      m1 = fmaxf(m1, __shfl_xor(m1, o));
-    }
-    __shared__ float nrm[2][4];
-    if (lane == 0) {
-      nrm[0][wave] = m0;
-      nrm[1][wave] = m1;
-    }
-    __syncthreads();
-    if (threadIdx.x < 2) {
-      const float* r = nrm[threadIdx.x];
-      dscale_out[threadIdx.x] = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
-    }
-  }
-  float row_lse2 = INFINITY, dsink_part = 0.f;
-  if (my_p < prows) {
-    const int64_t li = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
-                                : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
-    const float lse = a.lse[li];
-    if (lse != -INFINITY) {
-      row_lse2 = lse * LOG2E;
-      if (a.sinks) {
-        const float s2 = sink_log2(a.sinks, a.x, my_h);
-        const float mx = fmaxf(row_lse2, s2), mn = fminf(row_lse2, s2);
-        dsink_part = -row_d / (1.f + exp2_fast(row_lse2 - s2));
-        row_lse2 = mx + log2_fast(1.f + exp2_fast(mn - mx));
-      }
-    } else {
-      dsink_part = -row_d;  // no visible key: the sink takes the whole denominator
-    }
-    if (hh == 0) {
-      a.delta[li] = row_d;
-      a.lse2[li] = row_lse2;
-    }
-  }
-  if (dsink_out) {
-    // the block's rows summed per q head in a fixed order (no atomics): row r
-    // of the block (packed row p0 + r) belongs to head slot r mod G, and
-    // thread t < G adds rows t, t + G, t + 2G, ...; slot t is q head
-    // (p0 + t) mod G of the group
-    __shared__ float dsink_rows[BM];
-    if (hh == 0) dsink_rows[my_p - p0] = dsink_part;
-    __syncthreads();
-    if ((int)threadIdx.x < G) {
-      float v = 0.f;
-      for (int r = threadIdx.x; r < BM; r += G) v += dsink_rows[r];
-      dsink_out[(p0 + (int)threadIdx.x) % G] = v;
-    }
-  }
-  const float c = a.scale_log2;
-  const float mlse = row_lse2 == INFINITY ? 0.f : row_lse2;  // empty rows are fully masked
-  // score variants: this row's ALiBi slope / scale and its diagonal, less 4 hh
-  const float ext_kb = (EXT & EXT_ALIBI) ? alibi_kb(a.x, seq, my_h) : 0.f;
-  const float ext_diag = (float)(my_i + si.lk - si.lq - 4 * hh);
-
+  // K/V tiles stream through LDS like the forward's (two K and two V slots).
   uint32_t dma_off[SLABS];
 #pragma unroll
   for (int n = 0; n < SLABS; n++) {
     const int byte = (wave * SLABS + n) * 1024 + lane * 16;
     const int r = byte / ROWB, pos = (byte % ROWB) >> 4;
     dma_off[n] = chunk_off((uint32_t)(r * krow * 2), pos ^ swz<D>(r), dg);
-  }
-  int k_off[KS];
-#pragma unroll
-  for (int s = 0; s < KS; s++) k_off[s] = tile_off<D>(l32, 2 * s + hh);
-  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
-  int t_off[DB][2];
-#pragma unroll
-  for (int d = 0; d < DB; d++) {
-    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
-#pragma unroll
-    for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
   }
   // (byte offsets inside one sequence's K/V fit in 31 bits)
   const uint32_t tile_stride = (uint32_t)(FWD_BN * krow * 2);
@@ -252,6 +151,89 @@ void bwd_dq_kernel(const BwdArgs a) {
       dma_lds16(rv, smem + (2 + buf) * TILE + (wave * SLABS + n) * 1024, dma_off[n]);
     }
   };
+
+  // Every load the prologue needs is issued before any of them is waited on
+  // (each dependent round trip to HBM costs microseconds at full load): the
+  // row's Q, dO and O chunks, its lse and sink logit, and the first K/V tile.
+  const auto ro = make_rsrc((const uint16_t*)a.o + qbase_e, qbytes);
+  u32x4 qf[KS], df[KS], ov[KS];
+#pragma unroll
+  for (int s = 0; s < KS; s++) {
+    qf[s] = buf_load16(rq, chunk_off(qoff, 2 * s + hh, dg));
+    df[s] = buf_load16(rdo, chunk_off(qoff, 2 * s + hh, dg));
+    ov[s] = buf_load16(ro, chunk_off(qoff, 2 * s + hh, dg));
+  }
+  const int64_t row_idx = a.s.cu_q ? (int64_t)my_h * a.s.total_q + si.q0 + my_i
+                                   : ((int64_t)seq * a.s.hq + my_h) * a.s.sq + my_i;
+  const float lse = my_p < prows ? a.lse[row_idx] : -INFINITY;
+  const float sink2 = a.sinks ? sink_log2(a.sinks, a.x, my_h) : 0.f;
+  if (t_begin < t_end) load_tile(t_begin);
+
+  // Row statistics, computed here once per (query row, q head) and left in
+  // the workspace for the dK/dV kernel that runs after this one:
+  //   D = rowsum(dO * O), O being the stored (sink-gated) output;
+  //   lse' = log2(2^lse + 2^sink) in log2 units (+inf for an empty row, so
+  //   that P = 0 there);  dsink = -sum_rows (1 - gate) D, gate = sigmoid(lse - sink)
+  //   (dew-flash-attn page, sinks paragraph).
+  float row_d, row_dn;  // D_i and |dO_i|_2
+  {
+    float part = 0.f, sq = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; s++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float d0 = to_f32<F16>((uint16_t)(df[s][e] & 0xFFFF)), d1 = to_f32<F16>((uint16_t)(df[s][e] >> 16));
+        part = fmaf(to_f32<F16>((uint16_t)(ov[s][e] & 0xFFFF)), d0, part);
+        part = fmaf(to_f32<F16>((uint16_t)(ov[s][e] >> 16)), d1, part);
+        sq = fmaf(d0, d0, fmaf(d1, d1, sq));
+      }
+    row_d = half_sum(part);  // the two lanes holding one row's halves
+    row_dn = my_p < prows ? __builtin_sqrtf(half_sum(sq)) : 0.f;
+  }
+  float row_lse2 = INFINITY, dsink_part = 0.f;
+  if (my_p < prows) {
+    if (lse != -INFINITY) {
+      row_lse2 = lse * LOG2E;
+      if (a.sinks) {
+        const float mx = fmaxf(row_lse2, sink2), mn = fminf(row_lse2, sink2);
+        dsink_part = -row_d / (1.f + exp2_fast(row_lse2 - sink2));
+        row_lse2 = mx + log2_fast(1.f + exp2_fast(mn - mx));
+      }
+    } else {
+      dsink_part = -row_d;  // no visible key: the sink takes the whole denominator
+    }
+    if (hh == 0) {
+      a.delta[row_idx] = row_d;
+      a.lse2[row_idx] = row_lse2;
+    }
+  }
+  // Per-row inputs of the workgroup's reductions, parked in LDS until after
+  // the loop: |dO_i|_2, |D_i| and the row's d(sink) term (rows past the
+  // sequence contribute 0).
+  __shared__ float red_rows[3][BM];
+  if (hh == 0) {
+    const bool in = my_p < prows;
+    red_rows[0][my_p - p0] = row_dn;
+    red_rows[1][my_p - p0] = in ? fabsf(row_d) : 0.f;
+    red_rows[2][my_p - p0] = dsink_part;
+  }
+  const float c = a.scale_log2;
+  const float mlse = row_lse2 == INFINITY ? 0.f : row_lse2;  // empty rows are fully masked
+  // score variants: this row's ALiBi slope / scale and its diagonal, less 4 hh
+  const float ext_kb = (EXT & EXT_ALIBI) ? alibi_kb(a.x, seq, my_h) : 0.f;
+  const float ext_diag = (float)(my_i + si.lk - si.lq - 4 * hh);
+
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; s++) k_off[s] = tile_off<D>(l32, 2 * s + hh);
+  const int gq = lane >> 4, li = lane & 15, esrc = li >> 2, jsrc = li & 3;
+  int t_off[DB][2];
+#pragma unroll
+  for (int d = 0; d < DB; d++) {
+    const int col = d * 32 + 16 * (gq & 1) + 4 * jsrc;
+#pragma unroll
+    for (int w = 0; w < 2; w++) t_off[d][w] = tile_off<D>(4 * hh + esrc + 8 * w, col >> 3) + (jsrc & 1) * 8;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -361,10 +343,53 @@ void bwd_dq_kernel(const BwdArgs a) {
     ti1 = min(t_end, (full_hi + 1) / FWD_BN);
     if (ti1 <= ti0) ti0 = ti1 = t_begin;
   }
-  if (t_begin < t_end) load_tile(t_begin);
   run(t_begin, ti0, std::true_type{});
   run(ti0, ti1, std::false_type{});
   run(ti1, t_end, std::true_type{});
+
+  // The workgroup's maxima and sums for the later kernels, formed after the
+  // loop so that they do not delay its first tile: the largest |dO_i|_2 and
+  // |D_i| of the block (every row of one sequence and kv head; the dK/dV
+  // kernel's bound on |dS|), and with sinks the block's rows summed per q
+  // head in a fixed order (no atomics).  Row r of the block (packed row
+  // p0 + r) belongs to head slot r mod G; slot s is q head (p0 + s) mod G of
+  // the group.  The sum of slot s takes chunk c = 0..7 of its rows (rows
+  // s + G (c + 8 j)) in one thread each (fewer chunks when G > 32), then
+  // adds the chunk sums in order.
+  {
+    constexpr int NC = 8;
+    __shared__ float chunk_sum[NC][BM];
+    __syncthreads();
+    if (wave == 0) {
+      float m0 = fmaxf(red_rows[0][lane], red_rows[0][lane + 64]);
+      float m1 = fmaxf(red_rows[1][lane], red_rows[1][lane + 64]);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        m0 = fmaxf(m0, __shfl_xor(m0, o));
+        m1 = fmaxf(m1, __shfl_xor(m1, o));
+      }
+      if (lane == 0) {
+        dscale_out[0] = m0;
+        dscale_out[1] = m1;
+      }
+    }
+    if (dsink_out) {
+      const int t = threadIdx.x;
+      const int nc = G <= THREADS / NC ? NC : THREADS / G;  // G <= 128 q heads per kv head
+      if (t < G * nc) {
+        const int sl = t % G, ch = t / G;
+        float v = 0.f;
+        for (int r = sl + G * ch; r < BM; r += G * nc) v += red_rows[2][r];
+        chunk_sum[ch][sl] = v;
+      }
+      __syncthreads();
+      if (t < G) {
+        float v = 0.f;
+        for (int ch = 0; ch < nc; ch++) v += chunk_sum[ch][t];
+        dsink_out[(p0 + t) % G] = v;
+      }
+    }
+  }
 
   // dQ = scale * acc; lane = query row, registers = dims 8(i/4) + 4hh + i%4 of each 32-block
   if (a.grad_f32) {
