@@ -345,6 +345,43 @@ def run_variants(steps, warmup):
     return rows
 
 
+def run_stream(steps, warmup):
+    """Practical HBM rates on this machine for the decode shape's bytes: torch's
+    own streaming kernels over 4.295 GB (the K and V of the decode shape) --
+    a sum (reads only), a copy (read + write) and an add (two reads, one
+    write) -- each repetition after the MALL flush, timed with HIP events.
+    A reference for the decode's K/V rate, not a kernel of this library."""
+    import torch
+    n = 2 * 32 * 32768 * 8 * 128  # elements of K and V, bf16
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    flush = Flusher()
+    rows = []
+    for name, fn, nbytes in (
+            ("sum (read)", lambda: x.sum(dtype=torch.float32), 2 * n),
+            ("copy (read + write)", None, 4 * n),
+            ("add (2 reads + write)", None, 6 * n // 2)):
+        if name.startswith("copy"):
+            y = torch.empty_like(x)
+            fn = lambda: y.copy_(x)  # noqa: E731
+        elif name.startswith("add"):
+            a, b = x[: n // 2], x[n // 2:]
+            z = torch.empty_like(a)
+            fn = lambda: torch.add(a, b, out=z)  # noqa: E731
+        for _ in range(warmup):
+            fn()
+        st = summary(time_each(fn, steps, flush))
+        rows.append({"stream": name, "bytes": nbytes, "ms": st,
+                     "GBps": round(nbytes / (st["median"] * 1e-3) / 1e9, 1),
+                     "frac_of_8TBps": round(nbytes / (st["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        print(json.dumps(rows[-1]), flush=True)
+        if name.startswith("copy"):
+            del y
+        elif name.startswith("add"):
+            del z
+        torch.cuda.empty_cache()
+    return rows
+
+
 def run_latency(steps, warmup):
     """Launch-bound shape (B=1, H=2, S=128, D=64, bf16, non-causal forward):
     µs per call issued eagerly through the binding, per call of a HIP graph
@@ -777,7 +814,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the other workloads (configs 1, 3, 4 and the decode shape)")
-    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power", "configs"), default="step",
+    ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power", "configs",
+                                           "stream"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
                          "sweep: context sweep over S = 512..16384 (one JSON line per shape); configs: kernel times of the five "
@@ -785,7 +823,8 @@ def main():
                          "headdims: causal prefill at D = 32..256 (one JSON line per head dim); "
                          "variants: causal prefill with soft cap / ALiBi / 4 sinks (one line each); "
                          "latency: launch-bound forward, eager calls vs HIP graph replays; "
-                         "power: socket power and shader clock (amd-smi) under the step's kernels")
+                         "power: socket power and shader clock (amd-smi) under the step's kernels; "
+                         "stream: torch's own sum / copy / add over the decode shape's 4.3 GB (practical HBM rates)")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=None,
                     help="with --workload configs: run only this workload (1..5 in the order listed there)")
@@ -821,6 +860,9 @@ def main():
         return
     if args.workload == "power":
         run_power(args.seconds)
+        return
+    if args.workload == "stream":
+        run_stream(args.steps, args.warmup)
         return
     if args.workload == "decode":
         if args.copy_calibration:
