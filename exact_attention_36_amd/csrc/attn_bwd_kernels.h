@@ -18,11 +18,13 @@
 //
 // Kernels, in stream order:
 //   bwd_dq_kernel     query-major: one workgroup per 128 packed query rows
-//                     computes the rows' D_i, lse' (log2 units, with the
-//                     sink) and its per-head dsink sums, then
-//                     streams the visible K/V tiles (like the forward),
-//                     recomputes S, P, dP, dS and accumulates dQ in
-//                     registers; dQ is written once, no atomics
+//                     computes the rows' D_i and lse' (log2 units, with
+//                     the sink), streams the visible K/V tiles (like the
+//                     forward), recomputes S, P, dP, dS and accumulates dQ
+//                     in registers; after its loop it forms the block's
+//                     per-head dsink sums and its largest |dO_i|_2 and
+//                     |D_i| (the dK/dV kernel's dS scale); dQ is written
+//                     once, no atomics
 //   bwd_dkdv_kernel   key-major: one workgroup per 128-key block of one kv
 //                     head streams the visible query blocks of all the
 //                     group's q heads, recomputes S, P, dP, dS and
