@@ -91,9 +91,10 @@ def check_dsinks(name, got, ref, p):
         for h in range(p.hq):
             for i in range(int(p.q_len[sq_])):
                 seqs.append(sq_), heads.append(h), rws.append(i)
-    r = oracle.rows(p, seqs, heads, rws, grads=True)
     mag = np.zeros(p.hq)
-    np.add.at(mag, np.asarray(heads), np.abs((1.0 - r["gate"]) * r["delta"]))
+    if heads:  # (no used query rows at all: the bound is the constant term)
+        r = oracle.rows(p, seqs, heads, rws, grads=True)
+        np.add.at(mag, np.asarray(heads, dtype=np.int64), np.abs((1.0 - r["gate"]) * r["delta"]))
     tab = p.sink_table()
     share = np.exp(tab - tab.max(axis=1, keepdims=True))
     share /= share.sum(axis=1, keepdims=True)
