@@ -351,9 +351,9 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   // The workgroup's maxima and sums for the later kernels, formed after the
   // loop so that they do not delay its first tile: the largest |dO_i|_2 and
-  // |D_i| of the block (every row of one sequence and kv head; the dK/dV
-  // kernel's bound on |dS|), and with sinks the block's rows summed per q
-  // head in a fixed order (no atomics).  Row r of the block (packed row
+  // |D_i| of the block (the dK/dV kernel takes their maxima over the blocks of
+  // a sequence and kv head for its bound on |dS|), and with sinks the block's
+  // rows summed per q head in a fixed order (no atomics).  Row r of the block (packed row
   // p0 + r) belongs to head slot r mod G; slot s is q head (p0 + s) mod G of
   // the group.  The sum of slot s takes chunk c = 0..7 of its rows (rows
   // s + G (c + 8 j)) in one thread each (fewer chunks when G > 32), then
