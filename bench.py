@@ -4,7 +4,7 @@ N(0,1) inputs resident in HBM), through the C ABI.
 
 Prints one JSON line.  `value` is fwd+bwd algorithmic TFLOP/s (14 * D * visible
 (query, key) pairs per step: 4*D forward, 10*D backward) at the median of the
-K timed steps, each timed with HIP events after a 512 MB write that flushes
+K timed steps, each timed with HIP events after a 512 MB read that flushes
 the MALL (min, p90 and the unflushed "warm" steps are reported beside it).
 `roofline` reports the kernel with the most time per step (found in a pass
 with every launch timed), whose launches in the timed region are bracketed by
@@ -110,11 +110,31 @@ def copy_calibration():
 DECODE = dict(name="decode / chunked-prefill fwd B32 s_q16 s_kv32768 Hq64 Hkv8 D128 bf16 causal", B=32, SQ=16,
               SK=32768, HQ=64, HKV=8, D=128)
 FLUSH_BYTES = 512 << 20  # twice the 256 MB MALL (last-level cache)
+SPIN_CYCLES = 200000     # torch.cuda._sleep before a timed call in the flush check
 
 
 class Flusher:
-    """Writes a 512 MB buffer (a fill kernel on the current stream), which
-    evicts the K/V tiles the previous repetition left in the MALL."""
+    """Reads a 512 MB buffer (a reduction kernel on the current stream),
+    which evicts the tiles the previous repetition left in the MALL.  The
+    buffer is written once, here; the per-repetition flush only reads it, so
+    the MALL is left holding clean lines and the timed kernel that follows
+    pays for no write-back of the flush's own data (a 512 MB write before
+    each repetition evicts as well but slows the next kernel by that
+    write-back: `--workload flush` measures both)."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
+        self.sink = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+class WriteFlusher:
+    """The alternative flush: a 512 MB write (fill kernel) before each
+    repetition; kept for the comparison in `--workload flush`."""
 
     def __init__(self):
         import torch
@@ -380,6 +400,48 @@ def run_stream(steps, warmup):
             del z
         torch.cuda.empty_cache()
     return rows
+
+
+def run_flush_check(steps, warmup):
+    """What the MALL flush does to the timed call after it.  Three callers:
+    a decode-shaped forward over 67 MB of K/V (s_kv = 512: it fits in the
+    256 MB MALL, so it runs faster warm), the full decode shape (4.3 GB of
+    K/V, far larger than the MALL) and the causal prefill forward; each timed
+    with no flush (warm), after the 512 MB read flush and after a 512 MB
+    write.  A flush that evicts shows as the small decode slowing down; one
+    that leaves write-backs behind shows as the large decode slowing down.
+    In every mode a spin kernel runs just before the call (see below)."""
+    import torch
+    import exact_attention_36_amd as ea
+    from exact_attention_36_amd import synth
+    d = DECODE
+    flushes = {"none": None, "read": Flusher(), "write": WriteFlusher()}
+    w = WORKLOAD
+    shapes = [("decode B32 s_q16 s_kv512 Hq64 Hkv8 D128 (K/V 67 MB)", d["B"], d["SQ"], 512, d["HQ"], d["HKV"]),
+              ("decode B32 s_q16 s_kv32768 Hq64 Hkv8 D128 (K/V 4.3 GB)", d["B"], d["SQ"], d["SK"], d["HQ"], d["HKV"]),
+              ("causal prefill fwd B4 H16 S2048 D128", w["B"], w["S"], w["S"], w["HQ"], w["HKV"])]
+    for name, B, sq, sk, hq, hkv in shapes:
+        q, k, v = synth.device_normal(5, [(B, sq, hq, d["D"]), (B, sk, hkv, d["D"]), (B, sk, hkv, d["D"])])
+        o, lse = ea.attn_fwd(q, k, v, causal=True)
+        call = lambda: ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        res = {}
+        for _ in range(2):  # two alternations; the second is reported
+            for fname, f in flushes.items():
+                # a spin kernel after the flush (or alone) keeps the GPU busy
+                # while the host queues the call, so that no mode is timed
+                # with the host's launch latency in it
+                def pre(f=f):
+                    if f is not None:
+                        f()
+                    torch.cuda._sleep(SPIN_CYCLES)
+                res[fname] = summary(time_each(call, steps, pre))
+        print(json.dumps({"workload": "flush check", "caller": name, "kv_bytes": 2 * k.numel() * 2,
+                          "ms_per_call": res}), flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
 
 
 def run_latency(steps, warmup):
@@ -815,7 +877,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the other workloads (configs 1, 3, 4 and the decode shape)")
     ap.add_argument("--workload", choices=("step", "decode", "sweep", "headdims", "variants", "latency", "power", "configs",
-                                           "stream"), default="step",
+                                           "stream", "flush"), default="step",
                     help="step: the fwd+bwd line (default, also measures the decode shape); "
                          "decode: only the decode-shaped forward (for profiling it alone); "
                          "sweep: context sweep over S = 512..16384 (one JSON line per shape); configs: kernel times of the five "
@@ -824,7 +886,8 @@ def main():
                          "variants: causal prefill with soft cap / ALiBi / 4 sinks (one line each); "
                          "latency: launch-bound forward, eager calls vs HIP graph replays; "
                          "power: socket power and shader clock (amd-smi) under the step's kernels; "
-                         "stream: torch's own sum / copy / add over the decode shape's 4.3 GB (practical HBM rates)")
+                         "stream: torch's own sum / copy / add over the decode shape's 4.3 GB (practical HBM rates); "
+                         "flush: calls timed warm, after the read flush and after a 512 MB write")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=None,
                     help="with --workload configs: run only this workload (1..5 in the order listed there)")
@@ -863,6 +926,9 @@ def main():
         return
     if args.workload == "stream":
         run_stream(args.steps, args.warmup)
+        return
+    if args.workload == "flush":
+        run_flush_check(args.steps, args.warmup)
         return
     if args.workload == "decode":
         if args.copy_calibration:
