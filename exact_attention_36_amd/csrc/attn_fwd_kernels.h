@@ -461,18 +461,35 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
   const int i = div_group(p, a.s), hl = p - i * G, h = g * G + hl;
   const int64_t split_stride = (int64_t)a.s.nseq * a.s.hkv * rows_bg;
   const int ns = a.n_split;
-
+  // The first NST splits' partials (lse and this lane's 4 dims) are loaded
+  // together, before any is used, so that they are in flight at once; splits
+  // past them, if any, are read in the loops below.  A split with no visible
+  // key wrote O_s = 0 and lse_s = -inf, and so adds 0.
+  constexpr int NST = 4;
+  const float* op = a.o_part + row * D + sub * 4;
+  float lv[NST];
+  f32x4 ov[NST];
+#pragma unroll
+  for (int s = 0; s < NST; s++) {
+    lv[s] = s < ns ? a.lse_part[row + s * split_stride] : -INFINITY;
+    ov[s] = s < ns ? *(const f32x4*)(op + s * split_stride * D) : f32x4{};
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < ns; s++) mx = fmaxf(mx, a.lse_part[row + s * split_stride]);
+#pragma unroll
+  for (int s = 0; s < NST; s++) mx = fmaxf(mx, lv[s]);
+  for (int s = NST; s < ns; s++) mx = fmaxf(mx, a.lse_part[row + s * split_stride]);
   float sum = 0.f;
-  if (mx != -INFINITY)
-    for (int s = 0; s < ns; s++) sum += exp2_fast((a.lse_part[row + s * split_stride] - mx) * LOG2E);
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < NST; s++) sum += exp2_fast((lv[s] - mx) * LOG2E);
+    for (int s = NST; s < ns; s++) sum += exp2_fast((a.lse_part[row + s * split_stride] - mx) * LOG2E);
+  }
   const float lse = mx == -INFINITY ? -INFINITY : mx + log2_fast(sum) * LN2;
   f32x4 o{};
   if (mx != -INFINITY) {
-    const float* op = a.o_part + row * D + sub * 4;
-#pragma unroll 4
-    for (int s = 0; s < ns; s++) {
+#pragma unroll
+    for (int s = 0; s < NST; s++) o += exp2_fast((lv[s] - lse) * LOG2E) * ov[s];
+    for (int s = NST; s < ns; s++) {
       const float w = exp2_fast((a.lse_part[row + s * split_stride] - lse) * LOG2E);
       o += w * *(const f32x4*)(op + s * split_stride * D);
     }
