@@ -109,6 +109,8 @@ def copy_calibration():
 
 DECODE = dict(name="decode / chunked-prefill fwd B32 s_q16 s_kv32768 Hq64 Hkv8 D128 bf16 causal", B=32, SQ=16,
               SK=32768, HQ=64, HKV=8, D=128)
+DECODE_BATCHED = dict(name="batched decode fwd B128 s_q1 s_kv8192 Hq64 Hkv8 D128 bf16 causal (keys not split)",
+                      B=128, SQ=1, SK=8192, HQ=64, HKV=8, D=128)
 FLUSH_BYTES = 512 << 20  # twice the 256 MB MALL (last-level cache)
 SPIN_CYCLES = 200000     # torch.cuda._sleep before a timed call in the flush check
 
@@ -194,11 +196,29 @@ def run_decode(steps, warmup, flush=None):
     pairs = visible_pairs(d["B"], d["SQ"], d["SK"], d["HQ"], True, (-1, -1))
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+    # A batched decode with enough (sequence, kv head) work tiles not to split
+    # the keys: the same 4.3 GB of K/V, each tile read by one workgroup, no
+    # combine kernel.
+    b = DECODE_BATCHED
+    q, k, v = synth.device_normal(6, [(b["B"], b["SQ"], b["HQ"], b["D"]), (b["B"], b["SK"], b["HKV"], b["D"]),
+                                      (b["B"], b["SK"], b["HKV"], b["D"])])
+    o, lse = ea.attn_fwd(q, k, v, causal=True)
+    call = lambda: ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    st_b = summary(time_each(call, steps, flush))
+    kv_b = 2 * b["B"] * b["SK"] * b["HKV"] * b["D"] * 2
+    gb_b = kv_b / (st_b["median"] * 1e-3) / 1e9
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
     return {"workload": d["name"], "ms_per_call": st, "kv_bytes": kv_bytes, "kv_GBps": round(gbps, 1),
             "hbm_peak_GBps": HBM_PEAK_GBS, "frac": round(gbps / HBM_PEAK_GBS, 4),
             "warm_ms_per_call": warm, "warm_kv_GBps": round(kv_bytes / (warm["median"] * 1e-3) / 1e9, 1),
             "traffic": traffic_from_profile("fwd_decode"), "traffic_unit": "bytes per split-kernel launch",
-            "tflops": round(4.0 * d["D"] * pairs / (st["median"] * 1e-3) / 1e12, 2)}
+            "tflops": round(4.0 * d["D"] * pairs / (st["median"] * 1e-3) / 1e12, 2),
+            "batched_unsplit": {"workload": b["name"], "ms_per_call": st_b, "kv_bytes": kv_b,
+                                "kv_GBps": round(gb_b, 1), "frac": round(gb_b / HBM_PEAK_GBS, 4)}}
 
 
 def run_kvcache(steps, warmup, flush=None, page=256):

@@ -221,7 +221,10 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
     const int64_t ctas = (int64_t)a.nblk * p->heads_kv;
     if (ctas >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = (int32_t)ctas;
-    (void)max_q;
+    // every sequence's packed rows fit one work tile: each K/V tile is read
+    // once (max_q only selects the cache policy; a wrong value costs speed,
+    // not correctness)
+    a.kv_once = (int64_t)max_q * G <= a.bm;
   } else {
     int ns = 1, bm = 128;
     const size_t need = fwd_ws(p, nseq, sq, sk, &ns, &bm);
@@ -238,6 +241,7 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
     const int64_t ctas = GroupGrid{(int)(ns * p->heads_kv * (int64_t)nseq), a.nmb}.grid_size();
     if (ctas >= INT32_MAX || (int64_t)ns * p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = (int32_t)ctas;
+    a.kv_once = a.nmb == 1;  // one work tile per (sequence, kv head)
   }
   if (a.total_ctas == 0) return ATTN_OK;
   hipStream_t s = (hipStream_t)stream;

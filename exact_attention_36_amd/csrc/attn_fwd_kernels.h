@@ -39,12 +39,16 @@
 
 namespace attn {
 
-// SPLIT: the split-KV instance (a.n_split > 1): each K/V tile is read by one
-// workgroup only, so the tiles stream with the non-temporal hint, and the
-// epilogue writes fp32 partials for the combine kernel.
-template <int D, bool F16, bool PAD, int EXT, bool SPLIT>
+// PATH (FwdPath): FWD_SPLIT is the split-KV instance (a.n_split > 1), whose
+// epilogue writes fp32 partials for the combine kernel.  In it and in
+// FWD_STREAM each K/V tile is read by one workgroup only, so the tiles stream
+// with the non-temporal hint; FWD_SHARED keeps the default cache policy for
+// tiles that several workgroups of a head read.
+template <int D, bool F16, bool PAD, int EXT, int PATH>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
 void fwd_kernel(const FwdArgs a) {
+  constexpr bool SPLIT = PATH == FWD_SPLIT;
+  constexpr bool KV_NT = PATH != FWD_SHARED;
   // Two workgroups per CU, each with two K and two V buffers (64 KB of LDS
   // for D = 128).  The waits and loads below are written for NST buffers.
   constexpr int NW = THREADS / 64;         // waves per workgroup
@@ -208,7 +212,7 @@ void fwd_kernel(const FwdArgs a) {
       r = make_rsrc_words((const char*)((const uint16_t*)src + kbase_e) + skip, kbytes - skip);
     }
 #pragma unroll
-    for (int n = 0; n < SLABS; n++) dma_lds16<SPLIT>(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
+    for (int n = 0; n < SLABS; n++) dma_lds16<KV_NT>(r, dst + (wave * SLABS + n) * 1024, dma_off[n]);
   };
   auto kslot = [&](int t) { return smem + ((t - t_begin) & (NST - 1)) * TILE; };
   auto vslot = [&](int t) { return smem + (NST + ((t - t_begin) & (NST - 1))) * TILE; };
@@ -509,12 +513,16 @@ __global__ __launch_bounds__(THREADS) void fwd_combine_kernel(const FwdArgs a) {
 template <int EXT, int D, bool F16>
 hipError_t launch_fwd_dt(const FwdArgs& a, hipStream_t st) {
   const bool pad = a.s.dg != D;
+  const dim3 grid(a.total_ctas), block(THREADS);
   if (a.n_split > 1) {
-    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, true>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, FWD_SPLIT>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, FWD_SPLIT>), grid, block, 0, st, a);
+  } else if (a.kv_once) {
+    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, FWD_STREAM>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, FWD_STREAM>), grid, block, 0, st, a);
   } else {
-    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, false>), dim3(a.total_ctas), dim3(THREADS), 0, st, a);
+    if (pad) hipLaunchKernelGGL((fwd_kernel<D, F16, true, EXT, FWD_SHARED>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<D, F16, false, EXT, FWD_SHARED>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -77,7 +77,13 @@ struct FwdArgs {
   int32_t nblk;           // linear blocks per kv head in packed mode
   int32_t n_split;
   int32_t total_ctas;
+  int32_t kv_once;        // every K/V tile is read by one work tile only (see FwdPath)
 };
+
+// Forward instances: K/V tiles shared between work tiles (default cache
+// policy), K/V read once by a single work tile (streamed with the
+// non-temporal hint), or split-KV (read once, fp32 partials + combine).
+enum FwdPath : int { FWD_SHARED = 0, FWD_STREAM = 1, FWD_SPLIT = 2 };
 
 struct BwdArgs {
   SeqArgs s;

@@ -118,6 +118,7 @@ static void forward_layouts() {
   CHECK(attn_fwd_workspace_size(&p, 4, 2048, 2048) == 0);
   CHECK(attn_fwd(&p, 4, 2048, 2048, F, F, F, F, (float*)F, nullptr, 0, nullptr) == ATTN_OK);
   CHECK(stub::fwd_calls == before + 1 && stub::last_fwd.n_split == 1 && stub::last_fwd.total_ctas >= 1024);
+  CHECK(stub::last_fwd.kv_once == 0);  // 16 query tiles per head share its K/V tiles
   // decode: split keys, partials in the workspace
   p = params(64, 8, 128);
   const size_t n = attn_fwd_workspace_size(&p, 32, 16, 32768);
@@ -132,6 +133,11 @@ static void forward_layouts() {
   CHECK(regions_ok({{"o_part", (const char*)a.o_part, rows * stub::last_tile_d * 4},
                     {"lse_part", (const char*)a.lse_part, rows * 4}},
                    ws.data(), n));
+  // a batched decode with enough work tiles not to split: one work tile per
+  // (sequence, kv head), so each K/V tile is read once
+  CHECK(attn_fwd_workspace_size(&p, 128, 1, 8192) == 0);
+  CHECK(attn_fwd(&p, 128, 1, 8192, F, F, F, F, (float*)F, nullptr, 0, nullptr) == ATTN_OK);
+  CHECK(stub::last_fwd.n_split == 1 && stub::last_fwd.kv_once == 1 && stub::last_fwd.nmb == 1);
   // KV cache, paged: the same split path
   const size_t nk = attn_fwd_kvcache_workspace_size(&p, 32, 16, (int32_t*)F, 128, 256, 0);
   CHECK(nk > 0);
@@ -139,9 +145,13 @@ static void forward_layouts() {
   CHECK(attn_fwd_kvcache(&p, 32, 16, F, F, F, (int32_t*)F, (int32_t*)F, 128, 256, 0, F, (float*)F, wk.data(), nk,
                          nullptr) == ATTN_OK);
   CHECK(stub::last_fwd.s.block_table == (const int32_t*)F && stub::last_fwd.s.page_rows == 256);
-  // packed: no workspace
+  // packed: no workspace; K/V read once only when every sequence fits one work tile
   CHECK(attn_fwd_varlen(&p, 64, 65536, 65536, (int32_t*)F, (int32_t*)F, 5636, 5636, F, F, F, F, (float*)F, nullptr, 0,
                         nullptr) == ATTN_OK);
+  CHECK(stub::last_fwd.kv_once == 0);
+  CHECK(attn_fwd_varlen(&p, 64, 1024, 65536, (int32_t*)F, (int32_t*)F, 16, 5636, F, F, F, F, (float*)F, nullptr, 0,
+                        nullptr) == ATTN_OK);
+  CHECK(stub::last_fwd.kv_once == 1);
 }
 
 static void backward_layouts(bool sinks, bool packed) {

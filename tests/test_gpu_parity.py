@@ -27,6 +27,9 @@ BATCHED = [
     ("two_sided_fp16", 1, 257, 190, 2, 2, 64, False, (20, 13), False, "fp16", True),
     ("sinks_fp16_full", 1, 100, 100, 2, 1, 128, False, (-1, -1), True, "fp16", True),
     ("split_kv_decode", 2, 3, 5000, 8, 2, 128, True, (-1, -1), True, "bf16", True),
+    # batched decode that does not split (15 key tiles): one work tile per
+    # (sequence, kv head), so the K/V tiles take the read-once path
+    ("decode_unsplit_read_once", 16, 2, 900, 32, 4, 128, True, (-1, -1), True, "bf16", True),
     # 16 q heads per kv head (8 queries fill a 128-row tile), left window only, no causal
     ("mqa_g16_left_window", 1, 96, 200, 16, 1, 64, False, (50, -1), True, "bf16", True),
     # right window only, no causal: keys up to 7 past the diagonal
