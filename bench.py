@@ -386,27 +386,24 @@ def run_variants(steps, warmup):
 
 
 def run_stream(steps, warmup):
-    """Practical HBM rates on this machine for the decode shape's bytes: torch's
-    own streaming kernels over 4.295 GB (the K and V of the decode shape) --
-    a sum (reads only), a copy (read + write) and an add (two reads, one
-    write) -- each repetition after the MALL flush, timed with HIP events.
-    A reference for the decode's K/V rate, not a kernel of this library."""
+    """Practical HBM read rates on this machine for the decode shape's bytes
+    (4.295 GB: the K and V of the decode shape), each repetition after the
+    MALL flush, timed with HIP events.  First the read probes of
+    libattn36_probe.so, which read K and V [32, 32768, 8, 128] in the split-KV
+    forward's order (workgroup = sequence, kv head and split, 64-key tiles)
+    with no arithmetic: global -> LDS DMA in a two-deep ring with the default
+    cache policy and with the non-temporal hint, and plain 16-byte register
+    loads with the hint.  Then torch's own streaming kernels over the same
+    bytes: a sum (reads only), a copy (read + write) and an add (two reads,
+    one write).  References for the decode's K/V rate, not kernels of the
+    attention library."""
+    import ctypes
     import torch
-    n = 2 * 32 * 32768 * 8 * 128  # elements of K and V, bf16
-    x = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    d = DECODE
     flush = Flusher()
     rows = []
-    for name, fn, nbytes in (
-            ("sum (read)", lambda: x.sum(dtype=torch.float32), 2 * n),
-            ("copy (read + write)", None, 4 * n),
-            ("add (2 reads + write)", None, 6 * n // 2)):
-        if name.startswith("copy"):
-            y = torch.empty_like(x)
-            fn = lambda: y.copy_(x)  # noqa: E731
-        elif name.startswith("add"):
-            a, b = x[: n // 2], x[n // 2:]
-            z = torch.empty_like(a)
-            fn = lambda: torch.add(a, b, out=z)  # noqa: E731
+
+    def emit(name, fn, nbytes):
         for _ in range(warmup):
             fn()
         st = summary(time_each(fn, steps, flush))
@@ -414,11 +411,46 @@ def run_stream(steps, warmup):
                      "GBps": round(nbytes / (st["median"] * 1e-3) / 1e9, 1),
                      "frac_of_8TBps": round(nbytes / (st["median"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         print(json.dumps(rows[-1]), flush=True)
-        if name.startswith("copy"):
-            del y
-        elif name.startswith("add"):
-            del z
-        torch.cuda.empty_cache()
+
+    probe_path = os.path.join(ROOT, "exact_attention_36_amd", "libattn36_probe.so")
+    if not os.path.exists(probe_path):
+        raise SystemExit("libattn36_probe.so is not built: run __graft_entry__.build() first")
+    probe = ctypes.CDLL(probe_path)
+    shape = (d["B"], d["SK"], d["HKV"], d["D"])
+    k = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_()
+    v = torch.empty(shape, dtype=torch.bfloat16, device="cuda").normal_()
+    kv_bytes = 2 * k.numel() * 2
+    ns = 2  # the split count the attention forward picks for this shape
+    sink = torch.empty(d["B"] * d["HKV"] * ns * 256 * 4, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError("read probe failed with code %d" % rc)
+
+    for name, fn in (
+            ("probe: DMA to LDS, default policy (K/V read)",
+             lambda: call(probe.probe_read_dma(ptr(k), ptr(v), d["B"], d["SK"], d["HKV"], ns, 0, ptr(sink), stream))),
+            ("probe: DMA to LDS, non-temporal (K/V read)",
+             lambda: call(probe.probe_read_dma(ptr(k), ptr(v), d["B"], d["SK"], d["HKV"], ns, 1, ptr(sink), stream))),
+            ("probe: register loads, non-temporal (K/V read)",
+             lambda: call(probe.probe_read_regs(ptr(k), ptr(v), d["B"], d["SK"], d["HKV"], ns, ptr(sink), stream)))):
+        emit(name, fn, kv_bytes)
+    del k, v, sink
+    torch.cuda.empty_cache()
+
+    n = 2 * d["B"] * d["SK"] * d["HKV"] * d["D"]  # elements of K and V, bf16
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    emit("torch sum (read)", lambda: x.sum(dtype=torch.float32), 2 * n)
+    y = torch.empty_like(x)
+    emit("torch copy (read + write)", lambda: y.copy_(x), 4 * n)
+    del y
+    a, b = x[: n // 2], x[n // 2:]
+    z = torch.empty_like(a)
+    emit("torch add (2 reads + write)", lambda: torch.add(a, b, out=z), 6 * n // 2)
+    del z, x
+    torch.cuda.empty_cache()
     return rows
 
 
@@ -906,7 +938,8 @@ def main():
                          "variants: causal prefill with soft cap / ALiBi / 4 sinks (one line each); "
                          "latency: launch-bound forward, eager calls vs HIP graph replays; "
                          "power: socket power and shader clock (amd-smi) under the step's kernels; "
-                         "stream: torch's own sum / copy / add over the decode shape's 4.3 GB (practical HBM rates); "
+                         "stream: read probes in the decode's access order and torch's sum / copy / add over the decode "
+                         "shape's 4.3 GB (practical HBM rates); "
                          "flush: calls timed warm, after the read flush and after a 512 MB write")
     ap.add_argument("--seconds", type=float, default=10.0, help="duration of each --workload power phase")
     ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=None,

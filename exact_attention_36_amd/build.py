@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libattn36.so")
+# the benchmark's HBM read-rate reference (not part of the attention library)
+PROBE_SOURCE = "read_probe.hip"
+PROBE_PATH = os.path.join(PKG, "libattn36_probe.so")
 SOURCES = ["attn_api.cpp", "attn_timing.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_cache.hip", "attn_noalloc.hip",
            # one translation unit per score variant, compiled in parallel
            "attn_fwd_cap.hip", "attn_fwd_alibi.hip", "attn_fwd_cap_alibi.hip",
@@ -44,8 +47,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     _run([HIPCC, *FLAGS, "-shared", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    tmp = PROBE_PATH + ".tmp%d" % os.getpid()
+    _run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp])
+    os.replace(tmp, PROBE_PATH)
     if verbose:
-        print("built", LIB_PATH)
+        print("built", LIB_PATH, "and", PROBE_PATH)
     return LIB_PATH
 
 
