@@ -13,8 +13,11 @@
 //                    without its arithmetic
 //   probe_read_regs: 16-byte loads into registers, each lane's loads of two
 //                    keys in flight, non-temporal hint, no LDS and no barrier
-// Each lane xors what it read into one 16-byte value written to `sink`, so the
-// loads cannot be dropped; sink holds 4096 bytes per workgroup.
+// Each lane xors what it read (the DMA kernel: its share of each tile's
+// chunks, read back from LDS) into one 16-byte value written to `sink`, so
+// the loads cannot be dropped and every byte of K and V enters the xor of all
+// of sink exactly once (a test checks that); sink holds 4096 bytes per
+// workgroup.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,7 +93,12 @@ __global__ __launch_bounds__(THREADS) void read_dma_kernel(const char* k, const 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t is in LDS
     __builtin_amdgcn_s_barrier();                       // and everyone is done with tile t-1's slot
     if (t + 1 < nt) issue(t + 1);
-    acc ^= *(const u32x4*)&ring[t & 1][(threadIdx.x >> 7) & 1][(threadIdx.x & 127) * 16];
+    // every 16-byte chunk of the tile's K and V, once over the workgroup
+#pragma unroll
+    for (int i = 0; i < 2 * TB / 16 / THREADS; i++) {
+      const int c = i * THREADS + threadIdx.x;
+      acc ^= *(const u32x4*)&ring[t & 1][c / (TB / 16)][(c % (TB / 16)) * 16];
+    }
   }
   sink[blockIdx.x * THREADS + threadIdx.x] = acc;
 }
