@@ -435,7 +435,8 @@ void bwd_dq_kernel(const BwdArgs a) {
 // has no such branch in its loop (it measured a few per cent slower on
 // causal-only problems).
 template <int D, bool F16, bool PAD, int EXT, bool WSKIP>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
+__global__ __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd_fwd_dkdv(D, EXT), waves_per_simd_fwd_dkdv(D, EXT))))
 void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int KS = D / 16, DB = D / 32, ROWB = D * 2;
   constexpr int BN = BWD_BN, BM = BWD_BM;

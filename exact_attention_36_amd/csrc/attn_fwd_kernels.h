@@ -45,7 +45,8 @@ namespace attn {
 // with the non-temporal hint; FWD_SHARED keeps the default cache policy for
 // tiles that several workgroups of a head read.
 template <int D, bool F16, bool PAD, int EXT, int PATH>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_simd(D), waves_per_simd(D))))
+__global__ __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd_fwd_dkdv(D, EXT), waves_per_simd_fwd_dkdv(D, EXT))))
 void fwd_kernel(const FwdArgs a) {
   constexpr bool SPLIT = PATH == FWD_SPLIT;
   constexpr bool KV_NT = PATH != FWD_SHARED;

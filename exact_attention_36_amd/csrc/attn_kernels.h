@@ -19,6 +19,13 @@ constexpr int THREADS = 256;    // 4 wave64s
 // up to 512 (the MFMA accumulators then sit in AGPRs) and whose K/V tiles
 // take 128 KB of LDS, one workgroup per CU.
 constexpr int waves_per_simd(int D) { return D > 128 ? 1 : 2; }
+// The forward and the dK/dV kernel at the 64 width without score variants
+// (EXT = 0): three (168 registers, 32-33 KB of LDS per workgroup).  Their
+// D <= 64 work leaves the softmax-side VALU a larger share than at 128, which
+// a third wave overlaps: causal B=4, H=16, S=2048 at D = 64 forward 51 vs
+// 54-58 us and dK/dV 85 vs 95-103 us.  The dQ kernel measured 8 % slower
+// there and stays at two, as do the variant instances (they would spill).
+constexpr int waves_per_simd_fwd_dkdv(int D, int EXT) { return D > 128 ? 1 : (D > 64 || EXT != 0) ? 2 : 3; }
 
 // Sequence geometry shared by all kernels.  Batched problems have
 // cu_q == nullptr: sequence b starts at token b*sq (queries) and b*sk (keys).
