@@ -215,6 +215,14 @@ def test_config5_decode_split_kv():
     _batched_case("cfg5", 5, 32, 16, 32768, 64, 8, 128, True, (-1, -1), False, False, 256, [(0, 0), (31, 7)], 0)
 
 
+def test_batched_decode_unsplit_read_once():
+    """The benchmark's batched decode (B=128, s_q=1, s_kv=8192, GQA 64/8, the
+    same seeded inputs): one work tile per (sequence, kv head), keys not
+    split, so the read-once forward instance streams K/V; 256 sampled rows
+    and 2 full (batch, kv group) slices."""
+    _batched_case("dec_b128", 6, 128, 1, 8192, 64, 8, 128, True, (-1, -1), False, False, 256, [(0, 0), (127, 7)], 0)
+
+
 def test_config4_packed_varlen():
     print("case cfg4", flush=True)
     w = synth.packed_workload(seed=4)
