@@ -334,7 +334,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   auto run = [&](int t0, int t1, auto MASK) {
     for (int t = t0; t < t1; t++) {
       wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
+      barrier_reads_done();  // tile t is in; everyone is done with tile t - 1, whose buffers load_tile refills
       if (t + 1 < t_end) load_tile(t + 1);
       tile(t, MASK);
     }
@@ -708,9 +708,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const int pb = pb_end - 1 - it;
     const int buf = it & 1;
     wait_vmcnt<0>();               // dO tile, row statistics (and V block) are in LDS
-    // the Q tile's LDS writes (and with ALiBi the per-row terms) are done
-    if constexpr (ALIBI || !F16) wait_lgkm0();
-    __builtin_amdgcn_s_barrier();  // everyone's writes visible; everyone is done with the previous step
+    // the Q tile's LDS writes (and with ALiBi the per-row terms) are done, and
+    // everyone's reads of the buffers do_fetch refills have returned
+    barrier_reads_done();  // everyone's writes visible; everyone is done with the previous step
     if (it + 1 < nsteps) do_fetch(pb - 1, buf ^ 1);  // buffers of the previous step, which everyone has left
     const char* qt = q_lds + buf * QTILE;
     const char* dot = do_lds + buf * QTILE;

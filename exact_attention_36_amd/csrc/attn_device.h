@@ -217,6 +217,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Barrier ahead of LDS that the workgroup refills right after it.  The
+// wave's own LDS reads must have returned first: the compiler may issue an
+// operand read before the barrier and schedule the MFMA that consumes it
+// after, and s_barrier does not wait for reads in flight, so without the
+// wait the DMA that another wave issues right after the barrier could
+// overwrite the buffer before such a read returns.  Loads from global memory
+// in flight (the DMA prefetches) are not waited for.
+__device__ __forceinline__ void barrier_reads_done() {
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+}
 
 // Instruction-scheduling hints (sched_group_barrier masks): the compiler
 // otherwise issues each LDS operand read right before the MFMA that consumes

@@ -249,7 +249,7 @@ void fwd_kernel(const FwdArgs a) {
   auto idle_step = [&](int t, f32x16 (&sn)[KB], auto NEXT) __attribute__((always_inline)) {
     if (t + NST - 1 < t_end) wait_vmcnt<2 * (NST - 2) * SLABS>();
     else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    barrier_reads_done();
     refill(t);
     if constexpr (decltype(NEXT)::value) {
       s_tile(kslot(t + 1), sn);
@@ -265,7 +265,7 @@ void fwd_kernel(const FwdArgs a) {
     constexpr bool last = decltype(LAST)::value;
     if (t + NST - 1 < t_end) wait_vmcnt<2 * (NST - 2) * SLABS>();
     else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // everyone's part is in; everyone is done with step t-1
+    barrier_reads_done();  // everyone's part is in; everyone is done with step t-1
     refill(t);
     if constexpr (EXT != 0) {  // variant logits, before the mask sets invisible keys to -inf
       const float base = ext_diag - (float)(t * FWD_BN);
@@ -422,7 +422,7 @@ void fwd_kernel(const FwdArgs a) {
   // O goes out through LDS so that every store writes whole rows: the wave
   // puts its 32 rows (swizzled like the K/V tiles) in its own 32-row region,
   // then each store instruction writes 1 KB of consecutive 16-byte chunks.
-  __builtin_amdgcn_s_barrier();  // all waves are done reading the K/V slots
+  barrier_reads_done();  // all waves are done reading the K/V slots
   char* const ost = smem + wave * 32 * ROWB;
 #pragma unroll
   for (int d = 0; d < DB; d++)

@@ -90,8 +90,9 @@ __global__ __launch_bounds__(THREADS) void read_dma_kernel(const char* k, const 
   u32x4 acc = {0, 0, 0, 0};
   if (nt > 0) issue(0);
   for (int t = 0; t < nt; t++) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile t is in LDS
-    __builtin_amdgcn_s_barrier();                       // and everyone is done with tile t-1's slot
+    // tile t is in LDS, and this wave's reads of tile t-1's slot have returned
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // everyone is done with tile t-1's slot, which issue() refills
     if (t + 1 < nt) issue(t + 1);
     // every 16-byte chunk of the tile's K and V, once over the workgroup
 #pragma unroll
