@@ -825,14 +825,16 @@ def run_configs(steps, warmup, only=None):
         return {n: (ms / reps) for n, (c, ms) in r.items()}
 
     def line(name, D, pairs, tf, tb=None, kv_bytes=None):
-        f = tf["fwd"] + tf["fwd_combine"]
+        # packed calls may first build their grids' schedule tables ("order")
+        f = tf["fwd"] + tf["fwd_combine"] + tf.get("order", 0.0)
         r = {"workload": name, "fwd_ms": round(f, 4), "fwd_tflops": round(4.0 * D * pairs / (f * 1e-3) / 1e12, 1)}
         if kv_bytes:
             r["kv_GBps"] = round(kv_bytes / (f * 1e-3) / 1e9, 1)
         if tb:
-            b = tb["bwd_dsink"] + tb["bwd_dq"] + tb["bwd_dkdv"]
+            b = tb["bwd_dsink"] + tb["bwd_dq"] + tb["bwd_dkdv"] + tb.get("order", 0.0)
             r.update(bwd_ms=round(b, 4), dq_ms=round(tb["bwd_dq"], 4), dkdv_ms=round(tb["bwd_dkdv"], 4),
-                     dsink_ms=round(tb["bwd_dsink"], 4), bwd_tflops=round(10.0 * D * pairs / (b * 1e-3) / 1e12, 1),
+                     dsink_ms=round(tb["bwd_dsink"], 4), order_ms=round(tf.get("order", 0.0) + tb.get("order", 0.0), 4),
+                     bwd_tflops=round(10.0 * D * pairs / (b * 1e-3) / 1e12, 1),
                      fwdbwd_tflops=round(14.0 * D * pairs / ((f + b) * 1e-3) / 1e12, 1))
         print(json.dumps(r), flush=True)
 

@@ -26,7 +26,7 @@ EXPORTED = (
     "attn_bwd_varlen_workspace_size", "attn_last_error", "attn_version", "attn_timing_enable", "attn_timing_select",
     "attn_timing_read",
 )
-KERNELS = ("fwd", "fwd_combine", "bwd_dsink", "bwd_dq", "bwd_dkdv")
+KERNELS = ("fwd", "fwd_combine", "bwd_dsink", "bwd_dq", "bwd_dkdv", "order")
 
 
 class AttnError(RuntimeError):

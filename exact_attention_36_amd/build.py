@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG, "libattn36.so")
 PROBE_SOURCE = "read_probe.hip"
 PROBE_PATH = os.path.join(PKG, "libattn36_probe.so")
 SOURCES = ["attn_api.cpp", "attn_timing.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_cache.hip", "attn_noalloc.hip",
+           "attn_sched.hip",
            # one translation unit per score variant, compiled in parallel
            "attn_fwd_cap.hip", "attn_fwd_alibi.hip", "attn_fwd_cap_alibi.hip",
            "attn_bwd_cap.hip", "attn_bwd_alibi.hip", "attn_bwd_cap_alibi.hip"]

@@ -155,16 +155,33 @@ int64_t dq_blocks(const attn_params* p, bool packed, int64_t nseq, int64_t sq, i
   return packed ? (total_q * G) / BWD_QBM + nseq : nseq * cdiv(sq * G, BWD_QBM);
 }
 
+// The packed backward's grids run in the order of schedule tables built on
+// the device before them (attn_sched.hip, one extra launch) when the dK/dV
+// grid has at least ORDER_MIN_CTAS workgroups (four rounds of two per CU) and
+// some sequence may be ORDER_MIN_LEN queries long or more: then the work of
+// its key blocks ranges widely and the layout order can leave whole XCDs
+// running a few long blocks at the end.  Smaller grids finish in a round or
+// two anyway, and batches of short sequences have no long blocks.
+constexpr int64_t ORDER_MIN_CTAS = 2048;
+constexpr int64_t ORDER_MIN_LEN = 1024;
+bool use_order(const attn_params* p, int64_t nblk_k, int64_t nblk_q, int64_t nseq, int64_t max_q) {
+  return nblk_k * p->heads_kv >= ORDER_MIN_CTAS && max_q >= ORDER_MIN_LEN && nblk_k <= ORDER_MAX_BLOCKS &&
+         nblk_q <= ORDER_MAX_BLOCKS && nseq <= ORDER_MAX_SEQS;
+}
+
 // Backward workspace: D_i and the sink-adjusted log-sum-exp, laid out like
 // lse; each dQ workgroup's largest row norm of dO and largest |D_i|
 // ([Hkv][blocks][2]), from which the dK/dV kernel scales dS into fp16's
 // range; with sinks, each dQ workgroup's sums of the sink gradient per q head
 // of its group ([Hkv][blocks][G]), which a last kernel adds up in a fixed
-// order.
+// order; for packed calls, the schedule tables of the dQ and dK/dV grids
+// (nblk_k: key blocks per kv head, 0 when batched; nseq: the sequences;
+// max_q: the bound on their query counts).
 struct BwdWs {
-  size_t delta, lse2, dscale_part, dsink_part, total;
+  size_t delta, lse2, dscale_part, dsink_part, order_q, order_k, total;
 };
-BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) {
+BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int64_t nblk_k, int64_t nseq, int64_t max_q,
+             int32_t grad_dtype) {
   (void)grad_dtype;
   BwdWs w{};
   const int64_t rows = tq * p->heads_q;
@@ -172,7 +189,11 @@ BwdWs bwd_ws(const attn_params* p, int64_t tq, int64_t nbq, int32_t grad_dtype) 
   w.lse2 = align_up(rows * 4);
   w.dscale_part = align_up(nbq * p->heads_kv * 2 * 4);
   w.dsink_part = p->sinks ? align_up(nbq * p->heads_q * 4) : 0;  // Hkv * nbq * G = nbq * Hq
-  w.total = w.delta + w.lse2 + w.dscale_part + w.dsink_part;
+  if (nblk_k > 0 && use_order(p, nblk_k, nbq, nseq, max_q)) {
+    w.order_q = align_up(nbq * p->heads_kv * 4);
+    w.order_k = align_up(nblk_k * p->heads_kv * 4);
+  }
+  w.total = w.delta + w.lse2 + w.dscale_part + w.dsink_part + w.order_q + w.order_k;
   return w;
 }
 
@@ -251,7 +272,7 @@ attn_status run_fwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
 }
 
 attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, int64_t sq,
-                    int64_t sk, int64_t total_q, int64_t total_k, const void* q, const void* k, const void* v,
+                    int64_t sk, int64_t total_q, int64_t total_k, int64_t max_q, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dsinks,
                     int32_t grad_dtype, void* ws, size_t ws_bytes, void* stream) {
   const bool packed = cu_q != nullptr;
@@ -262,7 +283,7 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   if (tq * p->heads_q >= ((int64_t)1 << 29))
     return fail(ATTN_ENOTSUP, "%lld query rows x %d q heads exceed the backward's 2^29 row-statistics limit",
                 (long long)tq, p->heads_q);
-  const BwdWs w = bwd_ws(p, tq, nbq, grad_dtype);
+  const BwdWs w = bwd_ws(p, tq, nbq, packed ? total_k / BWD_BN + nseq : 0, nseq, max_q, grad_dtype);
   attn_status st = check_ws(ws, ws_bytes, w.total);
   if (st != ATTN_OK) return st;
   BwdArgs a{};
@@ -287,6 +308,10 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
   a.dscale_part = (float*)wp;
   wp += w.dscale_part;
   a.dsink_part = w.dsink_part ? (float*)wp : nullptr;
+  wp += w.dsink_part;
+  int32_t* const order_q = w.order_q ? (int32_t*)wp : nullptr;
+  wp += w.order_q;
+  int32_t* const order_k = w.order_k ? (int32_t*)wp : nullptr;
   a.nbq = (int32_t)nbq;
   const float scale = resolve_scale(p);
   a.scale = scale;
@@ -301,6 +326,18 @@ attn_status run_bwd(const attn_params* p, const int32_t* cu_q, const int32_t* cu
     if (ctas >= INT32_MAX || ctas_q >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.total_ctas = total_k > 0 ? (int32_t)ctas : 0;
     a.total_ctas_q = total_q > 0 ? (int32_t)ctas_q : 0;
+    // schedule tables (nblk_q == nbq, so the workspace sized them for these grids)
+    OrderArgs og[2];
+    int no = 0;
+    if (order_q && a.total_ctas_q > 0) {
+      og[no++] = OrderArgs{a.s, a.nblk_q, 0, BWD_QBM, order_q};
+      a.order_q = order_q;
+    }
+    if (order_k && a.total_ctas > 0) {
+      og[no++] = OrderArgs{a.s, a.nblk, 1, BWD_BN, order_k};
+      a.order_k = order_k;
+    }
+    if (no > 0 && (st = launched(launch_order(og, no, (hipStream_t)stream))) != ATTN_OK) return st;
   } else {
     if ((int64_t)p->heads_kv * nseq >= INT32_MAX) return fail(ATTN_ENOTSUP, "grid too large");
     a.nkb = (int32_t)cdiv(sk, BWD_BN);
@@ -337,7 +374,7 @@ size_t attn_bwd_workspace_size(const attn_params* p, int64_t batch, int64_t seql
                                int32_t grad_dtype) {
   (void)seqlen_k;
   if (check_params(p) != ATTN_OK || batch < 1 || seqlen_q < 1) return 0;
-  return bwd_ws(p, batch * seqlen_q, dq_blocks(p, false, batch, seqlen_q, 0), grad_dtype).total;
+  return bwd_ws(p, batch * seqlen_q, dq_blocks(p, false, batch, seqlen_q, 0), 0, batch, seqlen_q, grad_dtype).total;
 }
 
 // Bound on a KV-cache call's keys per slot: the slot capacity, or the pages
@@ -473,11 +510,11 @@ size_t attn_fwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, in
 
 size_t attn_bwd_varlen_workspace_size(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
                                       int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t grad_dtype) {
-  (void)total_k;
-  (void)max_seqlen_q;
   (void)max_seqlen_k;
   if (check_params(p) != ATTN_OK || total_q < 0 || num_seqs < 0) return 0;
-  return bwd_ws(p, total_q, dq_blocks(p, true, num_seqs, 0, total_q), grad_dtype).total;
+  if (total_k < 0) return 0;
+  return bwd_ws(p, total_q, dq_blocks(p, true, num_seqs, 0, total_q), total_k / BWD_BN + num_seqs, num_seqs,
+                max_seqlen_q, grad_dtype).total;
 }
 
 attn_status attn_fwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
@@ -519,15 +556,17 @@ attn_status attn_bwd_noalloc(const attn_params* p, int64_t batch, int64_t seqlen
                              void* stream) {
   attn_status st = check_bwd(p, batch, seqlen_q, seqlen_k, q, k, v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype);
   if (st != ATTN_OK) return st;
-  const size_t need = bwd_ws(p, batch * seqlen_q, dq_blocks(p, false, batch, seqlen_q, 0), grad_dtype).total;
+  const size_t need =
+      bwd_ws(p, batch * seqlen_q, dq_blocks(p, false, batch, seqlen_q, 0), 0, batch, seqlen_q, grad_dtype).total;
   if (need > ATTN_NOALLOC_SCRATCH_BYTES)
     return fail(ATTN_ENOTSUP, "attn_bwd_noalloc: this call needs %zu bytes of workspace, more than the %zu bytes "
                 "of fixed scratch (use attn_bwd with a workspace)", need, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
   const hipError_t e = noalloc_scratch(&ws);
   if (e != hipSuccess) return fail(ATTN_EHIP, "attn_bwd_noalloc: scratch lookup failed: %s", hipGetErrorString(e));
-  return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k, q, k,
-                 v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ATTN_NOALLOC_SCRATCH_BYTES, stream);
+  return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k,
+                 seqlen_q, q, k, v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ATTN_NOALLOC_SCRATCH_BYTES,
+                 stream);
 }
 
 attn_status attn_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int64_t seqlen_k, const void* q,
@@ -537,8 +576,8 @@ attn_status attn_bwd(const attn_params* p, int64_t batch, int64_t seqlen_q, int6
   const attn_status st =
       check_bwd(p, batch, seqlen_q, seqlen_k, q, k, v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype);
   if (st != ATTN_OK) return st;
-  return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k, q, k,
-                 v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ws_bytes, stream);
+  return run_bwd(p, nullptr, nullptr, (int32_t)batch, seqlen_q, seqlen_k, batch * seqlen_q, batch * seqlen_k,
+                 seqlen_q, q, k, v, o, lse, dout, dq, dk, dv, dsinks, grad_dtype, ws, ws_bytes, stream);
 }
 
 static attn_status check_varlen(const attn_params* p, int32_t num_seqs, int64_t total_q, int64_t total_k,
@@ -582,7 +621,7 @@ attn_status attn_bwd_varlen(const attn_params* p, int32_t num_seqs, int64_t tota
   if ((total_q > 0 && (!q || !o || !lse || !dout || !dq)) || (total_k > 0 && (!k || !v || !dk || !dv)))
     return fail(ATTN_EINVAL, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
   if (p->sinks && !dsinks) return fail(ATTN_EINVAL, "dsinks must be non-NULL when sinks are given");
-  return run_bwd(p, cu_q, cu_k, num_seqs, 0, 0, total_q, total_k, q, k, v, o, lse, dout, dq, dk, dv, dsinks,
+  return run_bwd(p, cu_q, cu_k, num_seqs, 0, 0, total_q, total_k, max_q, q, k, v, o, lse, dout, dq, dk, dv, dsinks,
                  grad_dtype, ws, ws_bytes, stream);
 }
 

@@ -71,7 +71,7 @@ void bwd_dq_kernel(const BwdArgs a) {
   const int G = a.s.group;
   int seq, g, mb, blk;  // blk: this workgroup's index among its kv head's dQ workgroups
   if (a.s.cu_q) {
-    const int id = xcd_remap(blockIdx.x, a.total_ctas_q);
+    const int id = a.order_q ? a.order_q[blockIdx.x] : xcd_remap(blockIdx.x, a.total_ctas_q);
     g = id / a.nblk_q;
     blk = id - g * a.nblk_q;
     seq = find_sequence(a.s.cu_q, a.s.nseq, blk, G, BM);
@@ -460,7 +460,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   int seq, g, nb;
   if (a.s.cu_q) {
-    const int id = xcd_remap(blockIdx.x, a.total_ctas);
+    const int id = a.order_k ? a.order_k[blockIdx.x] : xcd_remap(blockIdx.x, a.total_ctas);
     g = id / a.nblk;
     const int t = id - g * a.nblk;
     seq = find_sequence(a.s.cu_k, a.s.nseq, t, 1, BN);

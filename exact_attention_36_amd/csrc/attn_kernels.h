@@ -117,12 +117,34 @@ struct BwdArgs {
   int32_t nmb;            // query blocks per (sequence, kv head) in batched mode
   int32_t nblk_q;         // linear query blocks per kv head in packed mode
   int32_t total_ctas_q;
+  // packed mode: dispatch slot -> block id of the dQ and dK/dV grids
+  // (schedule tables), or nullptr
+  const int32_t* order_q;
+  const int32_t* order_k;
 };
 constexpr int BWD_QBM = 128;    // packed query rows per dQ workgroup
 
+// Dispatch order of a packed grid (attn_sched.hip).  Block t of kv head g is
+// logical id g * nblk + t; order[slot] is the id that dispatch slot `slot`
+// runs.  The table lists the blocks by their estimated work, largest first
+// (the heads of one block next to each other), so that the longest blocks
+// of the batch start first wherever their sequences sit in it.
+struct OrderArgs {
+  SeqArgs s;
+  int32_t nblk;       // linear blocks per kv head
+  int32_t key_major;  // blocks of BWD_BN keys (dK/dV grid) instead of bm packed query rows
+  int32_t bm;         // packed query rows per block (query-major grids)
+  int32_t* order;     // [hkv * nblk]
+};
+// Grids that get a schedule table: up to ORDER_MAX_BLOCKS blocks per kv head
+// and ORDER_MAX_SEQS sequences (the one workgroup that builds it keeps a byte
+// per block and four words per sequence in LDS).
+constexpr int ORDER_MAX_BLOCKS = 16384;
+constexpr int ORDER_MAX_SEQS = 8191;
+
 // Optional per-launch timing (attn_timing_enable): the launchers call these
 // around every kernel launch; they record HIP events only while enabled.
-enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_DSINK, K_BWD_DQ, K_BWD_DKDV, K_COUNT };
+enum KernelId { K_FWD = 0, K_FWD_COMBINE, K_BWD_DSINK, K_BWD_DQ, K_BWD_DKDV, K_ORDER, K_COUNT };
 void timing_begin(int kid, hipStream_t st);
 void timing_end(int kid, hipStream_t st);
 
@@ -150,6 +172,8 @@ struct AppendArgs {
 hipError_t launch_fwd(const FwdArgs& a, int tile_d, bool f16, hipStream_t st);
 hipError_t launch_fwd_combine(const FwdArgs& a, int tile_d, bool f16, hipStream_t st);
 hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool f16, hipStream_t st);
+// Builds the schedule tables of n (1 or 2) packed grids, one workgroup each.
+hipError_t launch_order(const OrderArgs* grids, int n, hipStream_t st);
 hipError_t launch_rotary(const void* x, void* out, int64_t rows, int S, int H, int D, const int32_t* pos0,
                          int per_token, const RotaryArgs& r, bool f16, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, int32_t* seqlens_out, bool f16, hipStream_t st);

@@ -267,7 +267,13 @@ attn_status attn_rotary(const attn_params *params, int64_t batch, int64_t seqlen
  * Forward, packed [T,H,D] with device int32 cu_seqlens_q/k [num_seqs+1].
  * total_q / total_k are the token counts (cu_seqlens_*[num_seqs]);
  * max_seqlen_q / max_seqlen_k bound every sequence's length.  lse is fp32
- * [Hq, total_q].
+ * [Hq, total_q].  A packed grid of 2048 workgroups or more (at most 16384
+ * blocks per kv head, 8191 sequences) first builds, in the workspace, a
+ * table that orders its blocks by their work under the mask, largest first,
+ * so that the longest blocks of the batch start first wherever their
+ * sequences sit in it (a short extra launch; the results do not depend on
+ * the order).  attn_fwd_varlen_workspace_size is then the table's size
+ * (4 bytes per workgroup), else 0.
  */
 attn_status attn_fwd_varlen(const attn_params *params, int32_t num_seqs, int64_t total_q,
                             int64_t total_k, const int32_t *cu_seqlens_q,
@@ -281,6 +287,8 @@ size_t attn_fwd_varlen_workspace_size(const attn_params *params, int32_t num_seq
 /*
  * Backward, packed.  Same arguments as attn_fwd_varlen plus o, lse (fp32
  * [Hq, total_q]), dout, and the outputs dq, dk, dv, dsinks as in attn_bwd.
+ * The dQ and the dK/dV grids each get a schedule table in the workspace by
+ * the same rule as the packed forward's.
  */
 attn_status attn_bwd_varlen(const attn_params *params, int32_t num_seqs, int64_t total_q,
                             int64_t total_k, const int32_t *cu_seqlens_q,
@@ -313,7 +321,8 @@ typedef enum {
     ATTN_KERNEL_BWD_DSINK = 2,    /* sums the dQ workgroups' sink-gradient partials into dsinks */
     ATTN_KERNEL_BWD_DQ = 3,       /* query-major backward: row statistics, dsinks, dQ */
     ATTN_KERNEL_BWD_DKDV = 4,     /* key-major backward: dK, dV */
-    ATTN_KERNEL_COUNT = 5
+    ATTN_KERNEL_ORDER = 5,        /* packed calls: the grids' dispatch-order tables */
+    ATTN_KERNEL_COUNT = 6
 } attn_kernel_id;
 attn_status attn_timing_enable(int32_t on);
 attn_status attn_timing_select(uint32_t kernel_mask);

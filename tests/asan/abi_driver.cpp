@@ -15,7 +15,9 @@
 namespace stub {
 extern attn::FwdArgs last_fwd;
 extern attn::BwdArgs last_bwd;
-extern int fwd_calls, combine_calls, bwd_calls, append_calls, rotary_calls;
+extern attn::OrderArgs last_order[2];
+extern int last_order_n;
+extern int fwd_calls, combine_calls, bwd_calls, append_calls, rotary_calls, order_calls;
 extern int last_tile_d;
 }  // namespace stub
 
@@ -146,6 +148,7 @@ static void forward_layouts() {
                          nullptr) == ATTN_OK);
   CHECK(stub::last_fwd.s.block_table == (const int32_t*)F && stub::last_fwd.s.page_rows == 256);
   // packed: no workspace; K/V read once only when every sequence fits one work tile
+  CHECK(attn_fwd_varlen_workspace_size(&p, 64, 65536, 65536, 5636, 5636) == 0);
   CHECK(attn_fwd_varlen(&p, 64, 65536, 65536, (int32_t*)F, (int32_t*)F, 5636, 5636, F, F, F, F, (float*)F, nullptr, 0,
                         nullptr) == ATTN_OK);
   CHECK(stub::last_fwd.kv_once == 0);
@@ -158,7 +161,7 @@ static void backward_layouts(bool sinks, bool packed) {
   attn_params p = params(32, 8, 128);
   float fake_sinks = 0.f;
   if (sinks) p.sinks = &fake_sinks;  // never read on the host
-  const int64_t B = 2, S = 8192, T = B * S;
+  const int64_t B = 2, S = 8192, T = packed ? 65536 : B * S;
   const size_t n = packed ? attn_bwd_varlen_workspace_size(&p, 64, T, T, 5000, 5000, ATTN_BF16)
                           : attn_bwd_workspace_size(&p, B, S, S, ATTN_BF16);
   CHECK(n > 0);
@@ -178,7 +181,29 @@ static void backward_layouts(bool sinks, bool packed) {
                            {"dscale_part", (const char*)a.dscale_part, (size_t)a.nbq * 8 * 2 * 4}};
   if (sinks) r.push_back({"dsink_part", (const char*)a.dsink_part, (size_t)a.nbq * 32 * 4});
   else CHECK(a.dsink_part == nullptr);
+  if (packed) {
+    // a dK/dV grid of 576 blocks x 8 kv heads with sequences of up to 5000
+    // queries: both grids run in the order of schedule tables, built by one
+    // launch before them
+    CHECK(a.order_q != nullptr && a.order_k != nullptr);
+    CHECK(stub::last_order_n == 2 && stub::last_order[0].order == a.order_q && !stub::last_order[0].key_major &&
+          stub::last_order[0].nblk == a.nblk_q && stub::last_order[1].order == a.order_k &&
+          stub::last_order[1].key_major && stub::last_order[1].nblk == a.nblk);
+    r.push_back({"order_q", (const char*)a.order_q, (size_t)a.nblk_q * 8 * 4});
+    r.push_back({"order_k", (const char*)a.order_k, (size_t)a.nblk * 8 * 4});
+  } else {
+    CHECK(a.order_q == nullptr && a.order_k == nullptr);
+  }
   CHECK(regions_ok(r, ws.data(), n));
+  if (packed) {
+    // sequences of at most 1000 queries: no tables, a smaller workspace
+    const size_t n2 = attn_bwd_varlen_workspace_size(&p, 64, T, T, 1000, 1000, ATTN_BF16);
+    CHECK(n2 < n);
+    const int oc = stub::order_calls;
+    CHECK(attn_bwd_varlen(&p, 64, T, T, (int32_t*)F, (int32_t*)F, 1000, 1000, F, F, F, F, (float*)F, F, F, F, F,
+                          sinks ? (float*)F : nullptr, ATTN_BF16, ws.data(), n2, nullptr) == ATTN_OK);
+    CHECK(stub::order_calls == oc && stub::last_bwd.order_q == nullptr && stub::last_bwd.order_k == nullptr);
+  }
   // the dQ grid covers the workgroups the slots are indexed by
   CHECK(a.total_ctas_q >= a.nbq * 8 || !packed);
   // too small a workspace is refused

@@ -7,7 +7,9 @@
 namespace stub {
 attn::FwdArgs last_fwd;
 attn::BwdArgs last_bwd;
-int fwd_calls = 0, combine_calls = 0, bwd_calls = 0, append_calls = 0, rotary_calls = 0;
+attn::OrderArgs last_order[2];
+int last_order_n = 0;
+int fwd_calls = 0, combine_calls = 0, bwd_calls = 0, append_calls = 0, rotary_calls = 0, order_calls = 0;
 int last_tile_d = 0;
 }  // namespace stub
 
@@ -27,6 +29,12 @@ hipError_t launch_bwd(const BwdArgs& a, int tile_d, bool, hipStream_t) {
   stub::last_bwd = a;
   stub::last_tile_d = tile_d;
   stub::bwd_calls++;
+  return hipSuccess;
+}
+hipError_t launch_order(const OrderArgs* grids, int n, hipStream_t) {
+  for (int i = 0; i < n; i++) stub::last_order[i] = grids[i];
+  stub::last_order_n = n;
+  stub::order_calls++;
   return hipSuccess;
 }
 hipError_t launch_rotary(const void*, void*, int64_t, int, int, int, const int32_t*, int, const RotaryArgs&, bool,

@@ -167,6 +167,49 @@ def test_varlen_equals_batched_calls():
         assert torch.equal(lse[:, a:b], lb[0]), s
 
 
+def test_packed_schedule_tables_bitwise():
+    """A packed batch large enough that its backward grids run in the order
+    of the device-built schedule tables (longest blocks first: a dK/dV grid of
+    2048 workgroups or more, a sequence of 1024 queries or more): every
+    sequence's forward and backward equal a packed call on that sequence
+    alone, whose grids are under the threshold and keep the layout order, bit
+    for bit, and a second call on the batch repeats the first.  A block the
+    tables missed would leave its rows unwritten.  (Packed calls never split
+    the keys, so the two sides run the same kernels.)"""
+    lens = [3000, 0, 17, 5000, 128, 1, 2500, 640, 0, 4095, 33, 1200, 2000, 300, 999, 4000, 666]
+    lens.append(32768 - sum(lens))  # a long last sequence (8189)
+    hq, hkv, d = 16, 8, 64  # dQ grid 32768*2/128+18 = 530 blocks x 8, dK/dV grid 274 x 8
+    inp = synth.varlen_inputs(11, lens, lens, hq, hkv, d, grads=True)
+    q, k, v, do = (dev_tensor(inp[n]) for n in ("q", "k", "v", "dout"))
+    cq = torch.from_numpy(inp["cu_q"]).cuda()
+    print("case packed_schedule", lens, flush=True)
+    outs = []
+    for _ in range(2):
+        o, lse = ea.attn_fwd_varlen(q, k, v, cq, cq, max(lens), max(lens), causal=True)
+        dq, dk, dv, _ = ea.attn_bwd_varlen(q, k, v, o, lse, do, cq, cq, max(lens), max(lens), causal=True,
+                                           grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs.append((o, lse, dq, dk, dv))
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x, y)
+    o, lse, dq, dk, dv = outs[0]
+    for s, L in enumerate(lens):
+        if L == 0:
+            continue
+        a, b = int(inp["cu_q"][s]), int(inp["cu_q"][s + 1])
+        sl = lambda t: t[a:b].contiguous()  # noqa: E731
+        c1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        ob, lb = ea.attn_fwd_varlen(sl(q), sl(k), sl(v), c1, c1, L, L, causal=True)
+        dqb, dkb, dvb, _ = ea.attn_bwd_varlen(sl(q), sl(k), sl(v), ob, lb, sl(do), c1, c1, L, L, causal=True,
+                                              grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], ob), s
+        assert torch.equal(lse[:, a:b], lb), s
+        assert torch.equal(dq[a:b], dqb), s
+        assert torch.equal(dk[a:b], dkb), s
+        assert torch.equal(dv[a:b], dvb), s
+
+
 RANGE = [
     # id, multipliers of q, k, v, dout (mq * mk = 1 keeps every score, hence P, unchanged)
     ("q_x1e3_k_x1e-3", 1e3, 1e-3, 1.0, 1.0),
