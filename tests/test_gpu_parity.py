@@ -167,7 +167,17 @@ def test_varlen_equals_batched_calls():
         assert torch.equal(lse[:, a:b], lb[0]), s
 
 
-def test_packed_schedule_tables_bitwise():
+SCHEDULE = [
+    # id, causal, window, sinks, seqused
+    ("causal", True, (-1, -1), False, False),
+    ("causal_window_sinks", True, (700, 0), True, False),
+    ("two_sided_window", False, (300, 40), False, False),
+    ("causal_seqused", True, (-1, -1), False, True),
+]
+
+
+@pytest.mark.parametrize("case", SCHEDULE, ids=[c[0] for c in SCHEDULE])
+def test_packed_schedule_tables_bitwise(case):
     """A packed batch large enough that its backward grids run in the order
     of the device-built schedule tables (longest blocks first: a dK/dV grid of
     2048 workgroups or more, a sequence of 1024 queries or more): every
@@ -175,39 +185,66 @@ def test_packed_schedule_tables_bitwise():
     alone, whose grids are under the threshold and keep the layout order, bit
     for bit, and a second call on the batch repeats the first.  A block the
     tables missed would leave its rows unwritten.  (Packed calls never split
-    the keys, so the two sides run the same kernels.)"""
+    the keys, so the two sides run the same kernels.)  With sinks, the
+    batch's d(sink) is the sum of the sequences' (to rounding: the order of
+    the sum differs)."""
+    name, causal, window, sinks, seqused = case
     lens = [3000, 0, 17, 5000, 128, 1, 2500, 640, 0, 4095, 33, 1200, 2000, 300, 999, 4000, 666]
     lens.append(32768 - sum(lens))  # a long last sequence (8189)
     hq, hkv, d = 16, 8, 64  # dQ grid 32768*2/128+18 = 530 blocks x 8, dK/dV grid 274 x 8
     inp = synth.varlen_inputs(11, lens, lens, hq, hkv, d, grads=True)
     q, k, v, do = (dev_tensor(inp[n]) for n in ("q", "k", "v", "dout"))
     cq = torch.from_numpy(inp["cu_q"]).cuda()
-    print("case packed_schedule", lens, flush=True)
+    sk = torch.from_numpy(np.random.default_rng(12).standard_normal(hq).astype(np.float32)).cuda() if sinks else None
+    used = None
+    if seqused:  # every other sequence uses part of its slot
+        used = [L if i % 2 else (L * 3) // 4 for i, L in enumerate(lens)]
+    uq = torch.tensor(used, dtype=torch.int32, device="cuda") if seqused else None
+    kw = dict(causal=causal, window=window, sinks=sk)
+    print("case packed_schedule", name, lens, used, flush=True)
     outs = []
     for _ in range(2):
-        o, lse = ea.attn_fwd_varlen(q, k, v, cq, cq, max(lens), max(lens), causal=True)
-        dq, dk, dv, _ = ea.attn_bwd_varlen(q, k, v, o, lse, do, cq, cq, max(lens), max(lens), causal=True,
-                                           grad_dtype=torch.float32)
+        o, lse = ea.attn_fwd_varlen(q, k, v, cq, cq, max(lens), max(lens), seqused_q=uq, seqused_k=uq, **kw)
+        dq, dk, dv, ds = ea.attn_bwd_varlen(q, k, v, o, lse, do, cq, cq, max(lens), max(lens), seqused_q=uq,
+                                            seqused_k=uq, grad_dtype=torch.float32, **kw)
         torch.cuda.synchronize()
-        outs.append((o, lse, dq, dk, dv))
-    for x, y in zip(outs[0], outs[1]):
-        assert torch.equal(x, y)
-    o, lse, dq, dk, dv = outs[0]
-    for s, L in enumerate(lens):
+        outs.append((o, lse, dq, dk, dv, ds))
+    rows = torch.ones(q.shape[0], dtype=torch.bool, device="cuda")  # query rows the call writes
+    if seqused:
+        for s_, L in enumerate(lens):
+            a = int(inp["cu_q"][s_])
+            rows[a + used[s_]:a + L] = False
+    for i, (x, y) in enumerate(zip(outs[0][:5], outs[1][:5])):
+        if i in (0, 2):  # o, dq: rows past the used lengths are unspecified
+            x, y = x[rows], y[rows]
+        elif i == 1:
+            x, y = x[:, rows], y[:, rows]
+        assert torch.equal(x, y), i
+    if sinks:
+        assert torch.equal(outs[0][5], outs[1][5])
+    o, lse, dq, dk, dv, ds = outs[0]
+    ds_sum = torch.zeros(hq, dtype=torch.float64, device="cuda")
+    for s_, L in enumerate(lens):
         if L == 0:
             continue
-        a, b = int(inp["cu_q"][s]), int(inp["cu_q"][s + 1])
+        a, b = int(inp["cu_q"][s_]), int(inp["cu_q"][s_ + 1])
         sl = lambda t: t[a:b].contiguous()  # noqa: E731
         c1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
-        ob, lb = ea.attn_fwd_varlen(sl(q), sl(k), sl(v), c1, c1, L, L, causal=True)
-        dqb, dkb, dvb, _ = ea.attn_bwd_varlen(sl(q), sl(k), sl(v), ob, lb, sl(do), c1, c1, L, L, causal=True,
-                                              grad_dtype=torch.float32)
+        u1 = torch.tensor([used[s_]], dtype=torch.int32, device="cuda") if seqused else None
+        ob, lb = ea.attn_fwd_varlen(sl(q), sl(k), sl(v), c1, c1, L, L, seqused_q=u1, seqused_k=u1, **kw)
+        dqb, dkb, dvb, dsb = ea.attn_bwd_varlen(sl(q), sl(k), sl(v), ob, lb, sl(do), c1, c1, L, L, seqused_q=u1,
+                                                seqused_k=u1, grad_dtype=torch.float32, **kw)
         torch.cuda.synchronize()
-        assert torch.equal(o[a:b], ob), s
-        assert torch.equal(lse[:, a:b], lb), s
-        assert torch.equal(dq[a:b], dqb), s
-        assert torch.equal(dk[a:b], dkb), s
-        assert torch.equal(dv[a:b], dvb), s
+        n = used[s_] if seqused else L
+        assert torch.equal(o[a:a + n], ob[:n]), s_
+        assert torch.equal(lse[:, a:a + n], lb[:, :n]), s_
+        assert torch.equal(dq[a:a + n], dqb[:n]), s_
+        assert torch.equal(dk[a:b], dkb), s_
+        assert torch.equal(dv[a:b], dvb), s_
+        if sinks:
+            ds_sum += dsb.double()
+    if sinks:
+        assert torch.allclose(ds.double(), ds_sum, rtol=1e-4, atol=1e-4), (ds, ds_sum)
 
 
 RANGE = [
