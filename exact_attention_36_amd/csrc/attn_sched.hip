@@ -62,7 +62,7 @@ __global__ __launch_bounds__(ORDER_THREADS) void packed_order_kernel(const Order
   // [class][counter]: counts, then offsets; before that, per sequence: its
   // first block and its lengths (the sequence table of step 1)
   __shared__ uint32_t cnt[ORDER_CLASSES * ORDER_COUNTERS];
-  __shared__ uint32_t part[ORDER_THREADS];
+  __shared__ uint32_t part[ORDER_THREADS / 64];  // the waves' running totals
   const int t = threadIdx.x, n = a.nblk, nseq = a.s.nseq;
   // 1. every block's work class: the sequences' first blocks and lengths
   // into LDS (one thread per sequence), then every block finds its sequence
@@ -117,15 +117,21 @@ __global__ __launch_bounds__(ORDER_THREADS) void packed_order_kernel(const Order
   };
   uint32_t sum = 0;
   for (int l = t * SPAN; l < (t + 1) * SPAN; l++) sum += entry(l);
-  part[t] = sum;
-  __syncthreads();
-  for (int d = 1; d < ORDER_THREADS; d <<= 1) {  // inclusive scan of the partial sums
-    const uint32_t v = t >= d ? part[t - d] : 0u;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  // inclusive scan of the threads' sums: within each wave by shuffles, then
+  // over the waves' totals
+  const int lane = t & 63, wv = t >> 6;
+  uint32_t inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t v = __shfl_up(inc, d);
+    if (lane >= d) inc += v;
   }
-  uint32_t run = part[t] - sum;
+  if (lane == 63) part[wv] = inc;
+  __syncthreads();
+  if (t == 0)
+    for (int w = 1; w < ORDER_THREADS / 64; w++) part[w] += part[w - 1];
+  __syncthreads();
+  uint32_t run = inc - sum + (wv > 0 ? part[wv - 1] : 0u);
   for (int l = t * SPAN; l < (t + 1) * SPAN; l++) {
     const uint32_t c = entry(l);
     entry(l) = run;
