@@ -267,13 +267,8 @@ attn_status attn_rotary(const attn_params *params, int64_t batch, int64_t seqlen
  * Forward, packed [T,H,D] with device int32 cu_seqlens_q/k [num_seqs+1].
  * total_q / total_k are the token counts (cu_seqlens_*[num_seqs]);
  * max_seqlen_q / max_seqlen_k bound every sequence's length.  lse is fp32
- * [Hq, total_q].  A packed grid of 2048 workgroups or more (at most 16384
- * blocks per kv head, 8191 sequences) first builds, in the workspace, a
- * table that orders its blocks by their work under the mask, largest first,
- * so that the longest blocks of the batch start first wherever their
- * sequences sit in it (a short extra launch; the results do not depend on
- * the order).  attn_fwd_varlen_workspace_size is then the table's size
- * (4 bytes per workgroup), else 0.
+ * [Hq, total_q].  The forward needs no workspace:
+ * attn_fwd_varlen_workspace_size returns 0, and workspace may be NULL.
  */
 attn_status attn_fwd_varlen(const attn_params *params, int32_t num_seqs, int64_t total_q,
                             int64_t total_k, const int32_t *cu_seqlens_q,
@@ -287,8 +282,15 @@ size_t attn_fwd_varlen_workspace_size(const attn_params *params, int32_t num_seq
 /*
  * Backward, packed.  Same arguments as attn_fwd_varlen plus o, lse (fp32
  * [Hq, total_q]), dout, and the outputs dq, dk, dv, dsinks as in attn_bwd.
- * The dQ and the dK/dV grids each get a schedule table in the workspace by
- * the same rule as the packed forward's.
+ * When the dK/dV grid has 2048 workgroups or more, max_seqlen_q is 1024 or
+ * more, and the batch fits the tables' limits (at most 16384 blocks per kv
+ * head in either grid, 8191 sequences), a short extra launch first builds,
+ * in the workspace, one table per grid (dQ and dK/dV, 4 bytes per
+ * workgroup) that orders the grid's blocks by their work under the mask,
+ * largest first, so that the longest blocks of the batch start first
+ * wherever their sequences sit in it.  The results do not depend on the
+ * order; attn_bwd_varlen_workspace_size includes the tables when they are
+ * built.
  */
 attn_status attn_bwd_varlen(const attn_params *params, int32_t num_seqs, int64_t total_q,
                             int64_t total_k, const int32_t *cu_seqlens_q,
