@@ -19,7 +19,7 @@
 namespace attn {
 
 constexpr int ORDER_THREADS = 1024;
-constexpr int ORDER_CLASSES = 128;   // work classes, 8 per doubling
+constexpr int ORDER_CLASSES = 128;   // work classes, 4 per doubling
 constexpr int ORDER_COUNTERS = 256;  // threads that count and scatter, each a contiguous run of blocks
 
 struct OrderGrids {
@@ -50,10 +50,13 @@ __device__ int block_work(const OrderArgs& a, const SeqInfo& si, int b) {
   return tiles + 2;
 }
 
-// Work class, larger for more work: 0 for idle slots, else 1 + 8 log2(work).
+// Work class, larger for more work: 0 for idle slots, else 1 + 4 log2(work).
+// Blocks within about a fifth of each other's work share a class and keep
+// their layout order, so runs of neighbouring blocks of one sequence (which
+// read mostly the same rows) are still dispatched together.
 __device__ __forceinline__ int work_class(int w) {
   if (w <= 0) return 0;
-  return min(ORDER_CLASSES - 1, 1 + (int)(8.f * __builtin_amdgcn_logf((float)w)));
+  return min(ORDER_CLASSES - 1, 1 + (int)(4.f * __builtin_amdgcn_logf((float)w)));
 }
 
 __global__ __launch_bounds__(ORDER_THREADS) void packed_order_kernel(const OrderGrids grids) {
