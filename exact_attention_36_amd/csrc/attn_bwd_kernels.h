@@ -78,7 +78,7 @@ void bwd_dq_kernel(const BwdArgs a) {
     mb = blk - packed_block_start(a.s.cu_q, seq, G, BM);
   } else {
     int grp, rank;
-    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nmb}.decode(blockIdx.x, grp, rank)) return;
+    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nmb, unmasked(a.s)}.decode(blockIdx.x, grp, rank)) return;
     g = grp % a.s.hkv;
     seq = grp / a.s.hkv;
     mb = a.nmb - 1 - rank;  // causal: the longest tiles start first
@@ -469,7 +469,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     // groups are (sequence, kv head); rank 0 is key block 0, the one most
     // query rows see under a causal mask
     int grp;
-    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nkb}.decode(blockIdx.x, grp, nb)) return;
+    if (!GroupGrid{a.s.nseq * a.s.hkv, a.nkb, unmasked(a.s)}.decode(blockIdx.x, grp, nb)) return;
     g = grp % a.s.hkv;
     seq = grp / a.s.hkv;
   }

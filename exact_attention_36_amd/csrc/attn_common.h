@@ -61,6 +61,10 @@ struct Band {
   }
 };
 
+// No causal mask and no window: every block of a batched grid's group does
+// the same work.
+__device__ __forceinline__ bool unmasked(const SeqArgs& s) { return !s.causal && s.wl < 0 && s.wr < 0; }
+
 // Queries that see key j: [qmin(j), qmax(j)], the inverse of the band.
 // Used by the key-major backward to visit only the query blocks that see a
 // key block.

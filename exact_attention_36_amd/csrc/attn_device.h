@@ -266,11 +266,15 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // block of a group.  With at least two groups per XCD, XCD x (which receives
 // workgroups x, x+8, x+16, ...) owns groups [x*gpx, (x+1)*gpx) and runs their
 // blocks heaviest rank first across those groups (longest-processing-time
-// order, and the blocks that share a group's K/V share an L2).  With fewer
-// groups the order is simply rank-major over the whole chip.  Returns false
-// for padding slots.  grid_size() gives the matching launch size.
+// order, and the blocks that share a group's K/V share an L2).  When every
+// rank does the same work (no mask), by_group runs an XCD's groups one after
+// the other instead, all ranks of a group side by side, so that the blocks
+// reading a group's K/V (or Q and dO) run together.  With fewer groups the
+// order is simply rank-major over the whole chip.  Returns false for padding
+// slots.  grid_size() gives the matching launch size.
 struct GroupGrid {
   int ngroups, nranks;
+  bool by_group = false;
   __host__ __device__ bool grouped() const { return ngroups >= 16; }
   __host__ __device__ int gpx() const { return (ngroups + 7) / 8; }
   __host__ __device__ long long grid_size() const {
@@ -287,6 +291,12 @@ struct GroupGrid {
     const int g0 = xcd * per;
     const int cnt = min(per, ngroups - g0);
     if (cnt <= 0 || slot >= cnt * nranks) return false;
+    if (by_group) {
+      const int gi = slot / nranks;
+      rank = slot - gi * nranks;
+      group = g0 + gi;
+      return true;
+    }
     rank = slot / cnt;
     group = g0 + (slot - rank * cnt);
     return true;

@@ -82,7 +82,7 @@ void fwd_kernel(const FwdArgs a) {
     // groups are (sequence, kv head, split); rank 0 is the last m-block, the
     // longest one under a causal mask
     int grp, rank;
-    if (!GroupGrid{a.s.nseq * a.s.hkv * a.n_split, a.nmb}.decode(blockIdx.x, grp, rank)) return;
+    if (!GroupGrid{a.s.nseq * a.s.hkv * a.n_split, a.nmb, unmasked(a.s)}.decode(blockIdx.x, grp, rank)) return;
     sp = grp % a.n_split;
     const int r = grp / a.n_split;
     g = r % a.s.hkv;
