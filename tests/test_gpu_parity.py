@@ -47,6 +47,11 @@ BATCHED = [
     ("sinks_g48_window_fp16", 1, 70, 70, 48, 1, 64, False, (30, 30), True, "fp16", True),
     ("sinks_g64_window_fp16", 2, 50, 60, 64, 1, 64, True, (10, 5), True, "fp16", True),
     ("sinks_g128_full_fp16", 1, 40, 40, 128, 1, 64, False, (-1, -1), True, "fp16", True),
+    # no mask with 16 or more (sequence, kv head) groups: the batched grids run
+    # each XCD's groups one after the other, every block of a group side by
+    # side (ragged last query and key blocks)
+    ("unmasked_16_groups", 4, 300, 300, 8, 4, 64, False, (-1, -1), False, "bf16", True),
+    ("unmasked_16_groups_sq_ne_sk_sinks_fp16", 8, 260, 390, 4, 2, 128, False, (-1, -1), True, "fp16", True),
 ]
 
 
