@@ -1,5 +1,4 @@
-"""AddressSanitizer builds of the host code, on the CPU (SURVEY's memory-safety
-plan): the C ABI's host side -- attn_api.cpp with host stand-ins for the
+"""AddressSanitizer builds of the host code, on the CPU: the C ABI's host side -- attn_api.cpp with host stand-ins for the
 kernel launchers, driven through every entry point by tests/asan/abi_driver.cpp,
 which also checks that each workspace region handed to the kernels lies
 inside the caller's workspace -- and the oracle, on small problems covering
