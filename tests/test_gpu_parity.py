@@ -172,6 +172,32 @@ def test_varlen_equals_batched_calls():
         assert torch.equal(lse[:, a:b], lb[0]), s
 
 
+def test_unmasked_group_order_bitwise():
+    """Without a mask a batched grid of 16 or more (sequence, kv head) groups
+    runs each XCD's groups one after the other, every block of a group side
+    by side, where a smaller grid runs heaviest block first over the chip.  A
+    workgroup's result does not depend on when it runs, so each batch entry's
+    forward and backward equal a call on that entry alone (2 groups, the other
+    order) bit for bit.  Neither side splits the keys (5 key tiles)."""
+    B, S, hq, hkv, d = 8, 260, 4, 2, 128
+    inp = synth.batched_inputs(21, B, S, S, hq, hkv, d, grads=True)
+    q, k, v, do = (dev_tensor(inp[n]) for n in ("q", "k", "v", "dout"))
+    print("case unmasked_group_order", B, S, hq, hkv, d, flush=True)
+    o, lse = ea.attn_fwd(q, k, v)
+    dq, dk, dv, _ = ea.attn_bwd(q, k, v, o, lse, do, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        sl = lambda t: t[b:b + 1].contiguous()  # noqa: E731
+        ob, lb = ea.attn_fwd(sl(q), sl(k), sl(v))
+        dqb, dkb, dvb, _ = ea.attn_bwd(sl(q), sl(k), sl(v), ob, lb, sl(do), grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o[b], ob[0]), b
+        assert torch.equal(lse[b], lb[0]), b
+        assert torch.equal(dq[b], dqb[0]), b
+        assert torch.equal(dk[b], dkb[0]), b
+        assert torch.equal(dv[b], dvb[0]), b
+
+
 SCHEDULE = [
     # id, causal, window, sinks, seqused
     ("causal", True, (-1, -1), False, False),
