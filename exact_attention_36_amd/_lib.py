@@ -130,8 +130,11 @@ def _ptr(t):
 
 
 def _need(cond, msg):
+    """Raise ValueError(msg) unless cond; msg may be a callable that builds the
+    message, so that the checks of a launch-bound call format nothing when
+    they pass."""
     if not cond:
-        raise ValueError(msg)
+        raise ValueError(msg() if callable(msg) else msg)
 
 
 def _check_tensors(named, dtype=None, shapes=None):
@@ -146,34 +149,43 @@ def _check_tensors(named, dtype=None, shapes=None):
         t = present.get(n)
         if t is None or want is None:
             continue
-        got = tuple(t.shape)
-        ok = len(got) == len(want) and all(w is None or int(w) == g for w, g in zip(want, got))
-        _need(ok, "%s must have shape %s, got %s" % (n, tuple("*" if w is None else int(w) for w in want), got))
+        got = t.shape
+        ok = len(got) == len(want)
+        if ok:
+            for w, g in zip(want, got):
+                if w is not None and w != g:
+                    ok = False
+                    break
+        _need(ok, lambda: "%s must have shape %s, got %s" % (n, tuple("*" if w is None else int(w) for w in want),
+                                                              tuple(got)))
     if dtype:
         ref = present[dtype[0]].dtype
-        _need(ref in (torch.bfloat16, torch.float16), "%s must be bf16 or fp16, got %s" % (dtype[0], ref))
+        _need(ref in (torch.bfloat16, torch.float16), lambda: "%s must be bf16 or fp16, got %s" % (dtype[0], ref))
         for n in dtype[1:]:
             if n in present:
-                _need(present[n].dtype == ref, "%s must have %s's dtype %s, got %s" % (n, dtype[0], ref,
-                                                                                       present[n].dtype))
+                _need(present[n].dtype == ref,
+                      lambda: "%s must have %s's dtype %s, got %s" % (n, dtype[0], ref, present[n].dtype))
     for n, t in present.items():
-        _need(t.is_contiguous(), "%s must be contiguous (got strides %s)" % (n, tuple(t.stride())))
-    devs = {t.device for t in present.values()}
-    _need(len(devs) == 1, "all tensors must be on one device, got %s" % sorted(str(d) for d in devs))
-    dev = devs.pop()
-    _need(dev.type == "cuda", "tensors must be on a GPU (got %s)" % dev)
+        _need(t.is_contiguous(), lambda: "%s must be contiguous (got strides %s)" % (n, tuple(t.stride())))
+    devs = {t.get_device() for t in present.values()}  # -1 off the GPU
+    _need(len(devs) == 1, lambda: "all tensors must be on one device, got %s"
+          % sorted({str(t.device) for t in present.values()}))
+    _need(devs.pop() >= 0 and next(iter(present.values())).is_cuda,
+          lambda: "tensors must be on a GPU (got %s)" % next(iter(present.values())).device)
 
 
 def _check_f32(name, t, shape):
     if t is not None:
-        _need(t.dtype == torch.float32, "%s must be fp32, got %s" % (name, t.dtype))
-        _need(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+        _need(t.dtype == torch.float32, lambda: "%s must be fp32, got %s" % (name, t.dtype))
+        _need(tuple(t.shape) == tuple(shape),
+              lambda: "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
 def _check_i32(name, t, shape):
     if t is not None:
-        _need(t.dtype == torch.int32, "%s must be int32, got %s" % (name, t.dtype))
-        _need(tuple(t.shape) == tuple(shape), "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+        _need(t.dtype == torch.int32, lambda: "%s must be int32, got %s" % (name, t.dtype))
+        _need(tuple(t.shape) == tuple(shape),
+              lambda: "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
 def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=None, softcap=0.0,
@@ -301,7 +313,7 @@ def attn_bwd_noalloc(q, k, v, o, lse, dout, causal=False, window=(-1, -1), sinks
     _check_f32("lse", lse, (B, hq, sq))
     for n, t, shp in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, v.shape)):
         if t is not None:
-            _need(t.dtype == gd and tuple(t.shape) == tuple(shp), "%s must be %s %s" % (n, gd, tuple(shp)))
+            _need(t.dtype == gd and tuple(t.shape) == tuple(shp), lambda: "%s must be %s %s" % (n, gd, tuple(shp)))
     if dsinks is not None and sinks is not None:
         _check_f32("dsinks", dsinks, tuple(sinks.shape))
     _check_tensors(dict(q=q, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, dsinks=dsinks),
