@@ -235,7 +235,14 @@ def _check(st):
         raise AttnError(st, last_error())
 
 
+# torch's current-stream handle as a plain integer, without building a Stream
+# object (a few microseconds a call); the public call where torch lacks it
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(dev):
+    if _RAW_STREAM is not None:
+        return ctypes.c_void_p(_RAW_STREAM(torch.cuda.current_device() if dev.index is None else dev.index))
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
