@@ -226,7 +226,8 @@ def make_params(q, k, causal=False, window=(-1, -1), sinks=None, softmax_scale=N
         if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (nseq,) or not t.is_contiguous()):
             raise ValueError("%s must be contiguous int32 [%s]; got %s %s" % (name, nseq, tuple(t.shape), t.dtype))
         setattr(p, name, _ptr(t))
-    _check_tensors(dict(q=q, sinks=sinks, alibi_slopes=alibi_slopes, seqused_q=seqused_q, seqused_k=seqused_k))
+    if sinks is not None or alibi_slopes is not None or seqused_q is not None or seqused_k is not None:
+        _check_tensors(dict(q=q, sinks=sinks, alibi_slopes=alibi_slopes, seqused_q=seqused_q, seqused_k=seqused_k))
     return p
 
 
